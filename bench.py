@@ -1,0 +1,394 @@
+"""Benchmark of the KV-cache attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads ...]
+
+Prints ONE JSON line.  The headline workload (`value`) is the Llama-3-8B-
+shaped paged GQA decode step: batch 32, 32 query / 8 KV heads, head_dim 128,
+bf16 cache in 16-token blocks behind a permuted block table, cached lengths
+uniform in [1, 8192]; a step appends one token per sequence (kv_append) and
+attends it (attn_decode = split-K partition pass + merge pass).  `value` is
+algorithmic HBM bytes per step / step time, in GB/s.
+
+Other workloads run in the same invocation and are reported under
+"workloads": the padded 32-layer MHA decode (batch 8, 4096-position
+contiguous cache, key padding mask), the 80-layer fp8 long-context decode
+(batch 1, 64/8 heads, 131,073 keys per layer) and the causal 8192-token
+prefill that writes the paged cache.
+
+Timing: W untimed warm-up steps, then K steps bracketed by synchronize +
+HIP events on the stream the library launches on (torch's current stream).
+Each decode step reads a different replica of the cache (round-robin) so the
+256 MB Infinity Cache cannot serve the previous step's bytes.  Per-launch
+HIP events inside the timed region give the decode call's own duration for
+the roofline.  The CPU baseline is the fp64 oracle on the host, timed on the
+same inputs (single thread).
+"""
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import kv_cache_decode_attn_amd as K  # noqa: E402
+from kv_cache_decode_attn_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
+METRIC = "decode-attn HBM GB/s (% of peak) & seqs/s; prefill TFLOP/s (% MFMA peak)"
+DEV = "cuda"
+
+
+def _events(n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _stats(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median_ms": float(np.median(a)), "min_ms": float(a.min()), "p90_ms": float(np.percentile(a, 90)),
+            "mean_ms": float(a.mean())}
+
+
+# ------------------------------------------------------------------ decode ---
+
+class PagedDecode:
+    """Llama-3-8B-shaped paged GQA decode step (one layer)."""
+
+    name = "llama3-8b-paged-gqa-decode"
+
+    def __init__(self, replicas=4, wid=2):
+        self.B, self.Hq, self.Hkv, self.D = 32, 32, 8, 128
+        self.cached = synth.uniform_lengths(self.B, 1, 8192, (wid, synth.T_LENS))
+        self.ctx = (self.cached + 1).astype(np.int32)          # keys incl. the appended token
+        self.maxlen = int(self.ctx.max()) if self.B else 0
+        self.max_seq_len = 8193
+        nbs = [synth.blocks_for(c) for c in self.ctx]
+        self.max_blocks = 513
+        table, self.nblk = synth.block_table(nbs, self.max_blocks, (wid, synth.T_PERM))
+        self.table = torch.from_numpy(table).to(DEV)
+        # logical K/V of every position, the query, and the new token's K/V
+        width = self.maxlen
+        self.src_k = synth.normal_device((self.B, self.Hkv, width, self.D), (wid, synth.T_K))
+        self.src_v = synth.normal_device((self.B, self.Hkv, width, self.D), (wid, synth.T_V))
+        self.q = synth.normal_device((self.B, self.Hq, self.D), (wid, synth.T_Q))
+        idx = torch.from_numpy(self.cached.astype(np.int64)).to(DEV).view(self.B, 1, 1, 1).expand(
+            self.B, self.Hkv, 1, self.D)
+        self.k_new = torch.gather(self.src_k, 2, idx).contiguous()
+        self.v_new = torch.gather(self.src_v, 2, idx).contiguous()
+        self.positions = torch.from_numpy(self.cached).to(DEV)
+        self.seq_lens = torch.from_numpy(self.ctx).to(DEV)
+        zeros = torch.zeros(self.B, dtype=torch.int32, device=DEV)
+        self.caches = []
+        for _ in range(replicas):
+            c = K.KVCache.paged(self.nblk, self.Hkv, self.D, K.BF16, DEV)
+            K.kv_append(c, self.src_k, self.src_v, zeros, block_table=self.table, n_valid=self.positions)
+            self.caches.append(c)
+        self.out = torch.empty((self.B, self.Hq, self.D), dtype=torch.float32, device=DEV)
+        self.part = K.decode_default_part_tokens(self.B, self.Hq, self.Hkv, self.max_seq_len)
+        self.ws = K.decode_workspace(self.caches[0], self.B, self.Hq, self.max_seq_len, self.part)
+        torch.cuda.synchronize()
+
+    def kv_bytes(self):
+        return 2 * self.Hkv * self.D * 2 * int(self.ctx.sum())
+
+    def decode_bytes(self):
+        """Algorithmic bytes of one attn_decode call: K/V of every attended
+        key, the query, the fp32 output, the block-table entries and lengths."""
+        blocks = sum(synth.blocks_for(c) for c in self.ctx)
+        return self.kv_bytes() + self.B * self.Hq * self.D * 2 + self.B * self.Hq * self.D * 4 + 4 * blocks + 4 * self.B
+
+    def append_bytes(self):
+        return 2 * (2 * self.B * self.Hkv * self.D * 2) + 4 * self.B + 4 * self.B
+
+    def step_bytes(self):
+        return self.decode_bytes() + self.append_bytes()
+
+    def step(self, i, ev=None):
+        c = self.caches[i % len(self.caches)]
+        if ev:
+            ev[0].record()
+        K.kv_append(c, self.k_new, self.v_new, self.positions, block_table=self.table)
+        if ev:
+            ev[1].record()
+        K.attn_decode(c, self.q, self.seq_lens, self.max_seq_len, block_table=self.table, out=self.out,
+                      workspace=self.ws, part_tokens=self.part)
+        if ev:
+            ev[2].record()
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "q_heads": self.Hq, "kv_heads": self.Hkv,
+                "head_dim": self.D, "kv_dtype": "bf16", "block_tokens": 16, "keys_total": int(self.ctx.sum()),
+                "cached_len": "U[1,8192] + 1 appended", "part_tokens": self.part, "cache_replicas": len(self.caches)}
+
+    def cpu_baseline(self, max_seqs=None):
+        """The oracle on the same bytes, single thread: bf16 -> fp64 decode of
+        the cache plus the attention, timed; returns (result dict, max abs err)."""
+        from threadpoolctl import threadpool_limits
+
+        from oracle import attention as OA
+        from oracle import cache as OC
+
+        seqs = list(range(self.B if max_seqs is None else min(max_seqs, self.B)))
+        kh = [self.src_k[b, :, :self.ctx[b]].cpu().view(torch.int16).numpy().view(np.uint16) for b in seqs]
+        vh = [self.src_v[b, :, :self.ctx[b]].cpu().view(torch.int16).numpy().view(np.uint16) for b in seqs]
+        qh = self.q[seqs].cpu().view(torch.int16).numpy().view(np.uint16)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            keys = [OC.to_f64(x, OC.BF16) for x in kh]
+            vals = [OC.to_f64(x, OC.BF16) for x in vh]
+            want = OA.decode(OC.to_f64(qh, OC.BF16), keys, vals, self.ctx[seqs], 1.0 / math.sqrt(self.D))
+            dt = time.perf_counter() - t0
+        # the GPU output of the last timed step covers the same sequences
+        got = self.out[seqs].cpu().numpy()
+        err = float(np.abs(got - want).max())
+        nbytes = 2 * self.Hkv * self.D * 2 * int(self.ctx[seqs].sum())
+        res = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "%d of %d sequences (%d keys, %.0f MB of K/V), fp64 numpy, 1 thread, %.1f s; %s" % (
+                   len(seqs), self.B, int(self.ctx[seqs].sum()), nbytes / 1e6, dt, platform.processor() or
+                   platform.machine()),
+               "seqs_per_s": len(seqs) / dt}
+        return res, err
+
+
+class PaddedDecode:
+    """Padded-batch MHA decode over 32 layers with a key padding mask."""
+
+    name = "padded-mha-decode-32-layers"
+
+    def __init__(self, wid=3):
+        self.L, self.B, self.H, self.D, self.cap = 32, 8, 32, 128, 4096
+        self.real = synth.uniform_lengths(self.B, 512, 4096, (wid, synth.T_LENS))
+        self.mask = torch.from_numpy(synth.padding_mask(self.real, self.cap)).to(DEV)
+        self.seq_lens = torch.from_numpy(self.real).to(DEV)
+        self.positions = torch.from_numpy(self.real - 1).to(DEV)
+        self.caches, self.k_new, self.v_new, self.q = [], [], [], []
+        idx = torch.from_numpy((self.real - 1).astype(np.int64)).to(DEV).view(self.B, 1, 1, 1).expand(
+            self.B, self.H, 1, self.D)
+        for layer in range(self.L):
+            c = K.KVCache.contiguous(self.B, self.H, self.cap, self.D, K.BF16, DEV)
+            synth.normal_device(c.k.shape, (wid, synth.T_K, layer), out=c.k)
+            synth.normal_device(c.v.shape, (wid, synth.T_V, layer), out=c.v)
+            self.caches.append(c)
+            # the new token is the one at real_b - 1 (re-written in place each step)
+            self.k_new.append(torch.gather(c.k, 2, idx).contiguous())
+            self.v_new.append(torch.gather(c.v, 2, idx).contiguous())
+            self.q.append(synth.normal_device((self.B, self.H, self.D), (wid, synth.T_Q, layer)))
+        self.out = torch.empty((self.L, self.B, self.H, self.D), dtype=torch.float32, device=DEV)
+        self.part = K.decode_default_part_tokens(self.B, self.H, self.H, self.cap)
+        self.ws = K.decode_workspace(self.caches[0], self.B, self.H, self.cap, self.part)
+        torch.cuda.synchronize()
+
+    def step_bytes(self):
+        per_layer = (2 * self.H * self.D * 2 * int(self.real.sum()) + self.B * self.H * self.D * (2 + 4)
+                     + 2 * 2 * self.B * self.H * self.D * 2 + int(self.real.sum()) + 8 * self.B)
+        return self.L * per_layer
+
+    def step(self, i, ev=None):
+        for layer in range(self.L):
+            c = self.caches[layer]
+            K.kv_append(c, self.k_new[layer], self.v_new[layer], self.positions)
+            K.attn_decode(c, self.q[layer], self.seq_lens, self.cap, key_mask=self.mask, out=self.out[layer],
+                          workspace=self.ws, part_tokens=self.part)
+
+    def config(self):
+        return {"workload": self.name, "layers": self.L, "batch": self.B, "q_heads": self.H, "kv_heads": self.H,
+                "head_dim": self.D, "kv_dtype": "bf16", "capacity": self.cap, "real_len": "U[512,4096]",
+                "part_tokens": self.part}
+
+
+class LongContextFp8Decode:
+    """Llama-3-70B-shaped fp8 long-context decode over 80 layers, batch 1."""
+
+    name = "llama3-70b-fp8-longctx-decode-80-layers"
+
+    def __init__(self, wid=5, layers=80):
+        self.L, self.B, self.Hq, self.Hkv, self.D = layers, 1, 64, 8, 128
+        self.cached = 131072
+        self.ctx = self.cached + 1
+        nb = synth.blocks_for(self.ctx)
+        self.caches, self.k_new, self.v_new, self.q, self.tables = [], [], [], [], []
+        scales = synth.fp8_scales(self.L * self.Hkv * 2, (wid, synth.T_SCALE)).reshape(self.L, 2, self.Hkv)
+        self.scales = torch.from_numpy(scales).to(DEV)
+        zeros = torch.zeros(1, dtype=torch.int32, device=DEV)
+        pos = torch.tensor([self.cached], dtype=torch.int32, device=DEV)
+        self.positions, self.seq_lens = pos, torch.tensor([self.ctx], dtype=torch.int32, device=DEV)
+        for layer in range(self.L):
+            table, nblk = synth.block_table([nb], nb, (wid, synth.T_PERM, layer))
+            tdev = torch.from_numpy(table).to(DEV)
+            c = K.KVCache.paged(nblk, self.Hkv, self.D, K.FP8_E4M3, DEV, self.scales[layer, 0].contiguous(),
+                                self.scales[layer, 1].contiguous())
+            sk = synth.normal_device((1, self.Hkv, self.ctx, self.D), (wid, synth.T_K, layer))
+            sv = synth.normal_device((1, self.Hkv, self.ctx, self.D), (wid, synth.T_V, layer))
+            K.kv_append(c, sk, sv, zeros, block_table=tdev, n_valid=pos)
+            self.k_new.append(sk[:, :, self.cached:].contiguous())
+            self.v_new.append(sv[:, :, self.cached:].contiguous())
+            del sk, sv
+            self.caches.append(c)
+            self.tables.append(tdev)
+            self.q.append(synth.normal_device((1, self.Hq, self.D), (wid, synth.T_Q, layer)))
+        self.out = torch.empty((self.L, 1, self.Hq, self.D), dtype=torch.float32, device=DEV)
+        self.part = K.decode_default_part_tokens(1, self.Hq, self.Hkv, self.ctx)
+        self.ws = K.decode_workspace(self.caches[0], 1, self.Hq, self.ctx, self.part)
+        torch.cuda.synchronize()
+
+    def step_bytes(self):
+        per_layer = (2 * self.Hkv * self.D * self.ctx + self.Hq * self.D * (2 + 4) + 2 * self.Hkv * self.D * (2 + 1)
+                     + 4 * synth.blocks_for(self.ctx) + 16)
+        return self.L * per_layer
+
+    def step(self, i, ev=None):
+        for layer in range(self.L):
+            c = self.caches[layer]
+            K.kv_append(c, self.k_new[layer], self.v_new[layer], self.positions, block_table=self.tables[layer])
+            K.attn_decode(c, self.q[layer], self.seq_lens, self.ctx, block_table=self.tables[layer],
+                          out=self.out[layer], workspace=self.ws, part_tokens=self.part)
+
+    def config(self):
+        return {"workload": self.name, "layers": self.L, "batch": 1, "q_heads": self.Hq, "kv_heads": self.Hkv,
+                "head_dim": self.D, "kv_dtype": "fp8_e4m3", "keys": self.ctx, "part_tokens": self.part}
+
+
+class CausalPrefill:
+    """Causal 8192-token prefill, GQA 32/8, d 128, bf16, writing the paged cache."""
+
+    name = "causal-prefill-8192-gqa"
+
+    def __init__(self, wid=4):
+        self.B, self.Hq, self.Hkv, self.N, self.D = 1, 32, 8, 8192, 128
+        std = 1.0 / math.sqrt(self.D)
+        self.q = synth.normal_device((1, self.Hq, self.N, self.D), (wid, synth.T_Q), std=std)
+        self.k = synth.normal_device((1, self.Hkv, self.N, self.D), (wid, synth.T_KNEW), std=std)
+        self.v = synth.normal_device((1, self.Hkv, self.N, self.D), (wid, synth.T_VNEW), std=std)
+        nb = self.N // 16
+        table, nblk = synth.block_table([nb], nb, (wid, synth.T_PERM))
+        self.table = torch.from_numpy(table).to(DEV)
+        self.cache = K.KVCache.paged(nblk, self.Hkv, self.D, K.BF16, DEV)
+        self.positions = torch.zeros(1, dtype=torch.int32, device=DEV)
+        self.out = torch.empty((1, self.Hq, self.N, self.D), dtype=torch.float32, device=DEV)
+        torch.cuda.synchronize()
+
+    def flops(self):
+        return 2 * self.D * self.Hq * self.N * (self.N + 1)  # QK^T and PV over the causal triangle
+
+    def step(self, i, ev=None):
+        K.attn_prefill(self.q, self.k, self.v, cache=self.cache, positions=self.positions, block_table=self.table,
+                       out=self.out)
+
+    def config(self):
+        return {"workload": self.name, "batch": 1, "q_heads": self.Hq, "kv_heads": self.Hkv, "seq": self.N,
+                "head_dim": self.D, "dtype": "bf16", "causal": True, "writes_paged_cache": True}
+
+
+def time_steps(w, steps, warmup, per_launch=False):
+    for i in range(warmup):
+        w.step(i)
+    torch.cuda.synchronize()
+    evs = [_events(3) for _ in range(steps)] if per_launch else [None] * steps
+    start, end = _events(2)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        w.step(warmup + i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    launch = None
+    if per_launch:
+        launch = {"append": _stats([e[0].elapsed_time(e[1]) for e in evs]),
+                  "decode": _stats([e[1].elapsed_time(e[2]) for e in evs])}
+    return total_ms / steps, launch
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="decode8b,padded32,longctx70b",
+                    help="comma list: decode8b (headline), padded32, longctx70b, prefill8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the headline workload the oracle runs")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the library is a single-GPU kernel library and this build runs on a "
+              "one-GPU box (how the path would shard is described in the design notes).", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    names = [x for x in args.workloads.split(",") if x]
+
+    w = PagedDecode()
+    ms, launch = time_steps(w, args.steps, args.warmup, per_launch=True)
+    step_bytes = w.step_bytes()
+    dec_ms = launch["decode"]["mean_ms"]
+    achieved = w.decode_bytes() / (dec_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": step_bytes / (ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/Q, seeded lengths and block permutation)",
+        "config": w.config(),
+        "frac_of_hbm_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "seqs_per_s": w.B / (ms * 1e-3),
+        "step_bytes": step_bytes,
+        "per_launch": launch,
+        "roofline": {"bound": "hbm", "kernel": "attn_decode (decode_partition + decode_merge)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "bytes_per_launch": w.decode_bytes(), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        base, err = w.cpu_baseline(args.cpu_seqs)
+        line["cpu_baseline"] = base
+        line["parity_max_abs_err_vs_oracle"] = err
+    del w
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if "padded32" in names:
+        p = PaddedDecode()
+        ms3, _ = time_steps(p, max(5, args.steps // 2), args.warmup)
+        gbs = p.step_bytes() / (ms3 * 1e-3) / 1e9
+        extra["padded32"] = {"config": p.config(), "ms_per_step": ms3, "GB/s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+                             "seqs_per_s": p.B / (ms3 * 1e-3), "step_bytes": p.step_bytes()}
+        del p
+        torch.cuda.empty_cache()
+    if "longctx70b" in names:
+        lw = LongContextFp8Decode()
+        ms5, _ = time_steps(lw, max(5, args.steps // 2), args.warmup)
+        gbs = lw.step_bytes() / (ms5 * 1e-3) / 1e9
+        extra["longctx70b"] = {"config": lw.config(), "ms_per_step": ms5, "GB/s": gbs,
+                               "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "seqs_per_s": 1 / (ms5 * 1e-3),
+                               "step_bytes": lw.step_bytes()}
+        del lw
+        torch.cuda.empty_cache()
+    if "prefill8k" in names:
+        pf = CausalPrefill()
+        msp, _ = time_steps(pf, max(3, args.steps // 4), 1)
+        tf = pf.flops() / (msp * 1e-3) / 1e12
+        extra["prefill8k"] = {"config": pf.config(), "ms_per_step": msp, "TFLOP/s": tf,
+                              "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS, "flops": pf.flops()}
+        del pf
+        torch.cuda.empty_cache()
+    if extra:
+        line["workloads"] = extra
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,275 @@
+/*
+ * kvattn.h - C ABI of a gfx950 (MI355X) KV-cache attention library.
+ *
+ * The library computes scaled dot-product attention of new query tokens
+ * against one layer's KV cache,
+ *     out = softmax(Q K^T * scale + mask) V,
+ * as defined in "Transformer Attention Masks and KV-Cache Inference"
+ * (c86j224s.github.io), section "State of scaled dot-product attention",
+ * and "KV Cache" (heepie.pages.dev), section "Self-Attention".
+ *
+ * Three hot calls: kvattn_kv_append (write new K/V into the cache),
+ * kvattn_attn_decode (one new token per sequence against the cache) and
+ * kvattn_attn_prefill (many new tokens, causal/padding masked, optionally
+ * writing the cache).  Plus sizing, validation and status helpers.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers named as "device" are HIP device pointers owned by the caller;
+ *    the library never allocates, frees or keeps them past the call.  Host
+ *    pointers (the kvattn_cache descriptor) are read during the call only.
+ *  - Every compute call is asynchronous: it validates its host-side
+ *    arguments, enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *    default stream) and returns without synchronising.  Kernel faults
+ *    surface at the caller's next synchronisation.
+ *  - Return value: KVATTN_OK (0) or a negative kvattn_status.  On error
+ *    nothing is enqueued; kvattn_last_error() returns a message for the
+ *    calling thread.  No C++ exception crosses this boundary.
+ *  - Positions are 0-based absolute token positions ("Transformer
+ *    Attention Masks and KV-Cache Inference", sections "Causal mask and
+ *    future positions" and "Position IDs and the append contract").
+ *  - Masks are uint8 with 1 = the query may attend the key, 0 = blocked;
+ *    a blocked key gets weight exactly 0 and its K/V bytes are never used
+ *    (so non-finite padding cannot leak into the output).  A query row that
+ *    can attend no key outputs 0.
+ *  - Grouped-query attention: query head h reads KV head
+ *    h / (num_q_heads / num_kv_heads) ("KV Cache Fully Explained",
+ *    section "(2) GQA"); num_q_heads must be a multiple of num_kv_heads
+ *    with a group size of 1, 2, 4 or 8.
+ *  - Device-supplied indices (positions, lengths, block ids) are bounds
+ *    checked in the kernels: an out-of-range write is skipped, an
+ *    out-of-range block is read as fully masked, and lengths are clamped to
+ *    the cache's capacity.  kvattn_validate reports such inputs.
+ */
+#ifndef KVATTN_H
+#define KVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Tokens per block of the paged layout: the 16-token blocks behind a page
+ * table of "KV Cache, Flash Attention and Inference Optimization"
+ * (factory.pai-world.com), section "PagedAttention", and "KV Cache Fully
+ * Explained" (techblog.paldyn.com), section "(4) PagedAttention". */
+#define KVATTN_BLOCK_TOKENS 16
+
+typedef enum kvattn_status {
+  KVATTN_OK = 0,
+  KVATTN_EINVAL = -1,       /* null pointer, bad size, bad enum, misalignment */
+  KVATTN_EUNSUPPORTED = -2, /* valid request this build has no kernel for   */
+  KVATTN_EWORKSPACE = -3,   /* decode workspace missing or too small        */
+  KVATTN_ELAUNCH = -4       /* the HIP runtime refused a kernel launch      */
+} kvattn_status;
+
+typedef enum kvattn_dtype {
+  KVATTN_F32 = 0,      /* IEEE binary32                                      */
+  KVATTN_BF16 = 1,     /* bfloat16                                           */
+  KVATTN_FP8_E4M3 = 2  /* OCP FP8 E4M3FN, cache only; real = code * scale    */
+} kvattn_dtype;
+
+typedef enum kvattn_layout {
+  /* k, v: [num_rows, num_kv_heads, capacity, head_dim]: the
+   * [batch, kv_heads, seq, head_dim] cache shape of "KV Cache"
+   * (heepie.pages.dev), section "Tensor", and "Transformer Attention Masks
+   * and KV-Cache Inference", section "Cache shape and memory calculation".
+   * Sequence b uses row b. */
+  KVATTN_CONTIGUOUS = 0,
+  /* k, v: [num_blocks, num_kv_heads, 16, head_dim] pools; position p of
+   * sequence b lives in block block_table[b * max_blocks + p / 16], slot
+   * p % 16. */
+  KVATTN_PAGED = 1
+} kvattn_layout;
+
+/* One layer's KV cache.  All memory is caller-owned device memory.
+ * k and v must be 16-byte aligned.  Element type `dtype`; fp8 caches carry
+ * one fp32 dequantisation scale per KV head for K and for V ("KV Cache
+ * Fully Explained", section "(1) FP8 quantization" stores the cache at 8
+ * bits; the per-head scale is this library's reading). */
+typedef struct kvattn_cache {
+  int32_t dtype;         /* kvattn_dtype                                   */
+  int32_t layout;        /* kvattn_layout                                  */
+  int32_t num_kv_heads;  /* >= 1                                           */
+  int32_t head_dim;      /* 64 or 128                                      */
+  int64_t capacity;      /* contiguous: positions per row; paged: ignored  */
+  int64_t num_rows;      /* contiguous: rows allocated; paged: ignored     */
+  int64_t num_blocks;    /* paged: blocks in each pool; contiguous: ignored*/
+  void* k;               /* device                                         */
+  void* v;               /* device                                         */
+  const float* k_scale;  /* device [num_kv_heads]; fp8 only, else NULL     */
+  const float* v_scale;  /* device [num_kv_heads]; fp8 only, else NULL     */
+} kvattn_cache;
+
+/* Library version string, e.g. "kvattn 0.1.0 gfx950". */
+const char* kvattn_version(void);
+
+/* Text for a kvattn_status value. */
+const char* kvattn_status_string(int status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* kvattn_last_error(void);
+
+/* Exact KV-cache bytes: 2 (K and V) * layers * batch * kv_heads * seq *
+ * head_dim * elem_bytes ("Transformer Attention Masks and KV-Cache
+ * Inference", section "Cache shape and memory calculation"; "KV Cache Fully
+ * Explained", section "KV cache memory size calculation").  Pure host
+ * arithmetic; returns 0 if the product overflows 64 bits. */
+uint64_t kvattn_cache_bytes(uint64_t layers, uint64_t batch, uint64_t kv_heads,
+                            uint64_t seq, uint64_t head_dim, uint64_t elem_bytes);
+
+/* kvattn_kv_append - write n_new tokens' K and V per sequence into the cache.
+ *
+ * Append-then-attend: the new token's K/V join the cache before its query
+ * attends ("Transformer Attention Masks and KV-Cache Inference", section
+ * "Prefill and decode stages"; "KV Cache", section "TO-BE").  Token i of
+ * sequence b goes to position p = positions[b] + i:
+ *   contiguous: cache[b, g, p, :] = x[b, g, i, :]
+ *   paged:      pool[block_table[b * max_blocks + p / 16], g, p % 16, :] = x[b, g, i, :]
+ * Same element type in and out: the bits are copied.  f32 or bf16 input
+ * into an fp8 cache: code = E4M3FN(fp32(x) / k_scale[g]) (or v_scale[g])
+ * with round-to-nearest-even, saturation to +-448 and NaN -> 0x7F.
+ *
+ *  cache        host descriptor of the destination layer
+ *  batch        sequences (contiguous: <= cache->num_rows)
+ *  n_new        tokens per sequence in k_new / v_new (>= 0; 0 is a no-op)
+ *  k_new, v_new device [batch, num_kv_heads, n_new, head_dim] of in_dtype,
+ *               16-byte aligned
+ *  in_dtype     KVATTN_F32 or KVATTN_BF16; equal to cache->dtype unless the
+ *               cache is fp8
+ *  positions    device int32 [batch]: position of token 0 of each sequence
+ *               (the caller's stored length, per the append contract of
+ *               "Position IDs and the append contract"; checked by
+ *               kvattn_validate, not here)
+ *  n_valid      device int32 [batch] or NULL: tokens of sequence b to write
+ *               (clamped to [0, n_new]); NULL = all n_new
+ *  block_table  device int32 [batch, max_blocks] (paged) or NULL (contiguous)
+ * Writes whose position or block falls outside the cache are skipped.
+ */
+int kvattn_kv_append(const kvattn_cache* cache, int32_t batch, int32_t n_new,
+                     const void* k_new, const void* v_new, int32_t in_dtype,
+                     const int32_t* positions, const int32_t* n_valid,
+                     const int32_t* block_table, int32_t max_blocks,
+                     void* stream);
+
+/* Bytes of device workspace kvattn_attn_decode needs for these sizes
+ * (split-K partials: per (sequence, query head, partition) an fp32 output
+ * vector plus the running max and sum).  part_tokens as in
+ * kvattn_attn_decode (0 = default).  Returns 0 for invalid sizes. */
+size_t kvattn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t max_seq_len, int32_t part_tokens);
+
+/* Keys per split-K partition that part_tokens == 0 selects for these sizes
+ * (enough partitions to give the 256 compute units several workgroups
+ * each).  Returns 0 for invalid sizes. */
+int32_t kvattn_decode_default_part_tokens(int32_t batch, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t max_seq_len);
+
+/* kvattn_attn_decode - one new query token per sequence against the cache.
+ *
+ * For sequence b and query head h (KV head g = h / G):
+ *   keys s in [0, seq_lens[b]) with key_mask[b * key_mask_stride + s] != 0,
+ *   z_s = scale * q[b, h, :] . K[b, g, s, :],
+ *   out[b, h, :] = sum_s softmax(z)_s V[b, g, s, :]   (0 if no key allowed).
+ * seq_lens counts the cached keys INCLUDING the token just appended: the new
+ * query sees itself ("KV Cache", section "TO-BE"; "Transformer Attention
+ * Masks and KV-Cache Inference", section "Causal mask and future
+ * positions").  The scan is split into partitions of part_tokens keys whose
+ * (max, sum, output) partial states are merged exactly afterwards - the
+ * running max/sum renormalisation of "KV Cache, Flash Attention and
+ * Inference Optimization", section "Flash Attention", numerical trick.
+ *
+ *  q           device [batch, num_q_heads, head_dim]: f32 for an f32 cache,
+ *              bf16 for bf16 and fp8 caches; 16-byte aligned
+ *  seq_lens    device int32 [batch]; values are clamped to [0, max_seq_len]
+ *              and to the cache capacity (kvattn_validate reports it)
+ *  max_seq_len host int32 upper bound of seq_lens (sizes the launch)
+ *  block_table device int32 [batch, max_blocks] (paged) or NULL
+ *  key_mask    device uint8 [batch, key_mask_stride] or NULL (no mask);
+ *              key_mask_stride >= max_seq_len
+ *  scale       score scale, normally 1/sqrt(head_dim)
+ *  out         device fp32 [batch, num_q_heads, head_dim]
+ *  workspace   device, >= kvattn_decode_workspace_bytes(...) bytes, 16-byte
+ *              aligned; contents on entry are ignored
+ *  part_tokens keys per partition: 0 = default, else a multiple of 64 in
+ *              [64, 8192] with part_tokens * G <= 8192
+ * Bitwise deterministic for fixed arguments (fixed partitioning, no atomics).
+ */
+int kvattn_attn_decode(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads,
+                       const void* q, int32_t q_dtype,
+                       const int32_t* seq_lens, int32_t max_seq_len,
+                       const int32_t* block_table, int32_t max_blocks,
+                       const uint8_t* key_mask, int64_t key_mask_stride,
+                       float scale, float* out,
+                       void* workspace, size_t workspace_bytes, int32_t part_tokens,
+                       void* stream);
+
+/* kvattn_attn_prefill - attention of n_max new tokens per sequence, causal
+ * and/or padding masked, tiled so that no n x n score matrix is ever
+ * stored ("KV Cache, Flash Attention and Inference Optimization", section
+ * "Flash Attention - tiling trick"); optionally writing their K/V into the
+ * cache ("KV Cache", section "Prefill and Decode": the prefill creates the
+ * cache).
+ *
+ * Sequence b has q_lens[b] real new tokens (rows t >= q_lens[b] output 0)
+ * at absolute positions P + t, P = positions[b].  Query t attends key
+ * position s iff
+ *   (attend_prefix ? 0 : P) <= s < P + q_lens[b],
+ *   causal == 0 or s <= P + t            ("Causal mask and future positions"),
+ *   key_mask == NULL or key_mask[b * key_mask_stride + s] != 0
+ *                                        ("Padding mask and batch length").
+ * Keys s >= P come from k / v (row s - P); keys s < P (attend_prefix only)
+ * are read from the cache.
+ *
+ *  cache       NULL: no cache access (positions may then be NULL = all 0;
+ *              attend_prefix must be 0).  Else the layer's cache: the new
+ *              K/V are written at positions P .. P + q_lens[b] - 1 (as
+ *              kvattn_kv_append would) before the attention runs.
+ *  num_kv_heads, head_dim: shapes of q/k/v (must equal the cache's if given)
+ *  q           device [batch, num_q_heads, n_max, head_dim] of dtype
+ *  k, v        device [batch, num_kv_heads, n_max, head_dim] of dtype
+ *  dtype       KVATTN_F32 or KVATTN_BF16 (q, k and v alike)
+ *  positions   device int32 [batch] or NULL (all 0)
+ *  q_lens      device int32 [batch] or NULL (all n_max); clamped to [0, n_max]
+ *  block_table device int32 [batch, max_blocks] for a paged cache, else NULL
+ *  key_mask    device uint8 or NULL; key_mask_stride >= largest P + n_max
+ *  out         device fp32 [batch, num_q_heads, n_max, head_dim]
+ * bf16 inputs run on bf16 MFMA with fp32 accumulation; the softmax
+ * weights are rounded to bf16 for the second product and the row sum is
+ * taken over the rounded weights.
+ */
+int kvattn_attn_prefill(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t n_max,
+                        const void* q, const void* k, const void* v, int32_t dtype,
+                        const int32_t* positions, const int32_t* q_lens,
+                        const int32_t* block_table, int32_t max_blocks,
+                        const uint8_t* key_mask, int64_t key_mask_stride,
+                        int32_t causal, int32_t attend_prefix, float scale,
+                        float* out, void* stream);
+
+/* kvattn_validate - device-side check of the cache metadata contract
+ * ("Transformer Attention Masks and KV-Cache Inference", section "Position
+ * IDs and the append contract": the append position must equal the stored
+ * length; lengths and block ids must stay inside the cache).
+ * For each sequence b: 0 <= seq_lens[b] <= max_seq_len and <= the capacity
+ * (contiguous: cache->capacity; paged: max_blocks * 16); every block id the
+ * first seq_lens[b] positions use lies in [0, num_blocks); and, if
+ * positions is not NULL, positions[b] == seq_lens[b] (the stored length
+ * before an append).  *err_word (device int32, caller zeroes it) receives
+ * the OR of KVATTN_VALIDATE_* bits.  A debug call, not on the timed path. */
+#define KVATTN_VALIDATE_LEN_RANGE   1
+#define KVATTN_VALIDATE_BLOCK_RANGE 2
+#define KVATTN_VALIDATE_POSITION    4
+int kvattn_validate(const kvattn_cache* cache, int32_t batch,
+                    const int32_t* seq_lens, int32_t max_seq_len,
+                    const int32_t* positions,
+                    const int32_t* block_table, int32_t max_blocks,
+                    int32_t* err_word, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVATTN_H */

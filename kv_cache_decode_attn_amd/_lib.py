@@ -1,0 +1,90 @@
+"""ctypes view of libkvattn.so (include/kvattn.h).  Argument marshalling only."""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+F32, BF16, FP8_E4M3 = 0, 1, 2
+CONTIGUOUS, PAGED = 0, 1
+BLOCK_TOKENS = 16
+VALIDATE_LEN_RANGE, VALIDATE_BLOCK_RANGE, VALIDATE_POSITION = 1, 2, 4
+
+# Every symbol include/kvattn.h declares.
+EXPORTS = (
+    "kvattn_version", "kvattn_status_string", "kvattn_last_error", "kvattn_cache_bytes",
+    "kvattn_kv_append", "kvattn_decode_workspace_bytes", "kvattn_decode_default_part_tokens",
+    "kvattn_attn_decode", "kvattn_attn_prefill", "kvattn_validate",
+)
+
+
+class KvattnCache(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+        ("num_rows", ctypes.c_int64),
+        ("num_blocks", ctypes.c_int64),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+    ]
+
+
+class KvattnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("kvattn status %d: %s" % (status, message))
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+_CP = ctypes.POINTER(KvattnCache)
+
+_SIGS = {
+    "kvattn_version": (ctypes.c_char_p, []),
+    "kvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvattn_last_error": (ctypes.c_char_p, []),
+    "kvattn_cache_bytes": (_U64, [_U64] * 6),
+    "kvattn_kv_append": (ctypes.c_int, [_CP, _I32, _I32, _P, _P, _I32, _P, _P, _P, _I32, _P]),
+    "kvattn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "kvattn_decode_default_part_tokens": (_I32, [_I32, _I32, _I32, _I32]),
+    "kvattn_attn_decode": (ctypes.c_int, [_CP, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _I64,
+                                          _F, _P, _P, _SZ, _I32, _P]),
+    "kvattn_attn_prefill": (ctypes.c_int, [_CP, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P,
+                                           _P, _I32, _P, _I64, _I32, _I32, _F, _P, _P]),
+    "kvattn_validate": (ctypes.c_int, [_CP, _I32, _P, _I32, _P, _P, _I32, _P, _P]),
+}
+
+
+def lib():
+    """The loaded library.  Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkvattn.so is not built (%s); run __graft_entry__.build() or "
+                               "python -m kv_cache_decode_attn_amd.build" % LIB_PATH)
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def check(status):
+    if status != OK:
+        raise KvattnError(status, lib().kvattn_last_error().decode())
+    return status

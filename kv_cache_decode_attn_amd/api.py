@@ -1,0 +1,239 @@
+"""Torch-facing binding of libkvattn: the same calls as include/kvattn.h.
+
+Argument marshalling only - tensors become device pointers, the current
+torch stream becomes the HIP stream, and every step of the computation runs
+in the library's HIP kernels.  PyTorch provides device memory (outputs and
+workspaces are allocated here when the caller does not pass them).  There is
+no fallback: without the built library or on CPU tensors these raise.
+"""
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import BF16, CONTIGUOUS, F32, FP8_E4M3, PAGED, BLOCK_TOKENS, check, lib
+
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.uint8}
+_CODE = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device (cuda/hip) tensor, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _i32(t, name):
+    t = _dev(t, name)
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError("%s must be int32" % name)
+    return t
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class KVCache:
+    """One layer's KV cache in device memory plus its layout.
+
+    contiguous: k, v of shape [rows, num_kv_heads, capacity, head_dim]
+    paged:      k, v of shape [num_blocks, num_kv_heads, 16, head_dim]
+    dtype is F32, BF16 or FP8_E4M3 (fp8 codes are stored in uint8 tensors and
+    need k_scale / v_scale, fp32 [num_kv_heads]).
+    """
+
+    def __init__(self, k, v, layout, dtype, k_scale=None, v_scale=None):
+        _dev(k, "k")
+        _dev(v, "v")
+        if k.shape != v.shape or k.dim() != 4:
+            raise ValueError("k and v must be 4-D tensors of one shape")
+        if k.dtype != _TORCH_DTYPE[dtype] or v.dtype != _TORCH_DTYPE[dtype]:
+            raise TypeError("storage dtype %s does not match cache dtype %d" % (k.dtype, dtype))
+        if dtype == FP8_E4M3:
+            for s, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+                _dev(s, n)
+                if s is None or s.dtype != torch.float32 or s.numel() != k.shape[1]:
+                    raise ValueError("%s must be fp32 [num_kv_heads]" % n)
+        self.k, self.v, self.layout, self.dtype = k, v, layout, dtype
+        self.k_scale, self.v_scale = k_scale, v_scale
+        self.num_kv_heads = k.shape[1]
+        self.head_dim = k.shape[3]
+        if layout == PAGED and k.shape[2] != BLOCK_TOKENS:
+            raise ValueError("paged pools hold 16 positions per block")
+
+    @classmethod
+    def contiguous(cls, rows, num_kv_heads, capacity, head_dim, dtype, device="cuda", k_scale=None,
+                   v_scale=None, fill=None):
+        shape = (rows, num_kv_heads, capacity, head_dim)
+        k = torch.empty(shape, dtype=_TORCH_DTYPE[dtype], device=device)
+        v = torch.empty(shape, dtype=_TORCH_DTYPE[dtype], device=device)
+        if fill is not None:
+            k.fill_(fill)
+            v.fill_(fill)
+        return cls(k, v, CONTIGUOUS, dtype, k_scale, v_scale)
+
+    @classmethod
+    def paged(cls, num_blocks, num_kv_heads, head_dim, dtype, device="cuda", k_scale=None, v_scale=None,
+              fill=None):
+        shape = (num_blocks, num_kv_heads, BLOCK_TOKENS, head_dim)
+        k = torch.empty(shape, dtype=_TORCH_DTYPE[dtype], device=device)
+        v = torch.empty(shape, dtype=_TORCH_DTYPE[dtype], device=device)
+        if fill is not None:
+            k.fill_(fill)
+            v.fill_(fill)
+        return cls(k, v, PAGED, dtype, k_scale, v_scale)
+
+    @property
+    def device(self):
+        return self.k.device
+
+    def desc(self):
+        d = _lib.KvattnCache()
+        d.dtype = self.dtype
+        d.layout = self.layout
+        d.num_kv_heads = self.num_kv_heads
+        d.head_dim = self.head_dim
+        if self.layout == CONTIGUOUS:
+            d.capacity = self.k.shape[2]
+            d.num_rows = self.k.shape[0]
+        else:
+            d.num_blocks = self.k.shape[0]
+        d.k = self.k.data_ptr()
+        d.v = self.v.data_ptr()
+        d.k_scale = self.k_scale.data_ptr() if self.k_scale is not None else None
+        d.v_scale = self.v_scale.data_ptr() if self.v_scale is not None else None
+        return d
+
+
+def version():
+    return lib().kvattn_version().decode()
+
+
+def cache_bytes(layers, batch, kv_heads, seq, head_dim, elem_bytes):
+    return int(lib().kvattn_cache_bytes(layers, batch, kv_heads, seq, head_dim, elem_bytes))
+
+
+def kv_append(cache, k_new, v_new, positions, block_table=None, n_valid=None):
+    """Write k_new/v_new [B, Hkv, n_new, d] at positions[b] + i (kvattn_kv_append)."""
+    _dev(k_new, "k_new")
+    _dev(v_new, "v_new")
+    _i32(positions, "positions")
+    _i32(block_table, "block_table")
+    _i32(n_valid, "n_valid")
+    if k_new.dtype not in _CODE or v_new.dtype != k_new.dtype or k_new.shape != v_new.shape:
+        raise TypeError("k_new/v_new must be matching f32 or bf16 tensors")
+    B, H, n, d = k_new.shape
+    if H != cache.num_kv_heads or d != cache.head_dim:
+        raise ValueError("k_new shape %s does not match the cache" % (tuple(k_new.shape),))
+    mb = block_table.shape[1] if block_table is not None else 0
+    check(lib().kvattn_kv_append(ctypes.byref(cache.desc()), B, n, _ptr(k_new), _ptr(v_new), _CODE[k_new.dtype],
+                                 _ptr(positions), _ptr(n_valid), _ptr(block_table), mb, _stream(k_new.device)))
+
+
+def decode_default_part_tokens(batch, num_q_heads, num_kv_heads, max_seq_len):
+    return int(lib().kvattn_decode_default_part_tokens(batch, num_q_heads, num_kv_heads, max_seq_len))
+
+
+def decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, part_tokens=0):
+    return int(lib().kvattn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                   part_tokens))
+
+
+def decode_workspace(cache, batch, num_q_heads, max_seq_len, part_tokens=0):
+    """A workspace tensor large enough for attn_decode with these sizes."""
+    n = decode_workspace_bytes(batch, num_q_heads, cache.num_kv_heads, cache.head_dim, max_seq_len, part_tokens)
+    return torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device=cache.device)
+
+
+def attn_decode(cache, q, seq_lens, max_seq_len, block_table=None, key_mask=None, scale=None, out=None,
+                workspace=None, part_tokens=0):
+    """One query token per sequence against the cache (kvattn_attn_decode).
+
+    q: [B, Hq, d] (f32 for an f32 cache, bf16 otherwise); seq_lens int32 [B]
+    counts keys including the appended token; key_mask uint8 [B, >= max_seq_len]
+    (1 = attend) or None.  Returns fp32 [B, Hq, d].
+    """
+    _dev(q, "q")
+    _i32(seq_lens, "seq_lens")
+    _i32(block_table, "block_table")
+    _dev(key_mask, "key_mask")
+    if key_mask is not None and key_mask.dtype != torch.uint8:
+        raise TypeError("key_mask must be uint8")
+    B, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _dev(out, "out")
+    if workspace is None:
+        workspace = decode_workspace(cache, B, Hq, max_seq_len, part_tokens)
+    _dev(workspace, "workspace")
+    qcode = _CODE.get(q.dtype, -1)
+    mb = block_table.shape[1] if block_table is not None else 0
+    stride = key_mask.shape[1] if key_mask is not None else 0
+    check(lib().kvattn_attn_decode(ctypes.byref(cache.desc()), B, Hq, _ptr(q), qcode, _ptr(seq_lens), int(max_seq_len),
+                                   _ptr(block_table), mb, _ptr(key_mask), stride, float(scale), _ptr(out),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), int(part_tokens),
+                                   _stream(q.device)))
+    return out
+
+
+def attn_prefill(q, k, v, cache=None, positions=None, q_lens=None, block_table=None, key_mask=None, causal=True,
+                 attend_prefix=False, scale=None, out=None):
+    """Attention of n_max new tokens per sequence (kvattn_attn_prefill).
+
+    q: [B, Hq, n_max, d]; k, v: [B, Hkv, n_max, d] (f32 or bf16).  With a cache
+    the new K/V are written at positions[b] + t; attend_prefix also attends
+    the cached positions < positions[b].  Returns fp32 [B, Hq, n_max, d].
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    _i32(positions, "positions")
+    _i32(q_lens, "q_lens")
+    _i32(block_table, "block_table")
+    _dev(key_mask, "key_mask")
+    if key_mask is not None and key_mask.dtype != torch.uint8:
+        raise TypeError("key_mask must be uint8")
+    if q.dtype not in _CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype, f32 or bf16")
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, n, d) or v.shape != k.shape:
+        raise ValueError("k/v shape %s incompatible with q %s" % (tuple(k.shape), tuple(q.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, n, d), dtype=torch.float32, device=q.device)
+    _dev(out, "out")
+    desc = ctypes.byref(cache.desc()) if cache is not None else None
+    mb = block_table.shape[1] if block_table is not None else 0
+    stride = key_mask.shape[1] if key_mask is not None else 0
+    check(lib().kvattn_attn_prefill(desc, B, Hq, Hkv, d, n, _ptr(q), _ptr(k), _ptr(v), _CODE[q.dtype], _ptr(positions),
+                                    _ptr(q_lens), _ptr(block_table), mb, _ptr(key_mask), stride, int(bool(causal)),
+                                    int(bool(attend_prefix)), float(scale), _ptr(out), _stream(q.device)))
+    return out
+
+
+def validate(cache, seq_lens, max_seq_len, positions=None, block_table=None):
+    """Device check of the cache metadata contract (kvattn_validate).
+    Returns the OR of VALIDATE_* bits (synchronises the stream to read it)."""
+    _i32(seq_lens, "seq_lens")
+    _i32(positions, "positions")
+    _i32(block_table, "block_table")
+    err = torch.zeros(1, dtype=torch.int32, device=seq_lens.device)
+    mb = block_table.shape[1] if block_table is not None else 0
+    check(lib().kvattn_validate(ctypes.byref(cache.desc()), seq_lens.shape[0], _ptr(seq_lens), int(max_seq_len),
+                                _ptr(positions), _ptr(block_table), mb, _ptr(err), _stream(seq_lens.device)))
+    return int(err.item())

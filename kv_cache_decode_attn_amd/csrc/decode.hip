@@ -1,0 +1,413 @@
+// Single-token decode attention against one layer's KV cache (gfx950).
+//
+// What is computed: for each sequence b and query head h, the softmax over
+// the cached keys (including the token just appended) of scale * q.k,
+// applied to the cached values ("Transformer Attention Masks and KV-Cache
+// Inference" (c86j224s.github.io), sections "State of scaled dot-product
+// attention" and "Prefill and decode stages"; "KV Cache" (heepie.pages.dev),
+// section "TO-BE").  Decode is bound by reading the cache from HBM
+// ("KV Cache", section "Prefill and Decode": decode is memory-bandwidth
+// bound), so the kernels are organised around streaming K and V once.
+//
+// Pass 1 (decode_partition): one workgroup of 4 waves per (partition of
+// part_tokens keys, KV head, sequence).  All G query heads of the KV head's
+// group are served by the same workgroup, so each K/V byte is read once per
+// group ("KV Cache Fully Explained", section "(2) GQA").
+//   phase 1  every wave streams 16-token blocks of K with 16-byte (8-byte for
+//            fp8) coalesced loads: lane (row, col) holds EPL elements of one
+//            token row; dot products with the G queries are reduced over the
+//            LPT lanes of a row with DPP row operations; scores go to LDS.
+//   phase 2  per query head, the partition's max and sum of exp2(z - max)
+//            (the score scale carries log2 e); weights replace the scores.
+//   phase 3  the waves stream the same blocks of V and accumulate
+//            o[h] += w * v in fp32 registers, then reduce across rows (lane
+//            shuffles) and waves (LDS).
+//   The partition's (max, sum, unnormalised o) is its split-K partial; a
+//   sequence that fits in one partition is normalised and written directly.
+// Pass 2 (decode_merge): per (sequence, query head), the partials are merged
+// with the exact running max/sum renormalisation of "KV Cache, Flash
+// Attention and Inference Optimization" (factory.pai-world.com), section
+// "Flash Attention", numerical trick.
+#include <math.h>
+
+#include "launch.h"
+
+namespace kvattn {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int KVT>
+struct Traits;
+
+// fp32 cache: 16-byte loads of 4 elements; q kept as fp32.
+template <>
+struct Traits<KVATTN_F32> {
+  static constexpr int EPL = 4;
+  typedef U4 Raw;
+  __device__ static void to_f32(const Raw& r, float* f) {
+    f[0] = __uint_as_float(r.x);
+    f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z);
+    f[3] = __uint_as_float(r.w);
+  }
+};
+
+// bf16 cache: 16-byte loads of 8 elements; q kept as packed bf16 pairs so
+// the dot product runs on v_dot2_f32_bf16 (fp32 accumulate) without
+// unpacking K.
+template <>
+struct Traits<KVATTN_BF16> {
+  static constexpr int EPL = 8;
+  typedef U4 Raw;
+  __device__ static void to_f32(const Raw& r, float* f) {
+    f[0] = bf16_lo(r.x);
+    f[1] = bf16_hi(r.x);
+    f[2] = bf16_lo(r.y);
+    f[3] = bf16_hi(r.y);
+    f[4] = bf16_lo(r.z);
+    f[5] = bf16_hi(r.z);
+    f[6] = bf16_lo(r.w);
+    f[7] = bf16_hi(r.w);
+  }
+};
+
+// fp8 cache: 8-byte loads of 8 codes, decoded exactly to fp32.
+template <>
+struct Traits<KVATTN_FP8_E4M3> {
+  static constexpr int EPL = 8;
+  typedef U2 Raw;
+  __device__ static void to_f32(const Raw& r, float* f) {
+    fp8x4_to_f32(r.x, f);
+    fp8x4_to_f32(r.y, f + 4);
+  }
+};
+
+// Query fragment of one lane: the EPL elements [col*EPL, col*EPL+EPL) of
+// each of the G query heads of the group.
+template <int KVT, int G>
+struct QFrag {
+  float f[G][Traits<KVT>::EPL];
+  __device__ void load(const uint8_t* q, int64_t row0, int D, int col) {
+    // q is fp32 for an fp32 cache, bf16 otherwise
+    constexpr int EPL = Traits<KVT>::EPL;
+    for (int h = 0; h < G; ++h) {
+      if constexpr (KVT == KVATTN_F32) {
+        const U4 r = *reinterpret_cast<const U4*>(q + ((row0 + h) * D + col * EPL) * 4);
+        Traits<KVATTN_F32>::to_f32(r, f[h]);
+      } else {
+        const U4 r = *reinterpret_cast<const U4*>(q + ((row0 + h) * D + col * EPL) * 2);
+        Traits<KVATTN_BF16>::to_f32(r, f[h]);
+      }
+    }
+  }
+  __device__ float dot(int h, const float* k) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < Traits<KVT>::EPL; ++e) acc = fmaf(f[h][e], k[e], acc);
+    return acc;
+  }
+};
+
+template <int G>
+struct QFrag<KVATTN_BF16, G> {
+  uint32_t w[G][4];
+  __device__ void load(const uint8_t* q, int64_t row0, int D, int col) {
+    for (int h = 0; h < G; ++h) {
+      const U4 r = *reinterpret_cast<const U4*>(q + ((row0 + h) * D + col * 8) * 2);
+      w[h][0] = r.x;
+      w[h][1] = r.y;
+      w[h][2] = r.z;
+      w[h][3] = r.w;
+    }
+  }
+  __device__ float dot_raw(int h, const U4& k) const {
+    float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[h][0]),
+                                                __builtin_bit_cast(bf16x2_t, k.x), 0.f, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[h][1]),
+                                          __builtin_bit_cast(bf16x2_t, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[h][2]),
+                                          __builtin_bit_cast(bf16x2_t, k.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[h][3]),
+                                          __builtin_bit_cast(bf16x2_t, k.w), acc, false);
+    return acc;
+  }
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;
+
+// LDS floats the partition kernel needs.
+__host__ __device__ constexpr int decode_lds_floats(int T, int G, int D) {
+  return ((T * G > kWaves * G * D) ? T * G : kWaves * G * D) + 2 * G;
+}
+
+template <int KVT, int D, int G, bool MASK>
+__global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
+  using TR = Traits<KVT>;
+  using Raw = typename TR::Raw;
+  constexpr int EPL = TR::EPL;
+  constexpr int LPT = D / EPL;        // lanes per token row
+  constexpr int TPI = kWave / LPT;    // token rows per wave-wide load
+  constexpr int NI = kBlockTokens / TPI;  // loads per 16-token block
+  static_assert(TPI * NI == kBlockTokens && NI >= 1, "row split");
+  constexpr int ROWB = D * (int)sizeof(Raw) / EPL;  // bytes per token row
+
+  extern __shared__ float lds[];
+  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane % LPT, row = lane / LPT;
+  const int T = p.part_tokens;
+  const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
+  const int hq0 = g * G;
+  const int t0 = part * T;
+  if (t0 >= ctx) {
+    // An empty sequence still has a defined output: zeros.
+    if (part == 0) {
+      for (int i = tid; i < G * D; i += 256)
+        p.out[((int64_t)b * p.num_q_heads + hq0) * D + i] = 0.f;
+    }
+    return;
+  }
+  const int t1 = min(t0 + T, ctx);
+  const int n = t1 - t0;
+  const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
+  const int j0 = t0 / kBlockTokens;
+
+  QFrag<KVT, G> q;
+  q.load(p.q, (int64_t)b * p.num_q_heads + hq0, D, col);
+  float zscale = p.scale * kLog2e;
+  if constexpr (KVT == KVATTN_FP8_E4M3) zscale *= p.k_scale[g];
+
+  float* s_lds = lds;                                   // [T][G] scores -> weights
+  float* stat = lds + decode_lds_floats(T, G, D) - 2 * G;  // [G][2] (max, sum)
+  const uint8_t* mask_row = MASK ? p.key_mask + (int64_t)b * p.key_mask_stride : nullptr;
+
+  // ---- phase 1: scores of every key of the partition ----
+  for (int jb = wave; jb < nblk; jb += kWaves) {
+    const int j = j0 + jb;
+    const int64_t off = block_offset(p.c, b, g, j);
+    Raw raw[NI];
+    if (off >= 0) {
+      const uint8_t* base = p.c.k + off + row * ROWB + col * (int)sizeof(Raw);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) raw[i] = *reinterpret_cast<const Raw*>(base + i * TPI * ROWB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) raw[i] = Raw{};
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int tok = j * kBlockTokens + i * TPI + row;
+      float acc[G];
+      if constexpr (KVT == KVATTN_BF16) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = q.dot_raw(h, raw[i]);
+      } else {
+        float kf[EPL];
+        TR::to_f32(raw[i], kf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = q.dot(h, kf);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = group_sum<LPT>(acc[h]);
+      if (tok < t1) {
+        bool valid = off >= 0;
+        if constexpr (MASK) valid = valid && mask_row[tok] != 0;
+        if (col == 0) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) s_lds[(tok - t0) * G + h] = valid ? acc[h] * zscale : -INFINITY;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: per-head max and sum; scores -> weights exp2(z - max) ----
+  for (int h = wave; h < G; h += kWaves) {
+    float m = -INFINITY;
+    for (int t = lane; t < n; t += kWave) m = fmaxf(m, s_lds[t * G + h]);
+    m = group_max<64>(m);
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    float l = 0.f;
+    for (int t = lane; t < n; t += kWave) {
+      const float e = exp2f(s_lds[t * G + h] - mref);
+      s_lds[t * G + h] = e;
+      l += e;
+    }
+    l = group_sum<64>(l);
+    if (lane == 0) {
+      stat[2 * h] = m;
+      stat[2 * h + 1] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: o[h] += w * v over the same blocks ----
+  float o[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+
+  for (int jb = wave; jb < nblk; jb += kWaves) {
+    const int j = j0 + jb;
+    const int64_t off = block_offset(p.c, b, g, j);
+    if (off < 0) continue;  // a block outside the cache was fully masked
+    const uint8_t* base = p.c.v + off + row * ROWB + col * (int)sizeof(Raw);
+    Raw raw[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) raw[i] = *reinterpret_cast<const Raw*>(base + i * TPI * ROWB);
+    // A block wholly inside the partition with no key mask has only live
+    // keys; otherwise a key with zero weight for every head is dropped so
+    // that non-finite bytes in padding or stale slots cannot reach o.
+    const bool full = !MASK && (j + 1) * kBlockTokens <= t1;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int tok = j * kBlockTokens + i * TPI + row;
+      float w[G];
+      bool live = true;
+      if (full) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) w[h] = s_lds[(tok - t0) * G + h];
+      } else {
+        live = false;
+        const bool in = tok < t1;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          w[h] = in ? s_lds[(tok - t0) * G + h] : 0.f;
+          live = live || (w[h] != 0.f);
+        }
+      }
+      float vf[EPL];
+      TR::to_f32(raw[i], vf);
+      if (!live) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(w[h], vf[e], o[h][e]);
+    }
+  }
+
+  // reduce over the TPI rows of the wave (lanes sharing col)
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = strided_sum<LPT>(o[h][e]);
+
+  __syncthreads();  // every wave is done reading weights; reuse LDS
+  float* red = lds;  // [kWaves][G][D]
+  if (row == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red[(wave * G + h) * D + col * EPL + e] = o[h][e];
+  }
+  __syncthreads();
+
+  const int nparts_b = (ctx + T - 1) / T;
+  float vscale = 1.f;
+  if constexpr (KVT == KVATTN_FP8_E4M3) vscale = p.v_scale[g];
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx - h * D;
+    float acc = red[(0 * G + h) * D + d];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) acc += red[(w * G + h) * D + d];
+    acc *= vscale;
+    const int hq = hq0 + h;
+    const float l = stat[2 * h + 1];
+    if (nparts_b == 1) {
+      p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = (l > 0.f) ? acc / l : 0.f;
+    } else {
+      const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.num_parts + part;
+      p.ws_o[slot * D + d] = acc;
+      if (d == 0) {
+        p.ws_ml[slot * 2] = stat[2 * h];
+        p.ws_ml[slot * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+// Merge the split-K partials of one (sequence, query head).
+template <int D>
+__global__ void __launch_bounds__(128) decode_merge(const DecodeLaunch p) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int T = p.part_tokens;
+  const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
+  const int np = (ctx + T - 1) / T;
+  if (np <= 1) return;  // written by the partition pass
+  const int64_t slot0 = ((int64_t)b * p.num_q_heads + hq) * p.num_parts;
+  const float* ml = p.ws_ml + slot0 * 2;
+  float M = -INFINITY;
+  for (int i = 0; i < np; ++i) M = fmaxf(M, ml[2 * i]);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.f, L = 0.f;
+    for (int i = 0; i < np; ++i) {
+      const float m = ml[2 * i];
+      if (m == -INFINITY) continue;
+      const float w = exp2f(m - M);
+      L = fmaf(w, ml[2 * i + 1], L);
+      acc = fmaf(w, p.ws_o[(slot0 + i) * D + d], acc);
+    }
+    p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = (L > 0.f) ? acc / L : 0.f;
+  }
+}
+
+template <int KVT, int D, int G, bool MASK>
+int launch_typed(const DecodeLaunch& a, hipStream_t s) {
+  const dim3 grid(a.num_parts, a.num_kv_heads, a.batch);
+  const size_t lds = (size_t)decode_lds_floats(a.part_tokens, G, D) * sizeof(float);
+  hipLaunchKernelGGL((decode_partition<KVT, D, G, MASK>), grid, dim3(256), lds, s, a);
+  if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
+  if (a.num_parts > 1) {
+    hipLaunchKernelGGL((decode_merge<D>), dim3(a.num_q_heads, a.batch), dim3(128), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
+  }
+  return KVATTN_OK;
+}
+
+template <int KVT, int D, int G>
+int launch_mask(const DecodeLaunch& a, hipStream_t s) {
+  return a.key_mask ? launch_typed<KVT, D, G, true>(a, s) : launch_typed<KVT, D, G, false>(a, s);
+}
+
+template <int KVT, int D>
+int launch_group(const DecodeLaunch& a, hipStream_t s) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_mask<KVT, D, 1>(a, s);
+    case 2: return launch_mask<KVT, D, 2>(a, s);
+    case 4: return launch_mask<KVT, D, 4>(a, s);
+    case 8: return launch_mask<KVT, D, 8>(a, s);
+    default: return KVATTN_EUNSUPPORTED;
+  }
+}
+
+template <int KVT>
+int launch_dim(const DecodeLaunch& a, hipStream_t s) {
+  switch (a.head_dim) {
+    case 64: return launch_group<KVT, 64>(a, s);
+    case 128: return launch_group<KVT, 128>(a, s);
+    default: return KVATTN_EUNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+int decode_lds_bytes(int part_tokens, int group, int head_dim) {
+  return decode_lds_floats(part_tokens, group, head_dim) * (int)sizeof(float);
+}
+
+int launch_decode(const DecodeLaunch& a, hipStream_t s) {
+  switch (a.cache_dtype) {
+    case KVATTN_F32: return launch_dim<KVATTN_F32>(a, s);
+    case KVATTN_BF16: return launch_dim<KVATTN_BF16>(a, s);
+    case KVATTN_FP8_E4M3: return launch_dim<KVATTN_FP8_E4M3>(a, s);
+    default: return KVATTN_EUNSUPPORTED;
+  }
+}
+
+}  // namespace kvattn

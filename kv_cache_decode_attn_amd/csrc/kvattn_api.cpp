@@ -1,0 +1,366 @@
+// C ABI of the kvattn library: host-side argument checks, launch geometry and
+// workspace sizing.  No allocation, no synchronisation: every call enqueues
+// on the caller's stream and returns.  See include/kvattn.h for the
+// contract of each entry point.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kvattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return KVATTN_OK;
+}
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case KVATTN_F32: return 4;
+    case KVATTN_BF16: return 2;
+    case KVATTN_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int group_ok(int32_t hq, int32_t hkv) {
+  if (hkv < 1 || hq < 1 || hq % hkv != 0) return 0;
+  const int g = hq / hkv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+// Fills the kernels' view of a cache descriptor; also returns the number of
+// positions a sequence can hold.
+int make_view(const char* who, const kvattn_cache* c, int32_t batch, const int32_t* block_table,
+              int32_t max_blocks, kvattn::CacheView* v, int64_t* cap_tokens) {
+  if (!c) return fail(KVATTN_EINVAL, "%s: cache descriptor is NULL", who);
+  const int eb = elem_bytes(c->dtype);
+  if (!eb) return fail(KVATTN_EINVAL, "%s: unknown cache dtype %d", who, c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(KVATTN_EUNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", who, c->head_dim);
+  if (c->num_kv_heads < 1 || c->num_kv_heads > 65535)
+    return fail(KVATTN_EINVAL, "%s: num_kv_heads %d out of range", who, c->num_kv_heads);
+  if (!c->k || !c->v) return fail(KVATTN_EINVAL, "%s: cache k/v pointer is NULL", who);
+  if (!aligned16(c->k) || !aligned16(c->v)) return fail(KVATTN_EINVAL, "%s: cache k/v not 16-byte aligned", who);
+  if (c->dtype == KVATTN_FP8_E4M3 && (!c->k_scale || !c->v_scale))
+    return fail(KVATTN_EINVAL, "%s: fp8 cache needs k_scale and v_scale", who);
+  const int64_t row = (int64_t)c->head_dim * eb;
+  *v = kvattn::CacheView{};
+  v->k = static_cast<uint8_t*>(c->k);
+  v->v = static_cast<uint8_t*>(c->v);
+  v->row_stride = row;
+  if (c->layout == KVATTN_CONTIGUOUS) {
+    if (c->capacity <= 0 || c->capacity % KVATTN_BLOCK_TOKENS != 0 || c->capacity > (int64_t)1 << 30)
+      return fail(KVATTN_EINVAL, "%s: contiguous capacity %lld must be a positive multiple of 16 (<= 2^30)",
+                  who, (long long)c->capacity);
+    if (c->num_rows < batch)
+      return fail(KVATTN_EINVAL, "%s: contiguous cache has %lld rows < batch %d", who, (long long)c->num_rows, batch);
+    v->head_stride = c->capacity * row;
+    v->seq_stride = c->num_kv_heads * v->head_stride;
+    v->capacity = c->capacity;
+    v->paged = 0;
+    *cap_tokens = c->capacity;
+  } else if (c->layout == KVATTN_PAGED) {
+    if (c->num_blocks <= 0 || c->num_blocks > INT32_MAX)
+      return fail(KVATTN_EINVAL, "%s: paged cache num_blocks %lld out of range", who, (long long)c->num_blocks);
+    if (!block_table) return fail(KVATTN_EINVAL, "%s: paged cache needs a block_table", who);
+    if (max_blocks <= 0 || max_blocks > (1 << 26))
+      return fail(KVATTN_EINVAL, "%s: max_blocks %d out of range", who, max_blocks);
+    v->head_stride = (int64_t)KVATTN_BLOCK_TOKENS * row;
+    v->block_stride = c->num_kv_heads * v->head_stride;
+    v->num_blocks = c->num_blocks;
+    v->block_table = block_table;
+    v->max_blocks = max_blocks;
+    v->paged = 1;
+    *cap_tokens = (int64_t)max_blocks * KVATTN_BLOCK_TOKENS;
+  } else {
+    return fail(KVATTN_EINVAL, "%s: unknown layout %d", who, c->layout);
+  }
+  return KVATTN_OK;
+}
+
+constexpr int32_t kMaxPartTokens = 8192;
+constexpr int32_t kMaxPartScores = 8192;  // part_tokens * group, bounds the LDS
+
+int32_t default_part_tokens(int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len) {
+  const int32_t group = hq / hkv;
+  int32_t t = 512;
+  while (t * group > kMaxPartScores) t /= 2;
+  // Shrink the partition until the grid offers >= 2048 workgroups.
+  while (t > 64) {
+    const int64_t parts = ((int64_t)max_seq_len + t - 1) / t;
+    if ((int64_t)batch * hkv * parts >= 2048) break;
+    t /= 2;
+  }
+  return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvattn_version(void) { return "kvattn 0.1.0 gfx950"; }
+
+const char* kvattn_status_string(int status) {
+  switch (status) {
+    case KVATTN_OK: return "ok";
+    case KVATTN_EINVAL: return "invalid argument";
+    case KVATTN_EUNSUPPORTED: return "unsupported configuration";
+    case KVATTN_EWORKSPACE: return "workspace missing or too small";
+    case KVATTN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* kvattn_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t kvattn_cache_bytes(uint64_t layers, uint64_t batch, uint64_t kv_heads, uint64_t seq,
+                            uint64_t head_dim, uint64_t elem_bytes) {
+  uint64_t r = 2;
+  const uint64_t f[6] = {layers, batch, kv_heads, seq, head_dim, elem_bytes};
+  for (uint64_t x : f)
+    if (__builtin_mul_overflow(r, x, &r)) return 0;
+  return r;
+}
+
+int kvattn_kv_append(const kvattn_cache* cache, int32_t batch, int32_t n_new, const void* k_new,
+                     const void* v_new, int32_t in_dtype, const int32_t* positions, const int32_t* n_valid,
+                     const int32_t* block_table, int32_t max_blocks, void* stream) {
+  const char* who = "kvattn_kv_append";
+  if (batch < 0 || n_new < 0) return fail(KVATTN_EINVAL, "%s: negative batch or n_new", who);
+  if (batch > 65535) return fail(KVATTN_EINVAL, "%s: batch %d too large", who, batch);
+  kvattn::CacheView view;
+  int64_t cap = 0;
+  int rc = make_view(who, cache, batch, block_table, max_blocks, &view, &cap);
+  if (rc) return rc;
+  if (in_dtype != KVATTN_F32 && in_dtype != KVATTN_BF16)
+    return fail(KVATTN_EINVAL, "%s: input dtype must be f32 or bf16", who);
+  if (in_dtype != cache->dtype && cache->dtype != KVATTN_FP8_E4M3)
+    return fail(KVATTN_EUNSUPPORTED, "%s: input dtype %d does not match cache dtype %d", who, in_dtype,
+                cache->dtype);
+  if ((int64_t)batch * n_new == 0) return ok();
+  if (!k_new || !v_new || !positions) return fail(KVATTN_EINVAL, "%s: k_new, v_new and positions are required", who);
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(KVATTN_EINVAL, "%s: k_new/v_new not 16-byte aligned", who);
+  kvattn::AppendLaunch a{};
+  a.c = view;
+  a.cache_dtype = cache->dtype;
+  a.in_dtype = in_dtype;
+  a.head_dim = cache->head_dim;
+  a.batch = batch;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.n_new = n_new;
+  a.k_new = static_cast<const uint8_t*>(k_new);
+  a.v_new = static_cast<const uint8_t*>(v_new);
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.positions = positions;
+  a.n_valid = n_valid;
+  rc = kvattn::launch_append(a, static_cast<hipStream_t>(stream));
+  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
+  return ok();
+}
+
+int32_t kvattn_decode_default_part_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t max_seq_len) {
+  if (batch < 0 || max_seq_len < 0 || !group_ok(num_q_heads, num_kv_heads)) return 0;
+  return default_part_tokens(batch, num_q_heads, num_kv_heads, max_seq_len);
+}
+
+size_t kvattn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t max_seq_len, int32_t part_tokens) {
+  if (batch < 0 || max_seq_len < 0 || head_dim <= 0 || !group_ok(num_q_heads, num_kv_heads)) return 0;
+  const int32_t t = part_tokens ? part_tokens : default_part_tokens(batch, num_q_heads, num_kv_heads, max_seq_len);
+  if (t <= 0) return 0;
+  const int64_t parts = ((int64_t)max_seq_len + t - 1) / t;
+  if (parts <= 1) return 0;
+  return (size_t)batch * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+}
+
+int kvattn_attn_decode(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, const void* q,
+                       int32_t q_dtype, const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                       int32_t max_blocks, const uint8_t* key_mask, int64_t key_mask_stride, float scale,
+                       float* out, void* workspace, size_t workspace_bytes, int32_t part_tokens, void* stream) {
+  const char* who = "kvattn_attn_decode";
+  if (batch < 0 || batch > 65535) return fail(KVATTN_EINVAL, "%s: batch %d out of range", who, batch);
+  kvattn::CacheView view;
+  int64_t cap = 0;
+  int rc = make_view(who, cache, batch, block_table, max_blocks, &view, &cap);
+  if (rc) return rc;
+  if (!group_ok(num_q_heads, cache->num_kv_heads))
+    return fail(KVATTN_EUNSUPPORTED, "%s: %d query heads over %d KV heads: group must be 1, 2, 4 or 8", who,
+                num_q_heads, cache->num_kv_heads);
+  const int32_t want_q = (cache->dtype == KVATTN_F32) ? KVATTN_F32 : KVATTN_BF16;
+  if (q_dtype != want_q)
+    return fail(KVATTN_EUNSUPPORTED, "%s: q dtype %d; this cache needs %s queries", who, q_dtype,
+                want_q == KVATTN_F32 ? "f32" : "bf16");
+  if (max_seq_len < 0) return fail(KVATTN_EINVAL, "%s: max_seq_len < 0", who);
+  if (batch == 0) return ok();
+  if (!q || !seq_lens || !out) return fail(KVATTN_EINVAL, "%s: q, seq_lens and out are required", who);
+  if (!aligned16(q) || !aligned16(out)) return fail(KVATTN_EINVAL, "%s: q/out not 16-byte aligned", who);
+  if (key_mask && key_mask_stride < max_seq_len)
+    return fail(KVATTN_EINVAL, "%s: key_mask_stride %lld < max_seq_len %d", who, (long long)key_mask_stride,
+                max_seq_len);
+  const int32_t group = num_q_heads / cache->num_kv_heads;
+  int32_t t = part_tokens;
+  if (t == 0) t = default_part_tokens(batch, num_q_heads, cache->num_kv_heads, max_seq_len);
+  if (t < 64 || t > kMaxPartTokens || t % 64 != 0 || t * group > kMaxPartScores)
+    return fail(KVATTN_EINVAL, "%s: part_tokens %d: need a multiple of 64 in [64, %d] with part_tokens*group <= %d",
+                who, t, kMaxPartTokens, kMaxPartScores);
+  const int64_t parts = ((int64_t)max_seq_len + t - 1) / t;
+  if (parts > 65535) return fail(KVATTN_EINVAL, "%s: too many partitions (%lld)", who, (long long)parts);
+  float* ws_o = nullptr;
+  float* ws_ml = nullptr;
+  if (parts > 1) {
+    const size_t need = kvattn_decode_workspace_bytes(batch, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                                      max_seq_len, t);
+    if (!workspace || workspace_bytes < need)
+      return fail(KVATTN_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", who, workspace ? workspace_bytes : 0,
+                  need);
+    if (!aligned16(workspace)) return fail(KVATTN_EINVAL, "%s: workspace not 16-byte aligned", who);
+    ws_o = static_cast<float*>(workspace);
+    ws_ml = ws_o + (size_t)batch * num_q_heads * parts * cache->head_dim;
+  }
+  kvattn::DecodeLaunch a{};
+  a.c = view;
+  a.cache_dtype = cache->dtype;
+  a.head_dim = cache->head_dim;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.q = static_cast<const uint8_t*>(q);
+  a.seq_lens = seq_lens;
+  a.ctx_limit = (int32_t)(cap < max_seq_len ? cap : max_seq_len);
+  a.key_mask = key_mask;
+  a.key_mask_stride = key_mask_stride;
+  a.scale = scale;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.out = out;
+  a.ws_o = ws_o;
+  a.ws_ml = ws_ml;
+  a.part_tokens = t;
+  a.num_parts = (int32_t)(parts < 1 ? 1 : parts);
+  rc = kvattn::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
+  return ok();
+}
+
+int kvattn_attn_prefill(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t n_max, const void* q, const void* k, const void* v, int32_t dtype,
+                        const int32_t* positions, const int32_t* q_lens, const int32_t* block_table,
+                        int32_t max_blocks, const uint8_t* key_mask, int64_t key_mask_stride, int32_t causal,
+                        int32_t attend_prefix, float scale, float* out, void* stream) {
+  const char* who = "kvattn_attn_prefill";
+  if (batch < 0 || batch > 65535 || n_max < 0)
+    return fail(KVATTN_EINVAL, "%s: batch %d / n_max %d out of range", who, batch, n_max);
+  if (dtype != KVATTN_F32 && dtype != KVATTN_BF16) return fail(KVATTN_EINVAL, "%s: dtype must be f32 or bf16", who);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(KVATTN_EUNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", who, head_dim);
+  if (!group_ok(num_q_heads, num_kv_heads) || num_q_heads > 65535)
+    return fail(KVATTN_EUNSUPPORTED, "%s: %d query heads over %d KV heads: group must be 1, 2, 4 or 8", who,
+                num_q_heads, num_kv_heads);
+  kvattn::PrefillLaunch a{};
+  if (cache) {
+    int64_t cap = 0;
+    int rc = make_view(who, cache, batch, block_table, max_blocks, &a.c, &cap);
+    if (rc) return rc;
+    if (cache->num_kv_heads != num_kv_heads || cache->head_dim != head_dim)
+      return fail(KVATTN_EINVAL, "%s: cache shape (%d heads, d %d) differs from k/v (%d, %d)", who,
+                  cache->num_kv_heads, cache->head_dim, num_kv_heads, head_dim);
+    if (cache->dtype != dtype && cache->dtype != KVATTN_FP8_E4M3)
+      return fail(KVATTN_EUNSUPPORTED, "%s: dtype %d cannot be written to a cache of dtype %d", who, dtype,
+                  cache->dtype);
+    a.has_cache = 1;
+    a.cache_dtype = cache->dtype;
+    a.k_scale = cache->k_scale;
+    a.v_scale = cache->v_scale;
+  } else if (attend_prefix) {
+    return fail(KVATTN_EINVAL, "%s: attend_prefix needs a cache", who);
+  }
+  if ((int64_t)batch * n_max == 0) return ok();
+  if (!q || !k || !v || !out) return fail(KVATTN_EINVAL, "%s: q, k, v and out are required", who);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(KVATTN_EINVAL, "%s: q/k/v/out not 16-byte aligned", who);
+  if (key_mask && key_mask_stride < n_max)
+    return fail(KVATTN_EINVAL, "%s: key_mask_stride %lld < n_max %d", who, (long long)key_mask_stride, n_max);
+  a.dtype = dtype;
+  a.head_dim = head_dim;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.n_max = n_max;
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.positions = positions;
+  a.q_lens = q_lens;
+  a.key_mask = key_mask;
+  a.key_mask_stride = key_mask_stride;
+  a.causal = causal ? 1 : 0;
+  a.attend_prefix = attend_prefix ? 1 : 0;
+  a.scale = scale;
+  a.out = out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache) {
+    kvattn::AppendLaunch w{};
+    w.c = a.c;
+    w.cache_dtype = cache->dtype;
+    w.in_dtype = dtype;
+    w.head_dim = head_dim;
+    w.batch = batch;
+    w.num_kv_heads = num_kv_heads;
+    w.n_new = n_max;
+    w.k_new = a.k;
+    w.v_new = a.v;
+    w.k_scale = cache->k_scale;
+    w.v_scale = cache->v_scale;
+    w.positions = positions;
+    w.n_valid = q_lens;
+    int rc = kvattn::launch_append(w, s);
+    if (rc) return fail(rc, "%s: cache write: %s", who, kvattn_status_string(rc));
+  }
+  int rc = kvattn::launch_prefill(a, s);
+  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
+  return ok();
+}
+
+int kvattn_validate(const kvattn_cache* cache, int32_t batch, const int32_t* seq_lens, int32_t max_seq_len,
+                    const int32_t* positions, const int32_t* block_table, int32_t max_blocks, int32_t* err_word,
+                    void* stream) {
+  const char* who = "kvattn_validate";
+  if (batch < 0) return fail(KVATTN_EINVAL, "%s: batch < 0", who);
+  kvattn::ValidateLaunch a{};
+  int64_t cap = 0;
+  int rc = make_view(who, cache, batch, block_table, max_blocks, &a.c, &cap);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  if (!seq_lens || !err_word) return fail(KVATTN_EINVAL, "%s: seq_lens and err_word are required", who);
+  a.batch = batch;
+  a.seq_lens = seq_lens;
+  a.max_seq_len = max_seq_len;
+  a.cap_tokens = cap;
+  a.positions = positions;
+  a.err_word = err_word;
+  rc = kvattn::launch_validate(a, static_cast<hipStream_t>(stream));
+  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Internal launch interface between the C ABI layer (kvattn_api.cpp) and the
+// kernel translation units.  Host arguments are already validated when these
+// are called; each returns KVATTN_OK or KVATTN_EUNSUPPORTED / KVATTN_ELAUNCH.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace kvattn {
+
+struct AppendLaunch {
+  CacheView c;
+  int32_t cache_dtype;
+  int32_t in_dtype;
+  int32_t head_dim;
+  int32_t batch, num_kv_heads, n_new;
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* positions;  // may be NULL (all 0)
+  const int32_t* n_valid;    // may be NULL (all n_new)
+};
+int launch_append(const AppendLaunch& a, hipStream_t stream);
+
+struct DecodeLaunch {
+  CacheView c;
+  int32_t cache_dtype;
+  int32_t head_dim;
+  int32_t batch, num_q_heads, num_kv_heads;
+  const uint8_t* q;
+  const int32_t* seq_lens;
+  int32_t ctx_limit;  // min(max_seq_len, capacity in tokens)
+  const uint8_t* key_mask;
+  int64_t key_mask_stride;
+  float scale;
+  const float* k_scale;
+  const float* v_scale;
+  float* out;
+  float* ws_o;   // [batch, num_q_heads, num_parts, head_dim]
+  float* ws_ml;  // [batch, num_q_heads, num_parts, 2]
+  int32_t part_tokens;
+  int32_t num_parts;
+};
+int launch_decode(const DecodeLaunch& a, hipStream_t stream);
+// Dynamic LDS bytes of the decode partition kernel.
+int decode_lds_bytes(int part_tokens, int group, int head_dim);
+
+struct PrefillLaunch {
+  CacheView c;          // valid when has_cache
+  int32_t has_cache;
+  int32_t cache_dtype;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t dtype;        // of q, k, v
+  int32_t head_dim;
+  int32_t batch, num_q_heads, num_kv_heads, n_max;
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* positions;  // may be NULL
+  const int32_t* q_lens;     // may be NULL
+  const uint8_t* key_mask;
+  int64_t key_mask_stride;
+  int32_t causal, attend_prefix;
+  float scale;
+  float* out;
+};
+int launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+
+struct ValidateLaunch {
+  CacheView c;
+  int32_t batch;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int64_t cap_tokens;
+  const int32_t* positions;
+  int32_t* err_word;
+};
+int launch_validate(const ValidateLaunch& a, hipStream_t stream);
+
+}  // namespace kvattn

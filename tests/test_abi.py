@@ -1,0 +1,142 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad host arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_decode_attn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvattn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvattn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.kvattn_version().decode().startswith("kvattn")
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code in (0, -1, -2, -3, -4):
+        assert L.kvattn_status_string(code).decode() != "unknown status"
+
+
+def test_cache_bytes_closed_forms_through_the_abi():
+    L = _lib.lib()
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", "kv_cache_bytes.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            rows.append(line.split())
+    for r in rows:
+        assert L.kvattn_cache_bytes(*[int(x) for x in r[:6]]) == int(r[6]), r[7]
+    assert L.kvattn_cache_bytes(1 << 40, 1 << 40, 2, 1, 1, 1) == 0  # overflow
+
+
+def test_workspace_and_partition_sizing():
+    L = _lib.lib()
+    t = L.kvattn_decode_default_part_tokens(32, 32, 8, 8193)
+    assert t % 64 == 0 and 64 <= t <= 8192
+    parts = (8193 + t - 1) // t
+    assert L.kvattn_decode_workspace_bytes(32, 32, 8, 128, 8193, t) == 32 * 32 * parts * 130 * 4
+    assert L.kvattn_decode_workspace_bytes(32, 32, 8, 128, 100, 512) == 0  # single partition
+    assert L.kvattn_decode_default_part_tokens(1, 3, 2, 100) == 0          # bad group
+
+
+FAKE = 0x10000  # an aligned non-null address; host validation never dereferences it
+
+
+def _cache(dtype=_lib.BF16, layout=_lib.PAGED, head_dim=128, hkv=8, num_blocks=64, capacity=256, rows=4):
+    c = _lib.KvattnCache()
+    c.dtype, c.layout, c.num_kv_heads, c.head_dim = dtype, layout, hkv, head_dim
+    c.capacity, c.num_rows, c.num_blocks = capacity, rows, num_blocks
+    c.k, c.v = FAKE, FAKE + 0x100000
+    return c
+
+
+def _decode(c, **kw):
+    a = dict(batch=4, hq=32, q=FAKE, qd=_lib.BF16, lens=FAKE, maxlen=1000, table=FAKE, mb=64, mask=None,
+             stride=0, scale=0.1, out=FAKE, ws=None, wsb=0, part=0)
+    a.update(kw)
+    L = _lib.lib()
+    return L.kvattn_attn_decode(ctypes.byref(c) if c is not None else None, a["batch"], a["hq"], a["q"], a["qd"],
+                                a["lens"], a["maxlen"], a["table"], a["mb"], a["mask"], a["stride"], a["scale"],
+                                a["out"], a["ws"], a["wsb"], a["part"], None)
+
+
+@pytest.mark.parametrize("kw,cache_kw,want", [
+    ({}, {"head_dim": 96}, _lib.EUNSUPPORTED),
+    ({"hq": 24}, {}, _lib.EUNSUPPORTED),              # group 3
+    ({"qd": _lib.F32}, {}, _lib.EUNSUPPORTED),        # bf16 cache needs bf16 q
+    ({"q": FAKE + 4}, {}, _lib.EINVAL),               # misaligned
+    ({"lens": None}, {}, _lib.EINVAL),
+    ({"table": None}, {}, _lib.EINVAL),               # paged without a table
+    ({"part": 100}, {}, _lib.EINVAL),                 # not a multiple of 64
+    ({"part": 4096}, {}, _lib.EINVAL),                # 4096 * group 4 > 8192 scores
+    ({"mask": FAKE, "stride": 10}, {}, _lib.EINVAL),  # stride < max_seq_len
+    ({}, {}, _lib.EWORKSPACE),                        # several partitions, no workspace
+    ({}, {"dtype": 7}, _lib.EINVAL),
+    ({}, {"layout": 5}, _lib.EINVAL),
+    ({}, {"layout": _lib.CONTIGUOUS, "capacity": 100}, _lib.EINVAL),  # not a multiple of 16
+    ({"batch": 8}, {"layout": _lib.CONTIGUOUS, "rows": 4}, _lib.EINVAL),
+    ({}, {"dtype": _lib.FP8_E4M3}, _lib.EINVAL),      # fp8 without scales
+])
+def test_decode_host_errors(kw, cache_kw, want):
+    assert _decode(_cache(**cache_kw), **kw) == want
+    assert _lib.lib().kvattn_last_error().decode() != ""
+
+
+def test_decode_null_cache():
+    assert _decode(None) == _lib.EINVAL
+
+
+def test_decode_workspace_too_small():
+    assert _decode(_cache(), ws=FAKE, wsb=64) == _lib.EWORKSPACE
+
+
+def test_append_host_errors():
+    L = _lib.lib()
+    c = _cache()
+    args = [ctypes.byref(c), 4, 1, FAKE, FAKE, _lib.BF16, FAKE, None, FAKE, 64, None]
+    bad = list(args)
+    bad[5] = _lib.F32  # f32 into a bf16 cache
+    assert L.kvattn_kv_append(*bad) == _lib.EUNSUPPORTED
+    bad = list(args)
+    bad[6] = None  # positions
+    assert L.kvattn_kv_append(*bad) == _lib.EINVAL
+    bad = list(args)
+    bad[3] = FAKE + 8
+    assert L.kvattn_kv_append(*bad) == _lib.EINVAL
+    zero = list(args)
+    zero[2] = 0  # n_new == 0: a no-op that never launches
+    assert L.kvattn_kv_append(*zero) == _lib.OK
+
+
+def test_prefill_host_errors():
+    L = _lib.lib()
+
+    def call(cache=None, hq=32, hkv=8, d=128, n=16, dtype=_lib.BF16, attend_prefix=0, q=FAKE):
+        return L.kvattn_attn_prefill(ctypes.byref(cache) if cache is not None else None, 1, hq, hkv, d, n, q, FAKE,
+                                     FAKE, dtype, None, None, None, 0, None, 0, 1, attend_prefix, 0.1, FAKE, None)
+
+    assert call(d=80) == _lib.EUNSUPPORTED
+    assert call(hq=12) == _lib.EUNSUPPORTED
+    assert call(dtype=_lib.FP8_E4M3) == _lib.EINVAL
+    assert call(attend_prefix=1) == _lib.EINVAL
+    assert call(q=FAKE + 2) == _lib.EINVAL
+    assert call(cache=_cache(hkv=4)) == _lib.EINVAL  # shape mismatch
+    assert call(n=0) == _lib.OK

@@ -1,0 +1,180 @@
+"""Prefill attention on the GPU (through the C ABI) vs the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_decode_attn_amd as K
+from kv_cache_decode_attn_amd import synth
+from oracle import attention as OA
+from oracle import cache as OC
+from tests.helpers import f64, max_abs, storage
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 2e-3
+
+
+def _inputs(B, Hq, Hkv, N, d, dtype, seed, std=1.0):
+    q = synth.normal((B, Hq, N, d), (seed, synth.T_Q), dtype, std=std)
+    k = synth.normal((B, Hkv, N, d), (seed, synth.T_KNEW), dtype, std=std)
+    v = synth.normal((B, Hkv, N, d), (seed, synth.T_VNEW), dtype, std=std)
+    return q, k, v
+
+
+def _oracle(q, k, v, positions, q_lens, causal=True, key_mask=None, prefix=None):
+    d = q.shape[-1]
+    kw = {}
+    if prefix is not None:
+        kw = dict(prefix_k=prefix[0], prefix_v=prefix[1], attend_prefix=True)
+    return OA.prefill(f64(q), f64(k), f64(v), positions, q_lens, 1.0 / math.sqrt(d), causal=causal,
+                      key_mask=key_mask, **kw)
+
+
+def test_tiny_config_prefill_fp32():
+    """1 layer, batch 1, 4/4 heads, d 64, fp32: causal prefill of 16 tokens."""
+    q, k, v = _inputs(1, 4, 4, 16, 64, torch.float32, 20)
+    got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV)).cpu().numpy()
+    assert max_abs(got, _oracle(q, k, v, [0], [16])) <= TOL
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("G,d", [(1, 64), (4, 128), (2, 64), (8, 128)])
+def test_causal_prefill_groups(dtype, G, d):
+    B, Hkv, N = 2, 2, 77
+    std = 1.0 if dtype == torch.float32 else 1.0 / math.sqrt(d)
+    q, k, v = _inputs(B, G * Hkv, Hkv, N, d, dtype, 21 + G, std=std)
+    got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV)).cpu().numpy()
+    assert np.isfinite(got).all()
+    assert max_abs(got, _oracle(q, k, v, [0, 0], [N, N])) <= TOL
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_q_lens_and_padding_mask(causal):
+    """Two real length-3 sequences padded to 5 ("Transformer Attention Masks
+    and KV-Cache Inference", "Implementation and verification procedure"),
+    then a ragged batch with a random key mask and NaN in the padding."""
+    B, Hq, Hkv, N, d = 2, 4, 2, 5, 64
+    q, k, v = _inputs(B, Hq, Hkv, N, d, torch.float32, 30)
+    q_lens = np.array([3, 3], np.int32)
+    mask = synth.padding_mask(q_lens, N)
+    k[:, :, 3:] = float("nan")
+    v[:, :, 3:] = float("nan")
+    got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), q_lens=torch.from_numpy(q_lens).to(DEV),
+                         key_mask=torch.from_numpy(mask).to(DEV), causal=causal).cpu().numpy()
+    assert np.isfinite(got).all()
+    assert np.all(got[:, :, 3:] == 0.0)
+    # real rows equal an unpadded run
+    ref = K.attn_prefill(q[:, :, :3].contiguous().to(DEV), k[:, :, :3].contiguous().to(DEV),
+                         v[:, :, :3].contiguous().to(DEV), causal=causal).cpu().numpy()
+    assert max_abs(got[:, :, :3], ref) <= 1e-6
+    assert max_abs(got, _oracle(q, k, v, [0, 0], q_lens, causal, mask)) <= TOL
+
+    B, N = 3, 150
+    q, k, v = _inputs(B, Hq, Hkv, N, d, torch.bfloat16, 31, std=1 / 8)
+    q_lens = np.array([150, 1, 97], np.int32)
+    mask = synth.random_mask((B, N), 0.7, (31, synth.T_MASK))
+    mask[:, 0] = 1
+    got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), q_lens=torch.from_numpy(q_lens).to(DEV),
+                         key_mask=torch.from_numpy(mask).to(DEV), causal=causal).cpu().numpy()
+    assert max_abs(got, _oracle(q, k, v, [0, 0, 0], q_lens, causal, mask)) <= TOL
+
+
+def test_causal_matrix_through_one_hot_values():
+    """V rows one-hot: output row t is the attention weight row t, so the
+    printed 4x4 causal pattern shows up as exact zeros above the diagonal."""
+    d, N = 64, 4
+    q, k, _ = _inputs(1, 1, 1, N, d, torch.float32, 32)
+    v = torch.zeros((1, 1, N, d), dtype=torch.float32)
+    for s in range(N):
+        v[0, 0, s, s] = 1.0
+    got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV)).cpu().numpy()[0, 0, :, :N]
+    assert np.all(got[np.triu_indices(N, 1)] == 0.0)
+    assert np.all(got[np.tril_indices(N)] > 0.0)
+    assert np.abs(got.sum(axis=1) - 1.0).max() <= 1e-6
+    want = OA.attention_weights(f64(q)[0, 0], f64(k)[0, 0], OA.causal_allow(N), 1 / math.sqrt(d))
+    assert max_abs(got, want) <= 1e-6
+
+
+@pytest.mark.parametrize("layout", [K.PAGED, K.CONTIGUOUS])
+def test_prefill_writes_cache_bit_exact(layout):
+    B, Hq, Hkv, N, d = 2, 8, 2, 40, 128
+    q, k, v = _inputs(B, Hq, Hkv, N, d, torch.bfloat16, 33, std=1 / math.sqrt(d))
+    q_lens = np.array([40, 23], np.int32)
+    if layout == K.PAGED:
+        table, nblk = synth.block_table([3, 2], 3, (33, synth.T_PERM), num_blocks=7)
+        cache = K.KVCache.paged(nblk, Hkv, d, K.BF16, DEV, fill=0.5)
+        tdev = torch.from_numpy(table).to(DEV)
+    else:
+        table, tdev = None, None
+        cache = K.KVCache.contiguous(B, Hkv, 48, d, K.BF16, DEV, fill=0.5)
+    before_k, before_v = storage(cache.k), storage(cache.v)
+    got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), cache=cache, q_lens=torch.from_numpy(q_lens).to(DEV),
+                         positions=torch.zeros(B, dtype=torch.int32, device=DEV), block_table=tdev).cpu().numpy()
+    want_k, want_v = OC.predict_append(before_k, before_v, storage(k), storage(v), [0, 0], N, layout == K.PAGED,
+                                       table, n_valid=q_lens)
+    np.testing.assert_array_equal(storage(cache.k), want_k)
+    np.testing.assert_array_equal(storage(cache.v), want_v)
+    assert max_abs(got, _oracle(q, k, v, [0, 0], q_lens)) <= TOL
+
+
+@pytest.mark.parametrize("cache_dtype", [K.BF16, K.FP8_E4M3])
+def test_chunked_prefill_attends_cached_prefix(cache_dtype):
+    """A second chunk at positions P.. attends the cached prefix plus itself,
+    equal to the matching rows of a one-shot prefill."""
+    B, Hq, Hkv, d, N = 2, 8, 2, 128, 96
+    P = np.array([40, 17], np.int32)
+    n2 = N - P
+    q, k, v = _inputs(B, Hq, Hkv, N, d, torch.bfloat16, 34, std=1 / math.sqrt(d))
+    table, nblk = synth.block_table([6, 6], 6, (34, synth.T_PERM))
+    ks = vs = None
+    if cache_dtype == K.FP8_E4M3:
+        ks = torch.full((Hkv,), 0.02, dtype=torch.float32, device=DEV)
+        vs = torch.full((Hkv,), 0.03, dtype=torch.float32, device=DEV)
+    cache = K.KVCache.paged(nblk, Hkv, d, cache_dtype, DEV, ks, vs)
+    cache.k.zero_()
+    cache.v.zero_()
+    tdev = torch.from_numpy(table).to(DEV)
+    zeros = torch.zeros(B, dtype=torch.int32, device=DEV)
+    K.kv_append(cache, k.to(DEV), v.to(DEV), zeros, block_table=tdev, n_valid=torch.from_numpy(P).to(DEV))
+    # second chunk: new tokens P .. N-1 (ragged), padded to the longest
+    n_max = int(n2.max())
+    q2 = torch.zeros((B, Hq, n_max, d), dtype=torch.bfloat16)
+    k2 = torch.zeros((B, Hkv, n_max, d), dtype=torch.bfloat16)
+    v2 = torch.zeros((B, Hkv, n_max, d), dtype=torch.bfloat16)
+    for b in range(B):
+        q2[b, :, :n2[b]] = q[b, :, P[b]:]
+        k2[b, :, :n2[b]] = k[b, :, P[b]:]
+        v2[b, :, :n2[b]] = v[b, :, P[b]:]
+    got = K.attn_prefill(q2.to(DEV), k2.to(DEV), v2.to(DEV), cache=cache, positions=torch.from_numpy(P).to(DEV),
+                         q_lens=torch.from_numpy(n2).to(DEV), block_table=tdev, attend_prefix=True).cpu().numpy()
+    if cache_dtype == K.BF16:
+        full = _oracle(q, k, v, [0, 0], [N, N])
+        for b in range(B):
+            assert max_abs(got[b, :, :n2[b]], full[b, :, P[b]:]) <= TOL
+            assert np.all(got[b, :, n2[b]:] == 0.0)
+    else:
+        # prefix read back from the fp8 cache: the oracle dequantises its own codes
+        pk = [np.stack([OC.to_f64(OC.encode_rows(storage(k)[b, g, :P[b]], OC.BF16, OC.FP8_E4M3, np.float32(0.02)),
+                                  OC.FP8_E4M3, np.float32(0.02)) for g in range(Hkv)]) for b in range(B)]
+        pv = [np.stack([OC.to_f64(OC.encode_rows(storage(v)[b, g, :P[b]], OC.BF16, OC.FP8_E4M3, np.float32(0.03)),
+                                  OC.FP8_E4M3, np.float32(0.03)) for g in range(Hkv)]) for b in range(B)]
+        want = _oracle(q2, k2, v2, P, n2, prefix=(pk, pv))
+        assert max_abs(got, want) <= TOL
+
+
+def test_decode_equals_last_row_of_prefill():
+    """Cached decode == the last row of a full recompute ("Transformer
+    Attention Masks and KV-Cache Inference", "Implementation and verification
+    procedure"), both on the GPU."""
+    Hq, Hkv, d, N = 8, 2, 128, 200
+    q, k, v = _inputs(1, Hq, Hkv, N, d, torch.bfloat16, 35, std=1 / math.sqrt(d))
+    full = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV)).cpu().numpy()
+    table, nblk = synth.block_table([13], 13, (35, synth.T_PERM))
+    cache = K.KVCache.paged(nblk, Hkv, d, K.BF16, DEV, fill=0.0)
+    tdev = torch.from_numpy(table).to(DEV)
+    K.kv_append(cache, k.to(DEV), v.to(DEV), torch.zeros(1, dtype=torch.int32, device=DEV), block_table=tdev)
+    dec = K.attn_decode(cache, q[:, :, -1].contiguous().to(DEV), torch.tensor([N], dtype=torch.int32, device=DEV), N,
+                        block_table=tdev, part_tokens=64).cpu().numpy()
+    assert max_abs(dec, full[:, :, -1]) <= TOL
