@@ -3,7 +3,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvattn.so")
+# KVATTN_LIB may name another build of the same library (e.g. a variant
+# built for a performance experiment); the default is the in-tree build.
+LIB_PATH = os.environ.get("KVATTN_LIB") or os.path.join(_PKG, "libkvattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
 F32, BF16, FP8_E4M3 = 0, 1, 2

@@ -14,7 +14,7 @@
 // group are served by the same workgroup, so each K/V byte is read once per
 // group ("KV Cache Fully Explained", section "(2) GQA").
 //   phase 1  every wave streams 16-token blocks of K with 16-byte (8-byte for
-//            fp8) coalesced loads: lane (row, col) holds EPL elements of one
+//            fp8) coalesced non-temporal loads: lane (row, col) holds EPL elements of one
 //            token row; dot products with the G queries are reduced over the
 //            LPT lanes of a row with DPP row operations; scores go to LDS.
 //   phase 2  per query head, the partition's max and sum of exp2(z - max)
@@ -137,9 +137,38 @@ struct QFrag<KVATTN_BF16, G> {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 
-// LDS floats the partition kernel needs.
+// LDS layout of the partition kernel, in floats: block offsets (int64, one
+// per 16-token block of the partition), then scores/weights [T][G] (reused
+// for the cross-wave output reduction [kWaves][G][D]), then (max, sum) per
+// head.
+__host__ __device__ constexpr int decode_off_floats(int T) { return 2 * (T / kBlockTokens); }
 __host__ __device__ constexpr int decode_lds_floats(int T, int G, int D) {
-  return ((T * G > kWaves * G * D) ? T * G : kWaves * G * D) + 2 * G;
+  return decode_off_floats(T) + ((T * G > kWaves * G * D) ? T * G : kWaves * G * D) + 2 * G;
+}
+
+// K and V bytes are read exactly once per call: load them non-temporally so
+// the stream does not displace reusable lines (q, block table, partials)
+// from the caches.
+template <typename Raw>
+__device__ __forceinline__ Raw stream_load(const Raw* p) {
+  if constexpr (sizeof(Raw) == 16) {
+    typedef unsigned v4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(Raw, __builtin_nontemporal_load(reinterpret_cast<const v4*>(p)));
+  } else {
+    typedef unsigned v2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(Raw, __builtin_nontemporal_load(reinterpret_cast<const v2*>(p)));
+  }
+}
+
+template <typename Raw, int NI, int TPI, int ROWB>
+__device__ __forceinline__ void load_block(Raw* r, const uint8_t* base, int64_t off) {
+  if (off >= 0) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) r[i] = stream_load(reinterpret_cast<const Raw*>(base + off + i * TPI * ROWB));
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) r[i] = Raw{};
+  }
 }
 
 template <int KVT, int D, int G, bool MASK>
@@ -154,7 +183,9 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   constexpr int ROWB = D * (int)sizeof(Raw) / EPL;  // bytes per token row
 
   extern __shared__ float lds[];
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // KV head fastest in the grid: neighbouring workgroups read the heads of
+  // the same 16-token blocks, which sit side by side in the paged pool.
+  const int g = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane % LPT, row = lane / LPT;
   const int T = p.part_tokens;
@@ -174,38 +205,39 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
   const int j0 = t0 / kBlockTokens;
 
+  int64_t* offs = reinterpret_cast<int64_t*>(lds);        // [T/16] block byte offsets (-1: outside)
+  float* s_lds = lds + decode_off_floats(T);              // [T][G] scores -> weights
+  float* stat = lds + decode_lds_floats(T, G, D) - 2 * G;  // [G][2] (max, sum)
+  for (int i = tid; i < nblk; i += 256) offs[i] = block_offset(p.c, b, g, j0 + i);
+
   QFrag<KVT, G> q;
   q.load(p.q, (int64_t)b * p.num_q_heads + hq0, D, col);
   float zscale = p.scale * kLog2e;
   if constexpr (KVT == KVATTN_FP8_E4M3) zscale *= p.k_scale[g];
-
-  float* s_lds = lds;                                   // [T][G] scores -> weights
-  float* stat = lds + decode_lds_floats(T, G, D) - 2 * G;  // [G][2] (max, sum)
   const uint8_t* mask_row = MASK ? p.key_mask + (int64_t)b * p.key_mask_stride : nullptr;
+  const uint8_t* kbase = p.c.k + row * ROWB + col * (int)sizeof(Raw);
+  const uint8_t* vbase = p.c.v + row * ROWB + col * (int)sizeof(Raw);
+  __syncthreads();
 
   // ---- phase 1: scores of every key of the partition ----
+  // Wave w handles blocks w, w + 4, ...; the next block's loads are issued
+  // before the current block is consumed, so two blocks are in flight.
+  Raw cur[NI], nxt[NI];
+  if (wave < nblk) load_block<Raw, NI, TPI, ROWB>(cur, kbase, offs[wave]);
   for (int jb = wave; jb < nblk; jb += kWaves) {
+    const int64_t off = offs[jb];
+    if (jb + kWaves < nblk) load_block<Raw, NI, TPI, ROWB>(nxt, kbase, offs[jb + kWaves]);
     const int j = j0 + jb;
-    const int64_t off = block_offset(p.c, b, g, j);
-    Raw raw[NI];
-    if (off >= 0) {
-      const uint8_t* base = p.c.k + off + row * ROWB + col * (int)sizeof(Raw);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) raw[i] = *reinterpret_cast<const Raw*>(base + i * TPI * ROWB);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) raw[i] = Raw{};
-    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = j * kBlockTokens + i * TPI + row;
       float acc[G];
       if constexpr (KVT == KVATTN_BF16) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = q.dot_raw(h, raw[i]);
+        for (int h = 0; h < G; ++h) acc[h] = q.dot_raw(h, cur[i]);
       } else {
         float kf[EPL];
-        TR::to_f32(raw[i], kf);
+        TR::to_f32(cur[i], kf);
 #pragma unroll
         for (int h = 0; h < G; ++h) acc[h] = q.dot(h, kf);
       }
@@ -220,7 +252,11 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) cur[i] = nxt[i];
   }
+  // The first V block is fetched while the softmax statistics are formed.
+  if (wave < nblk) load_block<Raw, NI, TPI, ROWB>(cur, vbase, offs[wave]);
   __syncthreads();
 
   // ---- phase 2: per-head max and sum; scores -> weights exp2(z - max) ----
@@ -251,17 +287,14 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
 
   for (int jb = wave; jb < nblk; jb += kWaves) {
+    const int64_t off = offs[jb];
+    if (jb + kWaves < nblk) load_block<Raw, NI, TPI, ROWB>(nxt, vbase, offs[jb + kWaves]);
     const int j = j0 + jb;
-    const int64_t off = block_offset(p.c, b, g, j);
-    if (off < 0) continue;  // a block outside the cache was fully masked
-    const uint8_t* base = p.c.v + off + row * ROWB + col * (int)sizeof(Raw);
-    Raw raw[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) raw[i] = *reinterpret_cast<const Raw*>(base + i * TPI * ROWB);
     // A block wholly inside the partition with no key mask has only live
     // keys; otherwise a key with zero weight for every head is dropped so
-    // that non-finite bytes in padding or stale slots cannot reach o.
-    const bool full = !MASK && (j + 1) * kBlockTokens <= t1;
+    // that non-finite bytes in padding or stale slots cannot reach o.  A
+    // block outside the cache was fully masked (all weights 0).
+    const bool full = !MASK && off >= 0 && (j + 1) * kBlockTokens <= t1;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = j * kBlockTokens + i * TPI + row;
@@ -272,7 +305,7 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
         for (int h = 0; h < G; ++h) w[h] = s_lds[(tok - t0) * G + h];
       } else {
         live = false;
-        const bool in = tok < t1;
+        const bool in = tok < t1 && off >= 0;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           w[h] = in ? s_lds[(tok - t0) * G + h] : 0.f;
@@ -280,7 +313,7 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
         }
       }
       float vf[EPL];
-      TR::to_f32(raw[i], vf);
+      TR::to_f32(cur[i], vf);
       if (!live) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) vf[e] = 0.f;
@@ -290,6 +323,8 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(w[h], vf[e], o[h][e]);
     }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) cur[i] = nxt[i];
   }
 
   // reduce over the TPI rows of the wave (lanes sharing col)
@@ -299,7 +334,7 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
     for (int e = 0; e < EPL; ++e) o[h][e] = strided_sum<LPT>(o[h][e]);
 
   __syncthreads();  // every wave is done reading weights; reuse LDS
-  float* red = lds;  // [kWaves][G][D]
+  float* red = s_lds;  // [kWaves][G][D]
   if (row == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -332,39 +367,69 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   }
 }
 
-// Merge the split-K partials of one (sequence, query head).
+// Merge the split-K partials of one (sequence, query head): the partition
+// maxima and sums are staged in LDS, their weights exp2(m_p - M) formed once,
+// then each thread combines one output element over all partitions.
 template <int D>
-__global__ void __launch_bounds__(128) decode_merge(const DecodeLaunch p) {
+__global__ void __launch_bounds__(256) decode_merge(const DecodeLaunch p) {
+  __shared__ float wts[1024];
+  __shared__ float red[2][4];
   const int hq = blockIdx.x, b = blockIdx.y;
   const int T = p.part_tokens;
   const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
   const int np = (ctx + T - 1) / T;
   if (np <= 1) return;  // written by the partition pass
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t slot0 = ((int64_t)b * p.num_q_heads + hq) * p.num_parts;
   const float* ml = p.ws_ml + slot0 * 2;
+  const float* wo = p.ws_o + slot0 * D;
+  // global max over partitions
   float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, ml[2 * i]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f, L = 0.f;
-    for (int i = 0; i < np; ++i) {
-      const float m = ml[2 * i];
-      if (m == -INFINITY) continue;
-      const float w = exp2f(m - M);
-      L = fmaf(w, ml[2 * i + 1], L);
-      acc = fmaf(w, p.ws_o[(slot0 + i) * D + d], acc);
-    }
-    p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = (L > 0.f) ? acc / L : 0.f;
+  for (int i = tid; i < np; i += 256) M = fmaxf(M, ml[2 * i]);
+  M = group_max<64>(M);
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  // partition weights (0 for empty partitions) and the total sum
+  float L = 0.f;
+  for (int i = tid; i < np; i += 256) {
+    const float m = ml[2 * i];
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    if (i < 1024) wts[i] = w;
+    L = fmaf(w, ml[2 * i + 1], L);
+  }
+  L = group_sum<64>(L);
+  if (lane == 0) red[1][wave] = L;
+  __syncthreads();
+  L = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  // 256 threads: D columns x (256 / D) partition phases, combined in LDS
+  constexpr int PH = 256 / D;
+  const int d = tid % D, ph = tid / D;
+  float acc = 0.f;
+  for (int i = ph; i < np; i += PH) {
+    const float w = (i < 1024) ? wts[i] : ((ml[2 * i] == -INFINITY) ? 0.f : exp2f(ml[2 * i] - M));
+    if (w != 0.f) acc = fmaf(w, wo[(int64_t)i * D + d], acc);
+  }
+  __syncthreads();
+  wts[tid] = acc;
+  __syncthreads();
+  if (ph == 0) {
+    float s = acc;
+#pragma unroll
+    for (int k = 1; k < PH; ++k) s += wts[k * D + d];
+    p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = s * inv;
   }
 }
 
 template <int KVT, int D, int G, bool MASK>
 int launch_typed(const DecodeLaunch& a, hipStream_t s) {
-  const dim3 grid(a.num_parts, a.num_kv_heads, a.batch);
+  const dim3 grid(a.num_kv_heads, a.num_parts, a.batch);
   const size_t lds = (size_t)decode_lds_floats(a.part_tokens, G, D) * sizeof(float);
   hipLaunchKernelGGL((decode_partition<KVT, D, G, MASK>), grid, dim3(256), lds, s, a);
   if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
   if (a.num_parts > 1) {
-    hipLaunchKernelGGL((decode_merge<D>), dim3(a.num_q_heads, a.batch), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((decode_merge<D>), dim3(a.num_q_heads, a.batch), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
   }
   return KVATTN_OK;
