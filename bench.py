@@ -312,7 +312,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode8b,padded32,longctx70b",
+    ap.add_argument("--workloads", default="decode8b,padded32,longctx70b,prefill8k",
                     help="comma list: decode8b (headline), padded32, longctx70b, prefill8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the headline workload the oracle runs")

@@ -178,3 +178,44 @@ def test_decode_equals_last_row_of_prefill():
     dec = K.attn_decode(cache, q[:, :, -1].contiguous().to(DEV), torch.tensor([N], dtype=torch.int32, device=DEV), N,
                         block_table=tdev, part_tokens=64).cpu().numpy()
     assert max_abs(dec, full[:, :, -1]) <= TOL
+
+
+@pytest.mark.parametrize("G,d,causal", [(4, 128, True), (1, 128, True), (8, 64, True), (2, 128, False)])
+def test_mfma_prefill_many_tiles_ragged(G, d, causal):
+    """bf16 MFMA path over several 32-key tiles and query tiles with a
+    ragged tail (N not a multiple of any tile) and ragged q_lens."""
+    B, Hkv, N = 2, 2, 333
+    q, k, v = _inputs(B, G * Hkv, Hkv, N, d, torch.bfloat16, 40 + G, std=1 / math.sqrt(d))
+    q_lens = np.array([333, 190], np.int32)
+    got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), q_lens=torch.from_numpy(q_lens).to(DEV),
+                         causal=causal).cpu().numpy()
+    assert np.isfinite(got).all()
+    assert np.all(got[1, :, 190:] == 0.0)
+    assert max_abs(got, _oracle(q, k, v, [0, 0], q_lens, causal)) <= TOL
+
+
+def test_mfma_prefill_unit_scale_inputs_and_key_mask():
+    """N(0,1) inputs (larger scores) with a random key mask and NaN in the
+    masked K/V rows."""
+    B, Hq, Hkv, N, d = 1, 8, 2, 200, 128
+    q, k, v = _inputs(B, Hq, Hkv, N, d, torch.bfloat16, 46, std=0.5)
+    mask = synth.random_mask((B, N), 0.5, (46, synth.T_MASK))
+    mask[:, 0] = 1
+    m = torch.from_numpy(mask == 0)
+    k[m[:, None, :, None].expand_as(k)] = float("nan")
+    v[m[:, None, :, None].expand_as(v)] = float("nan")
+    for causal in (True, False):
+        got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), key_mask=torch.from_numpy(mask).to(DEV),
+                             causal=causal).cpu().numpy()
+        assert np.isfinite(got).all()
+        assert max_abs(got, _oracle(q, k, v, [0], [N], causal, mask)) <= TOL
+
+
+def test_mfma_prefill_constant_values_give_ones():
+    """Row sums are taken over the same rounded weights as the output, so
+    V == 1 gives exactly-normalised rows."""
+    B, Hq, Hkv, N, d = 1, 4, 1, 257, 128
+    q, k, _ = _inputs(B, Hq, Hkv, N, d, torch.bfloat16, 47)
+    v = torch.ones((B, Hkv, N, d), dtype=torch.bfloat16)
+    got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV)).cpu().numpy()
+    assert np.abs(got - 1.0).max() <= 1e-6
