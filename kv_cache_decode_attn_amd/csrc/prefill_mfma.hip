@@ -1,4 +1,4 @@
-// bf16 prefill attention on MFMA (gfx950 v_mfma_f32_16x16x32_bf16).
+// bf16 prefill attention on MFMA (gfx950 v_mfma_f32_32x32x16_bf16).
 //
 // What is computed is the masked scaled dot-product attention of the new
 // tokens ("Transformer Attention Masks and KV-Cache Inference"
@@ -9,27 +9,30 @@
 // (factory.pai-world.com), section "Flash Attention - tiling trick"), with
 // the exact running (max, sum) rescaling of its numerical-trick paragraph.
 // Prefill is compute bound ("KV Cache" (heepie.pages.dev), section "Prefill
-// and Decode"), so both products run on the matrix cores.
+// and Decode"), so both products run on the matrix cores.  The 32x32x16
+// bf16 shape is used because it is the one that issues at the full matrix
+// rate on gfx950 (the 16x16x32 shape measured at about half of it).
 //
 // Work split.  A workgroup of 4 waves owns HW = min(G, 4) query heads of one
 // KV head and a tile of 32 * 4 / HW query rows; each wave owns one head and
 // 32 query rows.  The heads of a GQA group share the K/V tiles staged in LDS.
 // Causal tiles are issued heaviest first.
 //
-// Per 32-key tile, per wave:
-//   S^T[key][q] = K Q^T      A = K rows from LDS, B = Q (registers), fp32 acc.
-//                            The accumulator layout (lane l holds rows
-//                            4*(l/16)+r, column l%16) puts each query in one
-//                            lane column, so the row max needs only two
-//                            cross-lane steps and P^T is already the B
+// Per 32-key tile, per wave (h = lane / 32):
+//   S^T[key][q] = K Q^T      A = K rows from LDS, B = Q (registers), fp32
+//                            accumulate.  The 32x32 accumulator gives lane l
+//                            query column l % 32 and keys 8*(r/4) + 4h + r%4
+//                            (r = 0..15): a query's 32 scores sit in two
+//                            lanes, so the row max is a local max plus one
+//                            cross-half swap, and P^T is already the B
 //                            operand of the second product.
 //   P = exp2(S*c - m)        c = scale*log2(e); m is a per-query running
 //                            maximum that is only raised (with rescaling of
 //                            the accumulators) when the tile maximum exceeds
 //                            it by more than 8, so P <= 2^8; P rounded to bf16.
 //   O^T[d][q] += V^T P^T     A = V^T from LDS.  V is transposed while it is
-//                            staged into LDS; its key order inside an LDS row
-//                            follows the key order of P^T's operand slots.
+//                            staged into LDS; inside a V^T row the keys are
+//                            ordered like P^T's operand slots.
 //   l[q] += 1 . P^T          an MFMA against a ones operand, so the row sum
 //                            is the sum of the same bf16 weights used for O.
 // Masked keys (causal, beyond q_len, key_mask) get P = 0 and their V rows are
@@ -43,7 +46,7 @@ namespace kvattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kKeys = 32;      // keys per tile
 constexpr int kWaveQ = 32;     // query rows per wave
@@ -51,8 +54,8 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;  // log2 headroom before the running max moves
 
-__device__ __forceinline__ f32x4 mfma(const U4& a, const U4& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+__device__ __forceinline__ f32x16 mfma(const U4& a, const U4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                  0, 0);
 }
 
@@ -64,32 +67,36 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// LDS geometry (bytes).  K rows are padded to 68 dwords and V^T rows to 20
-// dwords so that 16 lanes reading 16 consecutive rows at one column touch 16
-// disjoint groups of 4 banks.
+// LDS geometry (bytes), two buffers.  K rows are padded to 68 dwords and V^T
+// rows to 20 dwords so that 16 lanes reading 16 consecutive rows at one
+// column touch 16 disjoint groups of 4 banks.
 template <int D>
 struct Geo {
   static constexpr int KROW = D * 2 + 16;
   static constexpr int VROW = kKeys * 2 + 16;
   static constexpr int KBYTES = kKeys * KROW;
   static constexpr int VBYTES = D * VROW;
-  static constexpr int BUF = KBYTES + VBYTES;
+  static constexpr int MBYTES = kKeys;  // per-key valid flags of the tile
+  static constexpr int BUF = KBYTES + VBYTES + MBYTES;
 };
 
-// Slot of key k (0..31) inside a V^T row: the PV operand of lane group lg
-// holds keys 4lg..4lg+3 (from the first 16-key score tile) then
-// 16+4lg..16+4lg+3 (second tile), as 8 consecutive bf16.
-__device__ __forceinline__ int vslot(int k) { return 8 * ((k & 15) >> 2) + (k & 3) + 4 * (k >> 4); }
+// Position of key k (0..31) inside a V^T row.  The PV product for keys
+// 16m .. 16m+15 takes, in lane half h, operand slot j = key
+// 16m + 8*(j/4) + 4h + j%4 (the key order of the score accumulator), so
+// keys are stored at 16m + 8h + j to make each slot group one 16-byte read.
+__device__ __forceinline__ int vpos(int k) {
+  return 16 * (k >> 4) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
+}
 
 template <int D, bool CAUSAL, bool MASK>
 __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const PrefillLaunch a, int hw) {
   using GE = Geo<D>;
-  constexpr int DC = D / 32;  // d chunks of the QK^T contraction
-  constexpr int DT = D / 16;  // d tiles of the output
+  constexpr int DK = D / 16;  // 16-wide d chunks of the QK^T contraction
+  constexpr int DT = D / 32;  // 32-row d tiles of the output
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lg = lane >> 4, lc = lane & 15;
+  const int hh = lane >> 5, lc = lane & 31;
   const int b = blockIdx.z;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int qw_per_head = 4 / hw;                  // 32-row sub-tiles per head
@@ -121,31 +128,32 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const Prefill
   const uint8_t* qg = a.q + ((int64_t)b * a.num_q_heads + h) * n_max * D * 2;
   const uint8_t* mrow = MASK ? a.key_mask + (int64_t)b * a.key_mask_stride : nullptr;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): rows q0 + 16 qt + lc ----
-  U4 qf[2][DC];
+  // ---- Q fragments (B operand of S^T = K Q^T): row q0 + lc, d 16c + 8hh ----
+  const int tq = q0 + lc;
+  U4 qf[DK];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int t = q0 + 16 * qt + lc;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      if (t < n_max)
-        qf[qt][dc] = *reinterpret_cast<const U4*>(qg + ((int64_t)t * D + 32 * dc + 8 * lg) * 2);
-      else
-        qf[qt][dc] = U4{0, 0, 0, 0};
-    }
-  }
+  for (int c = 0; c < DK; ++c)
+    qf[c] = (tq < n_max) ? *reinterpret_cast<const U4*>(qg + ((int64_t)tq * D + 16 * c + 8 * hh) * 2) : U4{0, 0, 0, 0};
 
   // ---- staging of one K/V tile: global -> registers -> LDS ----
-  // K: 32 rows x D*2 bytes = 32*D/8 chunks of 16 B; thread handles chunks
-  // tid, tid + 256 (D = 128) or tid (D = 64).
-  constexpr int KCH = kKeys * D / 8 / kThreads;  // 16-byte K chunks per thread
+  // K: 32 rows x D*2 bytes = 32*D/8 chunks of 16 B, KCH per thread.
+  constexpr int KCH = kKeys * D / 8 / kThreads;
   // V: thread handles keys (2m, 2m+1) x 8 columns d in [8 dg, 8 dg + 8);
   // 16 key pairs x D/8 column groups = 2*D threads (D = 64: half the block).
   const int vm = tid & 15, vdg = tid >> 4;
   const bool v_active = vdg < D / 8;
   U4 kreg[KCH], vreg[2];
+  uint32_t mflag = 0;  // threads 0..31: valid flag of key kt0 + tid
 
+  // A key is valid if it is a real token (< q_len) and, with a key mask,
+  // its mask byte (at absolute position P + key) is nonzero.
+  auto key_valid = [&](int key) -> bool {
+    bool ok = key < qlen;
+    if (MASK && ok) ok = (P + key < a.key_mask_stride) && mrow[P + key] != 0;
+    return ok;
+  };
   auto load_tile = [&](int kt0) {
+    if (tid < kKeys) mflag = key_valid(kt0 + tid) ? 1u : 0u;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int ch = tid + c * kThreads;
@@ -157,15 +165,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const Prefill
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int key = kt0 + 2 * vm + e;
-        bool live = key < qlen;
-        if (MASK && live) live = (P + key < a.key_mask_stride) && mrow[P + key] != 0;
-        vreg[e] = live ? *reinterpret_cast<const U4*>(vg + ((int64_t)key * D + 8 * vdg) * 2) : U4{0, 0, 0, 0};
+        vreg[e] = key_valid(key) ? *reinterpret_cast<const U4*>(vg + ((int64_t)key * D + 8 * vdg) * 2)
+                                 : U4{0, 0, 0, 0};
       }
     }
   };
   auto store_tile = [&](int buf) {
     uint8_t* kl = smem + buf * GE::BUF;
     uint8_t* vl = kl + GE::KBYTES;
+    if (tid < kKeys) vl[GE::VBYTES + tid] = (uint8_t)mflag;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int ch = tid + c * kThreads;
@@ -175,25 +183,26 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const Prefill
       // transpose 2 keys x 8 columns into 8 dwords (key 2m low, 2m+1 high)
       const uint32_t x0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
       const uint32_t x1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-      const int slot = vslot(2 * vm);
+      const int pos = vpos(2 * vm);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t lo = __builtin_amdgcn_perm(x1[i], x0[i], 0x05040100u);  // column 2i
         const uint32_t hi = __builtin_amdgcn_perm(x1[i], x0[i], 0x07060302u);  // column 2i+1
-        *reinterpret_cast<uint32_t*>(vl + (8 * vdg + 2 * i) * GE::VROW + slot * 2) = lo;
-        *reinterpret_cast<uint32_t*>(vl + (8 * vdg + 2 * i + 1) * GE::VROW + slot * 2) = hi;
+        *reinterpret_cast<uint32_t*>(vl + (8 * vdg + 2 * i) * GE::VROW + pos * 2) = lo;
+        *reinterpret_cast<uint32_t*>(vl + (8 * vdg + 2 * i + 1) * GE::VROW + pos * 2) = hi;
       }
     }
   };
 
   // ---- accumulators ----
-  f32x4 o[DT][2], lsum[2];
+  f32x16 o[DT], lsum;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int r = 0; r < 16; ++r) {
+    lsum[r] = 0.f;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  lsum[0] = lsum[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-INFINITY, -INFINITY};
+    for (int dt = 0; dt < DT; ++dt) o[dt][r] = 0.f;
+  }
+  float mrun = -INFINITY;
   const float c = a.scale * kLog2e;
   const uint32_t one2 = 0x3F803F80u;  // two bf16 1.0
   const U4 ones = U4{one2, one2, one2, one2};
@@ -209,94 +218,89 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const Prefill
     if (kt0 < wave_end) {
       const uint8_t* kl = smem + buf * GE::BUF;
       const uint8_t* vl = kl + GE::KBYTES;
-      // S^T for keys kt0 + 16 kk + 4 lg + r, queries q0 + 16 qt + lc
-      f32x4 s[2][2];
+      // S^T for keys kt0 + 8*(r/4) + 4hh + r%4, query q0 + lc
+      f32x16 s;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        s[kk][0] = s[kk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const U4 kf = *reinterpret_cast<const U4*>(kl + (16 * kk + lc) * GE::KROW + (32 * dc + 8 * lg) * 2);
-          s[kk][0] = mfma(kf, qf[0][dc], s[kk][0]);
-          s[kk][1] = mfma(kf, qf[1][dc], s[kk][1]);
-        }
+      for (int cc = 0; cc < DK; ++cc) {
+        const U4 kf = *reinterpret_cast<const U4*>(kl + lc * GE::KROW + (16 * cc + 8 * hh) * 2);
+        s = mfma(kf, qf[cc], s);
       }
-      // masking: causal edge, keys beyond q_len, key mask
+      // masking: causal edge, keys beyond q_len, key mask.  The tile's key
+      // flags come from LDS as words of 4 keys (keys 8g + 4hh + 0..3).
       const bool edge = (kt0 + kKeys > qlen) || (CAUSAL && kt0 + kKeys - 1 > q0);
       if (MASK || edge) {
+        const uint32_t* mw = reinterpret_cast<const uint32_t*>(vl + GE::VBYTES);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int gq = 0; gq < 4; ++gq) {
+          const uint32_t w = mw[2 * gq + hh];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kt0 + 16 * kk + 4 * lg + r;
-            bool kv = key < qlen;
-            if (MASK && kv) kv = (P + key < a.key_mask_stride) && mrow[P + key] != 0;
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-              const int t = q0 + 16 * qt + lc;
-              const bool ok = kv && (!CAUSAL || key <= t);
-              if (!ok) s[kk][qt][r] = -INFINITY;
-            }
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * gq + e;
+            const int key = kt0 + 8 * gq + 4 * hh + e;
+            const bool ok = ((w >> (8 * e)) & 0xffu) != 0 && (!CAUSAL || key <= tq);
+            s[r] = ok ? s[r] : -INFINITY;
           }
+        }
       }
-      // running maximum per query (log2 domain), raised lazily
+      // running maximum of this query (log2 domain), raised lazily
+      float tm = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tm = fmaxf(tm, s[r]);
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
+        tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+      }
+      const bool need = tm > mrun + kRescale;
+      if (__any(need)) {
+        const float mnew = need ? tm : mrun;
+        const float alpha = need ? exp2f(mrun - mnew) : 1.f;  // 0 when mrun = -inf
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        lsum *= alpha;
+        mrun = mnew;
+      }
+      const float msub = (mrun == -INFINITY) ? 0.f : mrun;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -msub));
       U4 pf[2];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        float tm = fmaxf(fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3])),
-                         fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
-        tm = fmaxf(tm, __shfl_xor(tm, 16));
-        tm = fmaxf(tm, __shfl_xor(tm, 32));
-        tm *= c;
-        const bool need = tm > mrun[qt] + kRescale;
-        if (__any(need)) {
-          const float mnew = need ? tm : mrun[qt];
-          const float alpha = need ? exp2f(mrun[qt] - mnew) : 1.f;  // 0 when mrun = -inf
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= alpha;
-          lsum[qt] *= alpha;
-          mrun[qt] = mnew;
-        }
-        const float msub = (mrun[qt] == -INFINITY) ? 0.f : mrun[qt];
-        float p[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(fmaf(s[0][qt][r], c, -msub));
-          p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[1][qt][r], c, -msub));
-        }
-        pf[qt] = U4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
-      }
+      for (int m = 0; m < 2; ++m)
+        pf[m] = U4{pack_bf16(p[8 * m], p[8 * m + 1]), pack_bf16(p[8 * m + 2], p[8 * m + 3]),
+                   pack_bf16(p[8 * m + 4], p[8 * m + 5]), pack_bf16(p[8 * m + 6], p[8 * m + 7])};
       // O^T += V^T P^T ; l += 1 . P^T
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const U4 vf = *reinterpret_cast<const U4*>(vl + (16 * dt + lc) * GE::VROW + 16 * lg);
-        o[dt][0] = mfma(vf, pf[0], o[dt][0]);
-        o[dt][1] = mfma(vf, pf[1], o[dt][1]);
-      }
-      lsum[0] = mfma(ones, pf[0], lsum[0]);
-      lsum[1] = mfma(ones, pf[1], lsum[1]);
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const U4 vf = *reinterpret_cast<const U4*>(vl + (32 * dt + lc) * GE::VROW + (16 * m + 8 * hh) * 2);
+          o[dt] = mfma(vf, pf[m], o[dt]);
+        }
+      lsum = mfma(ones, pf[0], lsum);
+      lsum = mfma(ones, pf[1], lsum);
     }
     if (it + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: O^T[d][q] / l[q] -> out[q][d]; rows >= q_len are 0 ----
+  if (tq < n_max) {
+    const float l = lsum[0];
+    const bool live = tq < qlen;
+    const float inv = (live && l > 0.f) ? 1.f / l : 0.f;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int t = q0 + 16 * qt + lc;
-    if (t >= n_max) continue;
-    const float l = lsum[qt][0];
-    const float inv = (t < qlen && l > 0.f) ? 1.f / l : 0.f;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const f32x4 v = o[dt][qt] * inv;
-      float4 w;
-      w.x = (t < qlen) ? v[0] : 0.f;
-      w.y = (t < qlen) ? v[1] : 0.f;
-      w.z = (t < qlen) ? v[2] : 0.f;
-      w.w = (t < qlen) ? v[3] : 0.f;
-      *reinterpret_cast<float4*>(out_h + (int64_t)t * D + 16 * dt + 4 * lg) = w;
-    }
+      for (int rg = 0; rg < 4; ++rg) {
+        float4 w;
+        w.x = live ? o[dt][4 * rg] * inv : 0.f;
+        w.y = live ? o[dt][4 * rg + 1] * inv : 0.f;
+        w.z = live ? o[dt][4 * rg + 2] * inv : 0.f;
+        w.w = live ? o[dt][4 * rg + 3] * inv : 0.f;
+        *reinterpret_cast<float4*>(out_h + (int64_t)tq * D + 32 * dt + 8 * rg + 4 * hh) = w;
+      }
   }
 }
 

@@ -219,3 +219,25 @@ def test_mfma_prefill_constant_values_give_ones():
     v = torch.ones((B, Hkv, N, d), dtype=torch.bfloat16)
     got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV)).cpu().numpy()
     assert np.abs(got - 1.0).max() <= 1e-6
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mfma_prefill_each_masked_key_gets_zero_weight(causal):
+    """V rows one-hot, so output row t is query t's weight vector.  Masking
+    single keys at every accumulator position of the two 32-key tiles must
+    give those keys weight exactly 0 and leave every row summing to 1."""
+    N, d = 64, 128
+    q = synth.normal((1, 1, N, d), (48, synth.T_Q), std=0.1)
+    k = synth.normal((1, 1, N, d), (48, synth.T_KNEW), std=0.1)
+    v = torch.zeros((1, 1, N, d), dtype=torch.bfloat16)
+    for s in range(N):
+        v[0, 0, s, s] = 1.0
+    for masked in ([0], [1], [3], [4], [8], [12], [16], [27], [31], [32], [33], [63], [0, 5, 40, 41]):
+        mask = np.ones((1, N), np.uint8)
+        mask[0, masked] = 0
+        got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), key_mask=torch.from_numpy(mask).to(DEV),
+                             causal=causal).cpu().numpy()[0, 0, :, :N]
+        for c in masked:
+            assert np.all(got[:, c] == 0.0), masked
+        rows = [t for t in range(N) if mask[0, :t + 1 if causal else N].any()]
+        assert np.abs(got[rows].sum(axis=1) - 1.0).max() <= 1e-6, masked
