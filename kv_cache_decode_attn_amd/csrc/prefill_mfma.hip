@@ -48,7 +48,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kKeys = 32;      // keys per tile
+constexpr int kKeys = 64;      // keys per tile (two 32-key score sub-tiles)
+constexpr int kSub = kKeys / 32;
 constexpr int kWaveQ = 32;     // query rows per wave
 constexpr int kThreads = 256;  // 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
@@ -67,9 +68,9 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// LDS geometry (bytes), two buffers.  K rows are padded to 68 dwords and V^T
-// rows to 20 dwords so that 16 lanes reading 16 consecutive rows at one
-// column touch 16 disjoint groups of 4 banks.
+// LDS geometry (bytes), two buffers.  K rows are padded to D/2 + 4 dwords
+// and V^T rows to kKeys/2 + 4 dwords, so that 16 lanes reading 16
+// consecutive rows at one column touch 16 disjoint groups of 4 banks.
 template <int D>
 struct Geo {
   static constexpr int KROW = D * 2 + 16;
@@ -80,12 +81,12 @@ struct Geo {
   static constexpr int BUF = KBYTES + VBYTES + MBYTES;
 };
 
-// Position of key k (0..31) inside a V^T row.  The PV product for keys
-// 16m .. 16m+15 takes, in lane half h, operand slot j = key
-// 16m + 8*(j/4) + 4h + j%4 (the key order of the score accumulator), so
+// Position of key k (0..kKeys-1) inside a V^T row.  The PV product for keys
+// 16m .. 16m+15 of a 32-key sub-tile takes, in lane half h, operand slot j =
+// key 16m + 8*(j/4) + 4h + j%4 (the key order of the score accumulator), so
 // keys are stored at 16m + 8h + j to make each slot group one 16-byte read.
 __device__ __forceinline__ int vpos(int k) {
-  return 16 * (k >> 4) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
+  return 32 * (k >> 5) + 16 * ((k >> 4) & 1) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
 }
 
 template <int D, bool CAUSAL, bool MASK>
@@ -136,14 +137,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const Prefill
     qf[c] = (tq < n_max) ? *reinterpret_cast<const U4*>(qg + ((int64_t)tq * D + 16 * c + 8 * hh) * 2) : U4{0, 0, 0, 0};
 
   // ---- staging of one K/V tile: global -> registers -> LDS ----
-  // K: 32 rows x D*2 bytes = 32*D/8 chunks of 16 B, KCH per thread.
+  // K: kKeys rows x D*2 bytes in 16-byte chunks, KCH per thread.
   constexpr int KCH = kKeys * D / 8 / kThreads;
-  // V: thread handles keys (2m, 2m+1) x 8 columns d in [8 dg, 8 dg + 8);
-  // 16 key pairs x D/8 column groups = 2*D threads (D = 64: half the block).
-  const int vm = tid & 15, vdg = tid >> 4;
-  const bool v_active = vdg < D / 8;
-  U4 kreg[KCH], vreg[2];
-  uint32_t mflag = 0;  // threads 0..31: valid flag of key kt0 + tid
+  // V: a thread handles key pairs (2m, 2m+1) x 8 columns d in [8 dg, 8 dg+8);
+  // kKeys/2 pairs x D/8 column groups = VCH items per thread.
+  constexpr int VITEMS = (kKeys / 2) * (D / 8);
+  constexpr int VCH = VITEMS / kThreads;
+  static_assert(VCH * kThreads == VITEMS && KCH * kThreads == kKeys * D / 8, "staging split");
+  U4 kreg[KCH], vreg[VCH][2];
+  uint32_t mflag = 0;  // threads 0..kKeys-1: valid flag of key kt0 + tid
 
   // A key is valid if it is a real token (< q_len) and, with a key mask,
   // its mask byte (at absolute position P + key) is nonzero.
@@ -161,12 +163,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const Prefill
       const int col = ch % (D / 8);
       kreg[c] = (key < n_max) ? *reinterpret_cast<const U4*>(kg + ((int64_t)key * D + col * 8) * 2) : U4{0, 0, 0, 0};
     }
-    if (v_active) {
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int item = tid + c * kThreads;
+      const int vm = item % (kKeys / 2), vdg = item / (kKeys / 2);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int key = kt0 + 2 * vm + e;
-        vreg[e] = key_valid(key) ? *reinterpret_cast<const U4*>(vg + ((int64_t)key * D + 8 * vdg) * 2)
-                                 : U4{0, 0, 0, 0};
+        vreg[c][e] = key_valid(key) ? *reinterpret_cast<const U4*>(vg + ((int64_t)key * D + 8 * vdg) * 2)
+                                    : U4{0, 0, 0, 0};
       }
     }
   };
@@ -179,10 +184,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const Prefill
       const int ch = tid + c * kThreads;
       *reinterpret_cast<U4*>(kl + (ch / (D / 8)) * GE::KROW + (ch % (D / 8)) * 16) = kreg[c];
     }
-    if (v_active) {
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int item = tid + c * kThreads;
+      const int vm = item % (kKeys / 2), vdg = item / (kKeys / 2);
       // transpose 2 keys x 8 columns into 8 dwords (key 2m low, 2m+1 high)
-      const uint32_t x0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t x1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+      const uint32_t x0[4] = {vreg[c][0].x, vreg[c][0].y, vreg[c][0].z, vreg[c][0].w};
+      const uint32_t x1[4] = {vreg[c][1].x, vreg[c][1].y, vreg[c][1].z, vreg[c][1].w};
       const int pos = vpos(2 * vm);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -218,36 +226,46 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const Prefill
     if (kt0 < wave_end) {
       const uint8_t* kl = smem + buf * GE::BUF;
       const uint8_t* vl = kl + GE::KBYTES;
-      // S^T for keys kt0 + 8*(r/4) + 4hh + r%4, query q0 + lc
-      f32x16 s;
+      // S^T of the two 32-key sub-tiles: keys kt0 + 32 st + 8*(r/4) + 4hh +
+      // r%4, query q0 + lc; the two accumulation chains interleave.
+      f32x16 s[kSub];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      for (int st = 0; st < kSub; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
 #pragma unroll
       for (int cc = 0; cc < DK; ++cc) {
-        const U4 kf = *reinterpret_cast<const U4*>(kl + lc * GE::KROW + (16 * cc + 8 * hh) * 2);
-        s = mfma(kf, qf[cc], s);
+#pragma unroll
+        for (int st = 0; st < kSub; ++st) {
+          const U4 kf = *reinterpret_cast<const U4*>(kl + (32 * st + lc) * GE::KROW + (16 * cc + 8 * hh) * 2);
+          s[st] = mfma(kf, qf[cc], s[st]);
+        }
       }
       // masking: causal edge, keys beyond q_len, key mask.  The tile's key
-      // flags come from LDS as words of 4 keys (keys 8g + 4hh + 0..3).
+      // flags come from LDS as words of 4 keys (keys 32st + 8g + 4hh + 0..3).
       const bool edge = (kt0 + kKeys > qlen) || (CAUSAL && kt0 + kKeys - 1 > q0);
       if (MASK || edge) {
         const uint32_t* mw = reinterpret_cast<const uint32_t*>(vl + GE::VBYTES);
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const uint32_t w = mw[2 * gq + hh];
+        for (int st = 0; st < kSub; ++st)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * gq + e;
-            const int key = kt0 + 8 * gq + 4 * hh + e;
-            const bool ok = ((w >> (8 * e)) & 0xffu) != 0 && (!CAUSAL || key <= tq);
-            s[r] = ok ? s[r] : -INFINITY;
+          for (int gq = 0; gq < 4; ++gq) {
+            const uint32_t w = mw[8 * st + 2 * gq + hh];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * gq + e;
+              const int key = kt0 + 32 * st + 8 * gq + 4 * hh + e;
+              const bool ok = ((w >> (8 * e)) & 0xffu) != 0 && (!CAUSAL || key <= tq);
+              s[st][r] = ok ? s[st][r] : -INFINITY;
+            }
           }
-        }
       }
       // running maximum of this query (log2 domain), raised lazily
-      float tm = s[0];
+      float tm = s[0][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) tm = fmaxf(tm, s[r]);
+      for (int st = 0; st < kSub; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[st][r]);
       {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
         tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
@@ -262,24 +280,31 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const Prefill
         mrun = mnew;
       }
       const float msub = (mrun == -INFINITY) ? 0.f : mrun;
-      float p[16];
+      U4 pf[kSub][2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -msub));
-      U4 pf[2];
+      for (int st = 0; st < kSub; ++st) {
+        float p[16];
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-        pf[m] = U4{pack_bf16(p[8 * m], p[8 * m + 1]), pack_bf16(p[8 * m + 2], p[8 * m + 3]),
-                   pack_bf16(p[8 * m + 4], p[8 * m + 5]), pack_bf16(p[8 * m + 6], p[8 * m + 7])};
-      // O^T += V^T P^T ; l += 1 . P^T
+        for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[st][r], c, -msub));
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int m = 0; m < 2; ++m)
+          pf[st][m] = U4{pack_bf16(p[8 * m], p[8 * m + 1]), pack_bf16(p[8 * m + 2], p[8 * m + 3]),
+                         pack_bf16(p[8 * m + 4], p[8 * m + 5]), pack_bf16(p[8 * m + 6], p[8 * m + 7])};
+      }
+      // O^T += V^T P^T ; l += 1 . P^T   (consecutive MFMAs hit different
+      // accumulators)
+#pragma unroll
+      for (int st = 0; st < kSub; ++st)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const U4 vf = *reinterpret_cast<const U4*>(vl + (32 * dt + lc) * GE::VROW + (16 * m + 8 * hh) * 2);
-          o[dt] = mfma(vf, pf[m], o[dt]);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const U4 vf =
+                *reinterpret_cast<const U4*>(vl + (32 * dt + lc) * GE::VROW + (32 * st + 16 * m + 8 * hh) * 2);
+            o[dt] = mfma(vf, pf[st][m], o[dt]);
+          }
+          lsum = mfma(ones, pf[st][m], lsum);
         }
-      lsum = mfma(ones, pf[0], lsum);
-      lsum = mfma(ones, pf[1], lsum);
     }
     if (it + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
