@@ -24,6 +24,7 @@ the roofline.  The CPU baseline is the fp64 oracle on the host, timed on the
 same inputs (single thread).
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -45,6 +46,32 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
 METRIC = "decode-attn HBM GB/s (% of peak) & seqs/s; prefill TFLOP/s (% MFMA peak)"
 DEV = "cuda"
+
+
+DECODE_SOURCES = ("kv_cache_decode_attn_amd/csrc/decode.hip", "kv_cache_decode_attn_amd/csrc/common.h",
+                  "kv_cache_decode_attn_amd/csrc/launch.h")
+
+
+def decode_source_sha():
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def decode_traffic():
+    """HBM bytes per attn_decode call measured with rocprofv3 counters
+    (profiles/decode_traffic.json), or None when that measurement was taken
+    on different decode kernel sources."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "decode_traffic.json")) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != decode_source_sha():
+        return None
+    return d.get("bytes_per_call")
 
 
 def _events(n):
@@ -349,7 +376,7 @@ def main(argv=None):
         "per_launch": launch,
         "roofline": {"bound": "hbm", "kernel": "attn_decode (decode_partition + decode_merge)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "bytes_per_launch": w.decode_bytes(), "traffic": None},
+                     "bytes_per_launch": w.decode_bytes(), "traffic": decode_traffic()},
     }
     if not args.no_cpu_baseline:
         base, err = w.cpu_baseline(args.cpu_seqs)
@@ -381,7 +408,10 @@ def main(argv=None):
         msp, _ = time_steps(pf, max(3, args.steps // 4), 1)
         tf = pf.flops() / (msp * 1e-3) / 1e12
         extra["prefill8k"] = {"config": pf.config(), "ms_per_step": msp, "TFLOP/s": tf,
-                              "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS, "flops": pf.flops()}
+                              "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS, "flops": pf.flops(),
+                              "roofline": {"bound": "mfma", "kernel": "attn_prefill (kv_append + prefill_mfma_kernel)",
+                                           "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                           "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
         del pf
         torch.cuda.empty_cache()
     if extra:
