@@ -367,14 +367,21 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   }
 }
 
-// Merge the split-K partials of one (sequence, query head): the partition
-// maxima and sums are staged in LDS, their weights exp2(m_p - M) formed once,
-// then each thread combines one output element over all partitions.
+// Merge the split-K partials of one (sequence, query head), for 32 output
+// columns per workgroup: the partition maxima give M, each partition's
+// weight exp2(m_p - M) is staged in LDS (0 for an empty partition), and the
+// 256 threads (32 columns x 8 partition phases) sum w_p * o_p with several
+// independent loads in flight, then combine the phases through LDS.
+constexpr int kMergeCols = 32;
+constexpr int kMergePhases = 8;
+constexpr int kMergeStage = 2048;  // partitions whose weights are staged in LDS
+
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge(const DecodeLaunch p) {
-  __shared__ float wts[1024];
+  __shared__ float wts[kMergeStage];
   __shared__ float red[2][4];
-  const int hq = blockIdx.x, b = blockIdx.y;
+  __shared__ float part[kMergePhases][kMergeCols];
+  const int hq = blockIdx.x, b = blockIdx.y, c0 = blockIdx.z * kMergeCols;
   const int T = p.part_tokens;
   const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
   const int np = (ctx + T - 1) / T;
@@ -383,19 +390,17 @@ __global__ void __launch_bounds__(256) decode_merge(const DecodeLaunch p) {
   const int64_t slot0 = ((int64_t)b * p.num_q_heads + hq) * p.num_parts;
   const float* ml = p.ws_ml + slot0 * 2;
   const float* wo = p.ws_o + slot0 * D;
-  // global max over partitions
   float M = -INFINITY;
   for (int i = tid; i < np; i += 256) M = fmaxf(M, ml[2 * i]);
   M = group_max<64>(M);
   if (lane == 0) red[0][wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  // partition weights (0 for empty partitions) and the total sum
   float L = 0.f;
   for (int i = tid; i < np; i += 256) {
     const float m = ml[2 * i];
     const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    if (i < 1024) wts[i] = w;
+    if (i < kMergeStage) wts[i] = w;
     L = fmaf(w, ml[2 * i + 1], L);
   }
   L = group_sum<64>(L);
@@ -403,22 +408,32 @@ __global__ void __launch_bounds__(256) decode_merge(const DecodeLaunch p) {
   __syncthreads();
   L = red[1][0] + red[1][1] + red[1][2] + red[1][3];
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  // 256 threads: D columns x (256 / D) partition phases, combined in LDS
-  constexpr int PH = 256 / D;
-  const int d = tid % D, ph = tid / D;
-  float acc = 0.f;
-  for (int i = ph; i < np; i += PH) {
-    const float w = (i < 1024) ? wts[i] : ((ml[2 * i] == -INFINITY) ? 0.f : exp2f(ml[2 * i] - M));
-    if (w != 0.f) acc = fmaf(w, wo[(int64_t)i * D + d], acc);
+  const int col = tid % kMergeCols, ph = tid / kMergeCols;
+  const float* src = wo + c0 + col;
+  auto weight = [&](int i) -> float {
+    if (i < kMergeStage) return wts[i];
+    const float m = ml[2 * i];
+    return (m == -INFINITY) ? 0.f : exp2f(m - M);
+  };
+  float acc0 = 0.f, acc1 = 0.f;
+  int i = ph;
+  for (; i + kMergePhases < np; i += 2 * kMergePhases) {
+    const float w0 = weight(i), w1 = weight(i + kMergePhases);
+    const float x0 = src[(int64_t)i * D], x1 = src[(int64_t)(i + kMergePhases) * D];
+    if (w0 != 0.f) acc0 = fmaf(w0, x0, acc0);
+    if (w1 != 0.f) acc1 = fmaf(w1, x1, acc1);
   }
-  __syncthreads();
-  wts[tid] = acc;
+  if (i < np) {
+    const float w0 = weight(i);
+    if (w0 != 0.f) acc0 = fmaf(w0, src[(int64_t)i * D], acc0);
+  }
+  part[ph][col] = acc0 + acc1;
   __syncthreads();
   if (ph == 0) {
-    float s = acc;
+    float sum = part[0][col];
 #pragma unroll
-    for (int k = 1; k < PH; ++k) s += wts[k * D + d];
-    p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = s * inv;
+    for (int k = 1; k < kMergePhases; ++k) sum += part[k][col];
+    p.out[((int64_t)b * p.num_q_heads + hq) * D + c0 + col] = sum * inv;
   }
 }
 
@@ -429,7 +444,7 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
   hipLaunchKernelGGL((decode_partition<KVT, D, G, MASK>), grid, dim3(256), lds, s, a);
   if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
   if (a.num_parts > 1) {
-    hipLaunchKernelGGL((decode_merge<D>), dim3(a.num_q_heads, a.batch), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_merge<D>), dim3(a.num_q_heads, a.batch, D / kMergeCols), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
   }
   return KVATTN_OK;
