@@ -258,3 +258,18 @@ def test_fp8_decode_table_through_attention():
                         block_table=table).cpu().numpy()
     want = codec.e4m3_decode(codes).reshape(2, 128)
     np.testing.assert_array_equal(got[:, 0, :], want)
+
+
+@pytest.mark.parametrize("G,d", [(8, 128), (4, 128), (8, 64), (4, 64)])
+def test_fp8_gqa_key_mask_nan_codes_and_edge_lengths(G, d):
+    """fp8 cache, GQA 4/8 (the matrix-core partition pass): a random key mask
+    whose masked positions hold NaN codes, stale NaN codes in the tail slots,
+    and lengths around the 16-token block and partition edges."""
+    lens = [1, 15, 16, 17, 64, 129, 300]
+    mask = synth.random_mask((len(lens), 304), 0.6, (21, synth.T_MASK))
+    mask[:, 0] = 1
+    c = Case(len(lens), 2 * G, 2, d, lens, dtype=K.FP8_E4M3, seed=21 + G + d, mask=mask)
+    for part in (64, 128, 0):
+        got = c.run(part).cpu().numpy()
+        assert np.isfinite(got).all()
+        assert max_abs(got, c.oracle(quantised=True)) <= TOL
