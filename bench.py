@@ -119,7 +119,7 @@ class PagedDecode:
             K.kv_append(c, self.src_k, self.src_v, zeros, block_table=self.table, n_valid=self.positions)
             self.caches.append(c)
         self.out = torch.empty((self.B, self.Hq, self.D), dtype=torch.float32, device=DEV)
-        self.part = K.decode_default_part_tokens(self.B, self.Hq, self.Hkv, self.max_seq_len)
+        self.part = K.decode_default_part_tokens(K.BF16, self.B, self.Hq, self.Hkv, self.max_seq_len)
         self.ws = K.decode_workspace(self.caches[0], self.B, self.Hq, self.max_seq_len, self.part)
         torch.cuda.synchronize()
 
@@ -209,7 +209,7 @@ class PaddedDecode:
             self.v_new.append(torch.gather(c.v, 2, idx).contiguous())
             self.q.append(synth.normal_device((self.B, self.H, self.D), (wid, synth.T_Q, layer)))
         self.out = torch.empty((self.L, self.B, self.H, self.D), dtype=torch.float32, device=DEV)
-        self.part = K.decode_default_part_tokens(self.B, self.H, self.H, self.cap)
+        self.part = K.decode_default_part_tokens(K.BF16, self.B, self.H, self.H, self.cap)
         self.ws = K.decode_workspace(self.caches[0], self.B, self.H, self.cap, self.part)
         torch.cuda.synchronize()
 
@@ -262,7 +262,7 @@ class LongContextFp8Decode:
             self.tables.append(tdev)
             self.q.append(synth.normal_device((1, self.Hq, self.D), (wid, synth.T_Q, layer)))
         self.out = torch.empty((self.L, 1, self.Hq, self.D), dtype=torch.float32, device=DEV)
-        self.part = K.decode_default_part_tokens(1, self.Hq, self.Hkv, self.ctx)
+        self.part = K.decode_default_part_tokens(K.FP8_E4M3, 1, self.Hq, self.Hkv, self.ctx)
         self.ws = K.decode_workspace(self.caches[0], 1, self.Hq, self.ctx, self.part)
         torch.cuda.synchronize()
 

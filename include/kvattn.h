@@ -158,13 +158,15 @@ int kvattn_kv_append(const kvattn_cache* cache, int32_t batch, int32_t n_new,
  * (split-K partials: per (sequence, query head, partition) an fp32 output
  * vector plus the running max and sum).  part_tokens as in
  * kvattn_attn_decode (0 = default).  Returns 0 for invalid sizes. */
-size_t kvattn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                     int32_t head_dim, int32_t max_seq_len, int32_t part_tokens);
+size_t kvattn_decode_workspace_bytes(int32_t cache_dtype, int32_t batch, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                     int32_t part_tokens);
 
 /* Keys per split-K partition that part_tokens == 0 selects for these sizes
- * (enough partitions to give the 256 compute units several workgroups
- * each).  Returns 0 for invalid sizes. */
-int32_t kvattn_decode_default_part_tokens(int32_t batch, int32_t num_q_heads,
+ * and this cache element type (measured per partition kernel: enough
+ * workgroups for the 256 compute units, few enough partials for the merge).
+ * Returns 0 for invalid sizes. */
+int32_t kvattn_decode_default_part_tokens(int32_t cache_dtype, int32_t batch, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t max_seq_len);
 
 /* kvattn_attn_decode - one new query token per sequence against the cache.
@@ -194,7 +196,8 @@ int32_t kvattn_decode_default_part_tokens(int32_t batch, int32_t num_q_heads,
  *  workspace   device, >= kvattn_decode_workspace_bytes(...) bytes, 16-byte
  *              aligned; contents on entry are ignored
  *  part_tokens keys per partition: 0 = default, else a multiple of 64 in
- *              [64, 8192] with part_tokens * G <= 8192
+ *              [64, 8192]; with a bf16/f32 cache (and fp8 with G < 4) also
+ *              part_tokens * G <= 8192
  * Bitwise deterministic for fixed arguments (fixed partitioning, no atomics).
  */
 int kvattn_attn_decode(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads,

@@ -59,8 +59,8 @@ _SIGS = {
     "kvattn_last_error": (ctypes.c_char_p, []),
     "kvattn_cache_bytes": (_U64, [_U64] * 6),
     "kvattn_kv_append": (ctypes.c_int, [_CP, _I32, _I32, _P, _P, _I32, _P, _P, _P, _I32, _P]),
-    "kvattn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
-    "kvattn_decode_default_part_tokens": (_I32, [_I32, _I32, _I32, _I32]),
+    "kvattn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "kvattn_decode_default_part_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "kvattn_attn_decode": (ctypes.c_int, [_CP, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _I64,
                                           _F, _P, _P, _SZ, _I32, _P]),
     "kvattn_attn_prefill": (ctypes.c_int, [_CP, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P,

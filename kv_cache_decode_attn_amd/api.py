@@ -142,18 +142,19 @@ def kv_append(cache, k_new, v_new, positions, block_table=None, n_valid=None):
                                  _ptr(positions), _ptr(n_valid), _ptr(block_table), mb, _stream(k_new.device)))
 
 
-def decode_default_part_tokens(batch, num_q_heads, num_kv_heads, max_seq_len):
-    return int(lib().kvattn_decode_default_part_tokens(batch, num_q_heads, num_kv_heads, max_seq_len))
+def decode_default_part_tokens(cache_dtype, batch, num_q_heads, num_kv_heads, max_seq_len):
+    return int(lib().kvattn_decode_default_part_tokens(cache_dtype, batch, num_q_heads, num_kv_heads, max_seq_len))
 
 
-def decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, part_tokens=0):
-    return int(lib().kvattn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                                   part_tokens))
+def decode_workspace_bytes(cache_dtype, batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, part_tokens=0):
+    return int(lib().kvattn_decode_workspace_bytes(cache_dtype, batch, num_q_heads, num_kv_heads, head_dim,
+                                                   max_seq_len, part_tokens))
 
 
 def decode_workspace(cache, batch, num_q_heads, max_seq_len, part_tokens=0):
     """A workspace tensor large enough for attn_decode with these sizes."""
-    n = decode_workspace_bytes(batch, num_q_heads, cache.num_kv_heads, cache.head_dim, max_seq_len, part_tokens)
+    n = decode_workspace_bytes(cache.dtype, batch, num_q_heads, cache.num_kv_heads, cache.head_dim, max_seq_len,
+                               part_tokens)
     return torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device=cache.device)
 
 

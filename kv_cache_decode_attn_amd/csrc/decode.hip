@@ -485,7 +485,9 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     const int tok0 = (j0 + jb) * kBlockTokens;
     if (off >= 0) {
       // ---- scores S^T (keys 4*lg + r, head r16) ----
-      v4f sacc = v4f{0.f, 0.f, 0.f, 0.f};
+      // two accumulation chains (even / odd steps) so consecutive MFMAs are
+      // independent
+      v4f sacc = v4f{0.f, 0.f, 0.f, 0.f}, sacc2 = v4f{0.f, 0.f, 0.f, 0.f};
       const uint32_t* kw = reinterpret_cast<const uint32_t*>(kr);
 #pragma unroll
       for (int sd = 0; sd < KS; ++sd) {
@@ -493,8 +495,12 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
         cvt4(kw[sd], a0, a1);
         const v4s av = __builtin_bit_cast(v4s, (uint2){a0, a1});
         const v4s bv = __builtin_bit_cast(v4s, (uint2){qb[sd][0], qb[sd][1]});
-        sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, sacc, 0, 0, 0);
+        if (sd & 1)
+          sacc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, sacc2, 0, 0, 0);
+        else
+          sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, sacc, 0, 0, 0);
       }
+      sacc += sacc2;
       // ---- mask, block max, lazily raised running max ----
       const bool full = !MASK && tok0 + kBlockTokens <= t1;
       float z[4];
@@ -557,14 +563,21 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
                                 __builtin_amdgcn_perm(t23l, t01l, 0x07060302u),
                                 __builtin_amdgcn_perm(t23h, t01h, 0x05040100u),
                                 __builtin_amdgcn_perm(t23h, t01h, 0x07060302u)};
+        v4s av[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           uint32_t b0, b1;
           cvt4(tj[j], b0, b1);
-          const v4s av = __builtin_bit_cast(v4s, (uint2){b0, b1});
-          o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, phi, o[4 * hf + j], 0, 0, 0);
-          o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, plo, o[4 * hf + j], 0, 0, 0);
+          av[j] = __builtin_bit_cast(v4s, (uint2){b0, b1});
         }
+        // hi parts of the four tiles, then the lo parts: no back-to-back
+        // MFMAs on one accumulator
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], phi, o[4 * hf + j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], plo, o[4 * hf + j], 0, 0, 0);
       }
     }
 #pragma unroll

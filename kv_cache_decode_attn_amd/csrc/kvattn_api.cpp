@@ -99,16 +99,25 @@ int make_view(const char* who, const kvattn_cache* c, int32_t batch, const int32
 constexpr int32_t kMaxPartTokens = 8192;
 constexpr int32_t kMaxPartScores = 8192;  // part_tokens * group, bounds the LDS
 
-int32_t default_part_tokens(int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len) {
+// Default keys per partition, per partition kernel (measured on MI355X):
+//  - fp8 cache with G >= 4 (matrix-core pass): long partitions amortise the
+//    per-workgroup combine and shrink the merge; take the largest size that
+//    still gives >= 512 workgroups (2048 keys at 131K keys x 8 KV heads).
+//  - vector-ALU pass: 512 keys for G >= 4, 256 for G <= 2, shrunk until the
+//    grid offers >= 2048 workgroups.
+bool fp8_mfma_pass(int32_t dtype, int32_t group) { return dtype == KVATTN_FP8_E4M3 && group >= 4; }
+
+int32_t default_part_tokens(int32_t dtype, int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len) {
   const int32_t group = hq / hkv;
-  int32_t t = 512;
-  while (t * group > kMaxPartScores) t /= 2;
-  // Shrink the partition until the grid offers >= 2048 workgroups.
-  while (t > 64) {
-    const int64_t parts = ((int64_t)max_seq_len + t - 1) / t;
-    if ((int64_t)batch * hkv * parts >= 2048) break;
-    t /= 2;
+  auto wgs = [&](int32_t t) { return (int64_t)batch * hkv * (((int64_t)max_seq_len + t - 1) / t); };
+  if (fp8_mfma_pass(dtype, group)) {
+    int32_t t = kMaxPartTokens;
+    while (t > 256 && wgs(t) < 512) t /= 2;
+    return t;
   }
+  int32_t t = group >= 4 ? 512 : 256;
+  while (t * group > kMaxPartScores) t /= 2;
+  while (t > 64 && wgs(t) < 2048) t /= 2;
   return t;
 }
 
@@ -177,16 +186,19 @@ int kvattn_kv_append(const kvattn_cache* cache, int32_t batch, int32_t n_new, co
   return ok();
 }
 
-int32_t kvattn_decode_default_part_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                          int32_t max_seq_len) {
-  if (batch < 0 || max_seq_len < 0 || !group_ok(num_q_heads, num_kv_heads)) return 0;
-  return default_part_tokens(batch, num_q_heads, num_kv_heads, max_seq_len);
+int32_t kvattn_decode_default_part_tokens(int32_t cache_dtype, int32_t batch, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t max_seq_len) {
+  if (batch < 0 || max_seq_len < 0 || !elem_bytes(cache_dtype) || !group_ok(num_q_heads, num_kv_heads)) return 0;
+  return default_part_tokens(cache_dtype, batch, num_q_heads, num_kv_heads, max_seq_len);
 }
 
-size_t kvattn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                     int32_t max_seq_len, int32_t part_tokens) {
-  if (batch < 0 || max_seq_len < 0 || head_dim <= 0 || !group_ok(num_q_heads, num_kv_heads)) return 0;
-  const int32_t t = part_tokens ? part_tokens : default_part_tokens(batch, num_q_heads, num_kv_heads, max_seq_len);
+size_t kvattn_decode_workspace_bytes(int32_t cache_dtype, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t max_seq_len, int32_t part_tokens) {
+  if (batch < 0 || max_seq_len < 0 || head_dim <= 0 || !elem_bytes(cache_dtype) ||
+      !group_ok(num_q_heads, num_kv_heads))
+    return 0;
+  const int32_t t =
+      part_tokens ? part_tokens : default_part_tokens(cache_dtype, batch, num_q_heads, num_kv_heads, max_seq_len);
   if (t <= 0) return 0;
   const int64_t parts = ((int64_t)max_seq_len + t - 1) / t;
   if (parts <= 1) return 0;
@@ -219,8 +231,10 @@ int kvattn_attn_decode(const kvattn_cache* cache, int32_t batch, int32_t num_q_h
                 max_seq_len);
   const int32_t group = num_q_heads / cache->num_kv_heads;
   int32_t t = part_tokens;
-  if (t == 0) t = default_part_tokens(batch, num_q_heads, cache->num_kv_heads, max_seq_len);
-  if (t < 64 || t > kMaxPartTokens || t % 64 != 0 || t * group > kMaxPartScores)
+  if (t == 0) t = default_part_tokens(cache->dtype, batch, num_q_heads, cache->num_kv_heads, max_seq_len);
+  // the fp8 matrix-core pass (group >= 4) keeps no per-key scores in LDS
+  const bool scores_in_lds = !fp8_mfma_pass(cache->dtype, group);
+  if (t < 64 || t > kMaxPartTokens || t % 64 != 0 || (scores_in_lds && t * group > kMaxPartScores))
     return fail(KVATTN_EINVAL, "%s: part_tokens %d: need a multiple of 64 in [64, %d] with part_tokens*group <= %d",
                 who, t, kMaxPartTokens, kMaxPartScores);
   const int64_t parts = ((int64_t)max_seq_len + t - 1) / t;
@@ -228,8 +242,8 @@ int kvattn_attn_decode(const kvattn_cache* cache, int32_t batch, int32_t num_q_h
   float* ws_o = nullptr;
   float* ws_ml = nullptr;
   if (parts > 1) {
-    const size_t need = kvattn_decode_workspace_bytes(batch, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                                                      max_seq_len, t);
+    const size_t need = kvattn_decode_workspace_bytes(cache->dtype, batch, num_q_heads, cache->num_kv_heads,
+                                                      cache->head_dim, max_seq_len, t);
     if (!workspace || workspace_bytes < need)
       return fail(KVATTN_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", who, workspace ? workspace_bytes : 0,
                   need);

@@ -49,12 +49,15 @@ def test_cache_bytes_closed_forms_through_the_abi():
 
 def test_workspace_and_partition_sizing():
     L = _lib.lib()
-    t = L.kvattn_decode_default_part_tokens(32, 32, 8, 8193)
+    t = L.kvattn_decode_default_part_tokens(_lib.BF16, 32, 32, 8, 8193)
     assert t % 64 == 0 and 64 <= t <= 8192
     parts = (8193 + t - 1) // t
-    assert L.kvattn_decode_workspace_bytes(32, 32, 8, 128, 8193, t) == 32 * 32 * parts * 130 * 4
-    assert L.kvattn_decode_workspace_bytes(32, 32, 8, 128, 100, 512) == 0  # single partition
-    assert L.kvattn_decode_default_part_tokens(1, 3, 2, 100) == 0          # bad group
+    assert L.kvattn_decode_workspace_bytes(_lib.BF16, 32, 32, 8, 128, 8193, t) == 32 * 32 * parts * 130 * 4
+    assert L.kvattn_decode_workspace_bytes(_lib.BF16, 32, 32, 8, 128, 100, 512) == 0  # single partition
+    assert L.kvattn_decode_default_part_tokens(_lib.BF16, 1, 3, 2, 100) == 0          # bad group
+    assert L.kvattn_decode_default_part_tokens(9, 1, 8, 8, 100) == 0                  # bad dtype
+    # the fp8 matrix-core pass takes long partitions for one long sequence
+    assert L.kvattn_decode_default_part_tokens(_lib.FP8_E4M3, 1, 64, 8, 131073) == 2048
 
 
 FAKE = 0x10000  # an aligned non-null address; host validation never dereferences it
