@@ -5,9 +5,11 @@
 Prints ONE JSON line.  The headline workload (`value`) is the Llama-3-8B-
 shaped paged GQA decode step: batch 32, 32 query / 8 KV heads, head_dim 128,
 bf16 cache in 16-token blocks behind a permuted block table, cached lengths
-uniform in [1, 8192]; a step appends one token per sequence (kv_append) and
-attends it (attn_decode = split-K partition pass + merge pass).  `value` is
-algorithmic HBM bytes per step / step time, in GB/s.
+uniform in [1, 8192]; a step appends one token per sequence and attends it,
+in one library call (attn_decode_append: the split-K partition pass, which
+also stores the new token, then the merge pass).  `value` is algorithmic
+HBM bytes per step / step time, in GB/s.  The same step as two calls
+(kv_append, then attn_decode) is timed too and reported beside it.
 
 Other workloads run in the same invocation and are reported under
 "workloads": the padded 32-layer MHA decode (batch 8, 4096-position
@@ -91,7 +93,8 @@ class PagedDecode:
 
     name = "llama3-8b-paged-gqa-decode"
 
-    def __init__(self, replicas=4, wid=2):
+    def __init__(self, replicas=4, wid=2, fused=True):
+        self.fused = fused
         self.B, self.Hq, self.Hkv, self.D = 32, 32, 8, 128
         self.cached = synth.uniform_lengths(self.B, 1, 8192, (wid, synth.T_LENS))
         self.ctx = (self.cached + 1).astype(np.int32)          # keys incl. the appended token
@@ -110,6 +113,8 @@ class PagedDecode:
             self.B, self.Hkv, 1, self.D)
         self.k_new = torch.gather(self.src_k, 2, idx).contiguous()
         self.v_new = torch.gather(self.src_v, 2, idx).contiguous()
+        self.k_new3 = self.k_new[:, :, 0].contiguous()   # [B, Hkv, D] rows of the fused call
+        self.v_new3 = self.v_new[:, :, 0].contiguous()
         self.positions = torch.from_numpy(self.cached).to(DEV)
         self.seq_lens = torch.from_numpy(self.ctx).to(DEV)
         zeros = torch.zeros(self.B, dtype=torch.int32, device=DEV)
@@ -142,6 +147,12 @@ class PagedDecode:
         c = self.caches[i % len(self.caches)]
         if ev:
             ev[0].record()
+        if self.fused:
+            K.attn_decode_append(c, self.q, self.k_new3, self.v_new3, self.seq_lens, self.max_seq_len,
+                                 block_table=self.table, out=self.out, workspace=self.ws, part_tokens=self.part)
+            if ev:
+                ev[1].record()
+            return
         K.kv_append(c, self.k_new, self.v_new, self.positions, block_table=self.table)
         if ev:
             ev[1].record()
@@ -149,6 +160,10 @@ class PagedDecode:
                       workspace=self.ws, part_tokens=self.part)
         if ev:
             ev[2].record()
+
+    def launch_names(self):
+        """Names of the calls the per-launch events of step() bracket."""
+        return ("attn_decode_append",) if self.fused else ("kv_append", "attn_decode")
 
     def config(self):
         return {"workload": self.name, "batch": self.B, "q_heads": self.Hq, "kv_heads": self.Hkv,
@@ -205,8 +220,8 @@ class PaddedDecode:
             synth.normal_device(c.v.shape, (wid, synth.T_V, layer), out=c.v)
             self.caches.append(c)
             # the new token is the one at real_b - 1 (re-written in place each step)
-            self.k_new.append(torch.gather(c.k, 2, idx).contiguous())
-            self.v_new.append(torch.gather(c.v, 2, idx).contiguous())
+            self.k_new.append(torch.gather(c.k, 2, idx)[:, :, 0].contiguous())
+            self.v_new.append(torch.gather(c.v, 2, idx)[:, :, 0].contiguous())
             self.q.append(synth.normal_device((self.B, self.H, self.D), (wid, synth.T_Q, layer)))
         self.out = torch.empty((self.L, self.B, self.H, self.D), dtype=torch.float32, device=DEV)
         self.part = K.decode_default_part_tokens(K.BF16, self.B, self.H, self.H, self.cap)
@@ -220,10 +235,9 @@ class PaddedDecode:
 
     def step(self, i, ev=None):
         for layer in range(self.L):
-            c = self.caches[layer]
-            K.kv_append(c, self.k_new[layer], self.v_new[layer], self.positions)
-            K.attn_decode(c, self.q[layer], self.seq_lens, self.cap, key_mask=self.mask, out=self.out[layer],
-                          workspace=self.ws, part_tokens=self.part)
+            K.attn_decode_append(self.caches[layer], self.q[layer], self.k_new[layer], self.v_new[layer],
+                                 self.seq_lens, self.cap, key_mask=self.mask, out=self.out[layer], workspace=self.ws,
+                                 part_tokens=self.part)
 
     def config(self):
         return {"workload": self.name, "layers": self.L, "batch": self.B, "q_heads": self.H, "kv_heads": self.H,
@@ -255,8 +269,8 @@ class LongContextFp8Decode:
             sk = synth.normal_device((1, self.Hkv, self.ctx, self.D), (wid, synth.T_K, layer))
             sv = synth.normal_device((1, self.Hkv, self.ctx, self.D), (wid, synth.T_V, layer))
             K.kv_append(c, sk, sv, zeros, block_table=tdev, n_valid=pos)
-            self.k_new.append(sk[:, :, self.cached:].contiguous())
-            self.v_new.append(sv[:, :, self.cached:].contiguous())
+            self.k_new.append(sk[:, :, self.cached].contiguous())
+            self.v_new.append(sv[:, :, self.cached].contiguous())
             del sk, sv
             self.caches.append(c)
             self.tables.append(tdev)
@@ -273,10 +287,9 @@ class LongContextFp8Decode:
 
     def step(self, i, ev=None):
         for layer in range(self.L):
-            c = self.caches[layer]
-            K.kv_append(c, self.k_new[layer], self.v_new[layer], self.positions, block_table=self.tables[layer])
-            K.attn_decode(c, self.q[layer], self.seq_lens, self.ctx, block_table=self.tables[layer],
-                          out=self.out[layer], workspace=self.ws, part_tokens=self.part)
+            K.attn_decode_append(self.caches[layer], self.q[layer], self.k_new[layer], self.v_new[layer],
+                                 self.seq_lens, self.ctx, block_table=self.tables[layer], out=self.out[layer],
+                                 workspace=self.ws, part_tokens=self.part)
 
     def config(self):
         return {"workload": self.name, "layers": self.L, "batch": 1, "q_heads": self.Hq, "kv_heads": self.Hkv,
@@ -329,8 +342,7 @@ def time_steps(w, steps, warmup, per_launch=False):
     total_ms = start.elapsed_time(end)
     launch = None
     if per_launch:
-        launch = {"append": _stats([e[0].elapsed_time(e[1]) for e in evs]),
-                  "decode": _stats([e[1].elapsed_time(e[2]) for e in evs])}
+        launch = {n: _stats([e[k].elapsed_time(e[k + 1]) for e in evs]) for k, n in enumerate(w.launch_names())}
     return total_ms / steps, launch
 
 
@@ -352,10 +364,14 @@ def main(argv=None):
     names = [x for x in args.workloads.split(",") if x]
 
     w = PagedDecode()
+    # the same step as two calls (kv_append, attn_decode), for reference
+    w.fused = False
+    ms2, launch2 = time_steps(w, args.steps, args.warmup, per_launch=True)
+    w.fused = True
     ms, launch = time_steps(w, args.steps, args.warmup, per_launch=True)
     step_bytes = w.step_bytes()
-    dec_ms = launch["decode"]["mean_ms"]
-    achieved = w.decode_bytes() / (dec_ms * 1e-3) / 1e9
+    call_ms = launch["attn_decode_append"]["mean_ms"]
+    achieved = step_bytes / (call_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": step_bytes / (ms * 1e-3) / 1e9,
@@ -374,9 +390,12 @@ def main(argv=None):
         "seqs_per_s": w.B / (ms * 1e-3),
         "step_bytes": step_bytes,
         "per_launch": launch,
-        "roofline": {"bound": "hbm", "kernel": "attn_decode (decode_partition + decode_merge)",
+        "two_call_step": {"ms_per_step": ms2, "GB/s": step_bytes / (ms2 * 1e-3) / 1e9, "per_launch": launch2,
+                          "attn_decode_GB/s": w.decode_bytes() / (launch2["attn_decode"]["mean_ms"] * 1e-3) / 1e9},
+        "roofline": {"bound": "hbm",
+                     "kernel": "attn_decode_append (decode_partition with the fused append + decode_merge)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "bytes_per_launch": w.decode_bytes(), "traffic": decode_traffic()},
+                     "bytes_per_launch": step_bytes, "traffic": decode_traffic()},
     }
     if not args.no_cpu_baseline:
         base, err = w.cpu_baseline(args.cpu_seqs)

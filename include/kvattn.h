@@ -8,10 +8,12 @@
  * (c86j224s.github.io), section "State of scaled dot-product attention",
  * and "KV Cache" (heepie.pages.dev), section "Self-Attention".
  *
- * Three hot calls: kvattn_kv_append (write new K/V into the cache),
- * kvattn_attn_decode (one new token per sequence against the cache) and
- * kvattn_attn_prefill (many new tokens, causal/padding masked, optionally
- * writing the cache).  Plus sizing, validation and status helpers.
+ * Hot calls: kvattn_kv_append (write new K/V into the cache),
+ * kvattn_attn_decode (one new token per sequence against the cache),
+ * kvattn_attn_decode_append (both in one launch sequence: the decode step)
+ * and kvattn_attn_prefill (many new tokens, causal/padding masked,
+ * optionally writing the cache).  Plus sizing, validation and status
+ * helpers.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -208,6 +210,38 @@ int kvattn_attn_decode(const kvattn_cache* cache, int32_t batch, int32_t num_q_h
                        float scale, float* out,
                        void* workspace, size_t workspace_bytes, int32_t part_tokens,
                        void* stream);
+
+/* kvattn_attn_decode_append - one decode step in one call: append the new
+ * token's K/V, then attend it (append-then-attend, "Transformer Attention
+ * Masks and KV-Cache Inference", section "Prefill and decode stages";
+ * "KV Cache", section "TO-BE").
+ *
+ * Same result as kvattn_kv_append(positions = seq_lens - 1, n_new = 1)
+ * followed by kvattn_attn_decode with the same arguments, bit for bit (the
+ * cache bytes and the output), for every sequence with
+ * 1 <= seq_lens[b] <= min(max_seq_len, capacity); a sequence outside that
+ * range has nothing written.  The workgroup that attends key seq_lens[b] - 1
+ * encodes the new rows, uses them in place of that cache slot and stores
+ * them after its last cache read, so no separate write pass is launched.
+ *
+ *  k_new, v_new device [batch, num_kv_heads, head_dim] of in_dtype, 16-byte
+ *               aligned: the new token of each sequence
+ *  in_dtype     KVATTN_F32 or KVATTN_BF16; equal to cache->dtype unless the
+ *               cache is fp8 (conversion as in kvattn_kv_append)
+ *  every other argument as in kvattn_attn_decode.
+ * The cache slot of position seq_lens[b] - 1 must belong to sequence b
+ * alone (no other sequence's block table may map it) - as for any append
+ * that runs beside a read of the same layer.
+ */
+int kvattn_attn_decode_append(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads,
+                              const void* q, int32_t q_dtype,
+                              const void* k_new, const void* v_new, int32_t in_dtype,
+                              const int32_t* seq_lens, int32_t max_seq_len,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const uint8_t* key_mask, int64_t key_mask_stride,
+                              float scale, float* out,
+                              void* workspace, size_t workspace_bytes, int32_t part_tokens,
+                              void* stream);
 
 /* kvattn_attn_prefill - attention of n_max new tokens per sequence, causal
  * and/or padding masked, tiled so that no n x n score matrix is ever

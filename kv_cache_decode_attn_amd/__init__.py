@@ -7,11 +7,11 @@ the cache append, as hand-written HIP kernels behind a C ABI
 """
 from ._lib import (BF16, BLOCK_TOKENS, CONTIGUOUS, EINVAL, ELAUNCH, EUNSUPPORTED, EWORKSPACE, F32, FP8_E4M3, OK,
                    PAGED, VALIDATE_BLOCK_RANGE, VALIDATE_LEN_RANGE, VALIDATE_POSITION, KvattnError)
-from .api import (KVCache, attn_decode, attn_prefill, cache_bytes, decode_default_part_tokens, decode_workspace,
-                  decode_workspace_bytes, kv_append, validate, version)
+from .api import (KVCache, attn_decode, attn_decode_append, attn_prefill, cache_bytes, decode_default_part_tokens,
+                  decode_workspace, decode_workspace_bytes, kv_append, validate, version)
 
 __all__ = [
-    "KVCache", "attn_decode", "attn_prefill", "cache_bytes", "decode_default_part_tokens", "decode_workspace",
-    "decode_workspace_bytes", "kv_append", "validate", "version", "KvattnError",
+    "KVCache", "attn_decode", "attn_decode_append", "attn_prefill", "cache_bytes", "decode_default_part_tokens",
+    "decode_workspace", "decode_workspace_bytes", "kv_append", "validate", "version", "KvattnError",
     "F32", "BF16", "FP8_E4M3", "CONTIGUOUS", "PAGED", "BLOCK_TOKENS",
 ]

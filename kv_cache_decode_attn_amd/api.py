@@ -158,14 +158,7 @@ def decode_workspace(cache, batch, num_q_heads, max_seq_len, part_tokens=0):
     return torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device=cache.device)
 
 
-def attn_decode(cache, q, seq_lens, max_seq_len, block_table=None, key_mask=None, scale=None, out=None,
-                workspace=None, part_tokens=0):
-    """One query token per sequence against the cache (kvattn_attn_decode).
-
-    q: [B, Hq, d] (f32 for an f32 cache, bf16 otherwise); seq_lens int32 [B]
-    counts keys including the appended token; key_mask uint8 [B, >= max_seq_len]
-    (1 = attend) or None.  Returns fp32 [B, Hq, d].
-    """
+def _decode_args(cache, q, seq_lens, max_seq_len, block_table, key_mask, scale, out, workspace, part_tokens):
     _dev(q, "q")
     _i32(seq_lens, "seq_lens")
     _i32(block_table, "block_table")
@@ -181,13 +174,48 @@ def attn_decode(cache, q, seq_lens, max_seq_len, block_table=None, key_mask=None
     if workspace is None:
         workspace = decode_workspace(cache, B, Hq, max_seq_len, part_tokens)
     _dev(workspace, "workspace")
-    qcode = _CODE.get(q.dtype, -1)
     mb = block_table.shape[1] if block_table is not None else 0
     stride = key_mask.shape[1] if key_mask is not None else 0
-    check(lib().kvattn_attn_decode(ctypes.byref(cache.desc()), B, Hq, _ptr(q), qcode, _ptr(seq_lens), int(max_seq_len),
-                                   _ptr(block_table), mb, _ptr(key_mask), stride, float(scale), _ptr(out),
+    return B, Hq, float(scale), out, workspace, mb, stride
+
+
+def attn_decode(cache, q, seq_lens, max_seq_len, block_table=None, key_mask=None, scale=None, out=None,
+                workspace=None, part_tokens=0):
+    """One query token per sequence against the cache (kvattn_attn_decode).
+
+    q: [B, Hq, d] (f32 for an f32 cache, bf16 otherwise); seq_lens int32 [B]
+    counts keys including the appended token; key_mask uint8 [B, >= max_seq_len]
+    (1 = attend) or None.  Returns fp32 [B, Hq, d].
+    """
+    B, Hq, scale, out, workspace, mb, stride = _decode_args(cache, q, seq_lens, max_seq_len, block_table, key_mask,
+                                                            scale, out, workspace, part_tokens)
+    check(lib().kvattn_attn_decode(ctypes.byref(cache.desc()), B, Hq, _ptr(q), _CODE.get(q.dtype, -1), _ptr(seq_lens),
+                                   int(max_seq_len), _ptr(block_table), mb, _ptr(key_mask), stride, scale, _ptr(out),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), int(part_tokens),
                                    _stream(q.device)))
+    return out
+
+
+def attn_decode_append(cache, q, k_new, v_new, seq_lens, max_seq_len, block_table=None, key_mask=None, scale=None,
+                       out=None, workspace=None, part_tokens=0):
+    """One decode step (kvattn_attn_decode_append): k_new/v_new [B, Hkv, d]
+    (f32 or bf16) are stored at position seq_lens[b] - 1, then q attends the
+    cache as in attn_decode.  Returns fp32 [B, Hq, d]."""
+    _dev(k_new, "k_new")
+    _dev(v_new, "v_new")
+    if k_new.dtype not in _CODE or v_new.dtype != k_new.dtype or k_new.shape != v_new.shape:
+        raise TypeError("k_new/v_new must be matching f32 or bf16 tensors")
+    if k_new.dim() != 3 or k_new.shape[1] != cache.num_kv_heads or k_new.shape[2] != cache.head_dim:
+        raise ValueError("k_new shape %s does not match the cache" % (tuple(k_new.shape),))
+    if k_new.shape[0] != q.shape[0]:
+        raise ValueError("k_new batch %d differs from q batch %d" % (k_new.shape[0], q.shape[0]))
+    B, Hq, scale, out, workspace, mb, stride = _decode_args(cache, q, seq_lens, max_seq_len, block_table, key_mask,
+                                                            scale, out, workspace, part_tokens)
+    check(lib().kvattn_attn_decode_append(ctypes.byref(cache.desc()), B, Hq, _ptr(q), _CODE.get(q.dtype, -1),
+                                          _ptr(k_new), _ptr(v_new), _CODE[k_new.dtype], _ptr(seq_lens),
+                                          int(max_seq_len), _ptr(block_table), mb, _ptr(key_mask), stride, scale,
+                                          _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          int(part_tokens), _stream(q.device)))
     return out
 
 

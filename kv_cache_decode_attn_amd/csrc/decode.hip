@@ -145,6 +145,52 @@ __host__ __device__ constexpr int decode_off_floats(int T) { return 2 * (T / kBl
 __host__ __device__ constexpr int decode_lds_floats(int T, int G, int D) {
   return decode_off_floats(T) + ((T * G > kWaves * G * D) ? T * G : kWaves * G * D) + 2 * G;
 }
+// Fused append: the workgroup that attends key tn = seq_lens[b] - 1 (the
+// last key of the sequence, in its last partition) first stores the new
+// token's K and V rows of KV head g into that slot, encoded as kv_append
+// encodes them (a copy for an fp32 or bf16 cache, E4M3(x / scale) for an fp8
+// cache), then reads the cache as usual: the barrier that follows makes the
+// stores visible to every wave of the workgroup (a workgroup-scope release
+// and acquire on global memory).  No other workgroup of the launch reads
+// the slot, so the step needs no separate write pass.
+template <int KVT, int D>
+__device__ void store_new_rows(const DecodeLaunch& p, int b, int g, int tn) {
+  constexpr int ES = (KVT == KVATTN_F32) ? 4 : (KVT == KVATTN_BF16) ? 2 : 1;
+  constexpr int EPW = 4 / ES;     // elements per 32-bit word
+  constexpr int W = D * ES / 4;   // words per row
+  const int64_t off = position_offset(p.c, b, g, tn);
+  if (off < 0) return;  // outside the cache: nothing is stored (and the key is masked)
+  for (int i = threadIdx.x; i < 2 * W; i += blockDim.x) {
+    const int kv = i / W, w = i - kv * W;
+    const int64_t src = ((int64_t)b * p.num_kv_heads + g) * D + (int64_t)w * EPW;
+    const uint8_t* in = kv ? p.v_new : p.k_new;
+    uint32_t word;
+    if constexpr (KVT == KVATTN_F32) {
+      word = reinterpret_cast<const uint32_t*>(in)[src];
+    } else if constexpr (KVT == KVATTN_BF16) {
+      word = *reinterpret_cast<const uint32_t*>(in + src * 2);
+    } else {
+      const float s = (kv ? p.v_scale : p.k_scale)[g];
+      float x[4];
+      if (p.in_dtype == KVATTN_F32) {
+        const U4 r = *reinterpret_cast<const U4*>(in + src * 4);
+        x[0] = __uint_as_float(r.x);
+        x[1] = __uint_as_float(r.y);
+        x[2] = __uint_as_float(r.z);
+        x[3] = __uint_as_float(r.w);
+      } else {
+        const U2 r = *reinterpret_cast<const U2*>(in + src * 2);
+        x[0] = bf16_lo(r.x);
+        x[1] = bf16_hi(r.x);
+        x[2] = bf16_lo(r.y);
+        x[3] = bf16_hi(r.y);
+      }
+      word = f32_to_e4m3(x[0] / s) | (f32_to_e4m3(x[1] / s) << 8) | (f32_to_e4m3(x[2] / s) << 16) |
+             (f32_to_e4m3(x[3] / s) << 24);
+    }
+    *reinterpret_cast<uint32_t*>((kv ? p.c.v : p.c.k) + off + 4 * w) = word;
+  }
+}
 
 // K and V bytes are read exactly once per call: load them non-temporally so
 // the stream does not displace reusable lines (q, block table, partials)
@@ -209,6 +255,9 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   float* s_lds = lds + decode_off_floats(T);              // [T][G] scores -> weights
   float* stat = lds + decode_lds_floats(T, G, D) - 2 * G;  // [G][2] (max, sum)
   for (int i = tid; i < nblk; i += 256) offs[i] = block_offset(p.c, b, g, j0 + i);
+  // fused append: the partition that ends the sequence stores the new key
+  const bool app = p.k_new != nullptr && t1 == ctx && p.seq_lens[b] == ctx;
+  if (app) store_new_rows<KVT, D>(p, b, g, ctx - 1);
 
   QFrag<KVT, G> q;
   q.load(p.q, (int64_t)b * p.num_q_heads + hq0, D, col);
@@ -217,7 +266,7 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   const uint8_t* mask_row = MASK ? p.key_mask + (int64_t)b * p.key_mask_stride : nullptr;
   const uint8_t* kbase = p.c.k + row * ROWB + col * (int)sizeof(Raw);
   const uint8_t* vbase = p.c.v + row * ROWB + col * (int)sizeof(Raw);
-  __syncthreads();
+  __syncthreads();  // also publishes the fused append's stores to every wave
 
   // ---- phase 1: scores of every key of the partition ----
   // Wave w handles blocks w, w + 4, ...; the next block's loads are issued
@@ -416,6 +465,9 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
   int64_t* offs = reinterpret_cast<int64_t*>(lds);
   float* red = lds + decode_off_floats(T);  // [kWaves][G][D] outputs, then [kWaves][G][2]
   for (int i = tid; i < nblk; i += 256) offs[i] = block_offset(p.c, b, g, j0 + i);
+  // fused append (as in decode_partition)
+  const bool app = p.k_new != nullptr && t1 == ctx && p.seq_lens[b] == ctx;
+  if (app) store_new_rows<KVATTN_FP8_E4M3, D>(p, b, g, ctx - 1);
 
   // q of head r16 as bf16 pairs: step s uses d GD*lg + 4s + 0..3
   uint32_t qb[KS][2];
@@ -434,7 +486,7 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
   }
   const float zscale = p.scale * kLog2e * p.k_scale[g];
   const uint8_t* mask_row = MASK ? p.key_mask + (int64_t)b * p.key_mask_stride : nullptr;
-  __syncthreads();
+  __syncthreads();  // also publishes the fused append's stores to every wave
 
   v4f o[NT];
 #pragma unroll

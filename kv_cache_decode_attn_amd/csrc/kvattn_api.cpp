@@ -121,6 +121,97 @@ int32_t default_part_tokens(int32_t dtype, int32_t batch, int32_t hq, int32_t hk
   return t;
 }
 
+// Shared body of kvattn_attn_decode and kvattn_attn_decode_append (k_new
+// NULL for the former).
+int attn_decode_impl(const char* who, const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, const void* q,
+                     int32_t q_dtype, const void* k_new, const void* v_new, int32_t in_dtype,
+                     const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table, int32_t max_blocks,
+                     const uint8_t* key_mask, int64_t key_mask_stride, float scale, float* out, void* workspace,
+                     size_t workspace_bytes, int32_t part_tokens, void* stream) {
+  if (batch < 0 || batch > 65535) return fail(KVATTN_EINVAL, "%s: batch %d out of range", who, batch);
+  kvattn::CacheView view;
+  int64_t cap = 0;
+  int rc = make_view(who, cache, batch, block_table, max_blocks, &view, &cap);
+  if (rc) return rc;
+  if (!group_ok(num_q_heads, cache->num_kv_heads))
+    return fail(KVATTN_EUNSUPPORTED, "%s: %d query heads over %d KV heads: group must be 1, 2, 4 or 8", who,
+                num_q_heads, cache->num_kv_heads);
+  const int32_t want_q = (cache->dtype == KVATTN_F32) ? KVATTN_F32 : KVATTN_BF16;
+  if (q_dtype != want_q)
+    return fail(KVATTN_EUNSUPPORTED, "%s: q dtype %d; this cache needs %s queries", who, q_dtype,
+                want_q == KVATTN_F32 ? "f32" : "bf16");
+  if (max_seq_len < 0) return fail(KVATTN_EINVAL, "%s: max_seq_len < 0", who);
+  const bool append = k_new || v_new || in_dtype >= 0;
+  if (append) {
+    if (in_dtype != KVATTN_F32 && in_dtype != KVATTN_BF16)
+      return fail(KVATTN_EINVAL, "%s: input dtype must be f32 or bf16", who);
+    if (in_dtype != cache->dtype && cache->dtype != KVATTN_FP8_E4M3)
+      return fail(KVATTN_EUNSUPPORTED, "%s: input dtype %d does not match cache dtype %d", who, in_dtype,
+                  cache->dtype);
+  }
+  if (batch == 0) return ok();
+  if (append) {
+    if (!k_new || !v_new) return fail(KVATTN_EINVAL, "%s: k_new and v_new are required", who);
+    if (!aligned16(k_new) || !aligned16(v_new))
+      return fail(KVATTN_EINVAL, "%s: k_new/v_new not 16-byte aligned", who);
+  }
+  if (!q || !seq_lens || !out) return fail(KVATTN_EINVAL, "%s: q, seq_lens and out are required", who);
+  if (!aligned16(q) || !aligned16(out)) return fail(KVATTN_EINVAL, "%s: q/out not 16-byte aligned", who);
+  if (key_mask && key_mask_stride < max_seq_len)
+    return fail(KVATTN_EINVAL, "%s: key_mask_stride %lld < max_seq_len %d", who, (long long)key_mask_stride,
+                max_seq_len);
+  const int32_t group = num_q_heads / cache->num_kv_heads;
+  int32_t t = part_tokens;
+  if (t == 0) t = default_part_tokens(cache->dtype, batch, num_q_heads, cache->num_kv_heads, max_seq_len);
+  // the fp8 matrix-core pass (group >= 4) keeps no per-key scores in LDS
+  const bool scores_in_lds = !fp8_mfma_pass(cache->dtype, group);
+  if (t < 64 || t > kMaxPartTokens || t % 64 != 0 || (scores_in_lds && t * group > kMaxPartScores))
+    return fail(KVATTN_EINVAL, "%s: part_tokens %d: need a multiple of 64 in [64, %d] with part_tokens*group <= %d",
+                who, t, kMaxPartTokens, kMaxPartScores);
+  const int64_t parts = ((int64_t)max_seq_len + t - 1) / t;
+  if (parts > 65535) return fail(KVATTN_EINVAL, "%s: too many partitions (%lld)", who, (long long)parts);
+  float* ws_o = nullptr;
+  float* ws_ml = nullptr;
+  if (parts > 1) {
+    const size_t need = kvattn_decode_workspace_bytes(cache->dtype, batch, num_q_heads, cache->num_kv_heads,
+                                                      cache->head_dim, max_seq_len, t);
+    if (!workspace || workspace_bytes < need)
+      return fail(KVATTN_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", who, workspace ? workspace_bytes : 0,
+                  need);
+    if (!aligned16(workspace)) return fail(KVATTN_EINVAL, "%s: workspace not 16-byte aligned", who);
+    ws_o = static_cast<float*>(workspace);
+    ws_ml = ws_o + (size_t)batch * num_q_heads * parts * cache->head_dim;
+  }
+  kvattn::DecodeLaunch a{};
+  a.c = view;
+  a.cache_dtype = cache->dtype;
+  a.head_dim = cache->head_dim;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.q = static_cast<const uint8_t*>(q);
+  a.seq_lens = seq_lens;
+  a.ctx_limit = (int32_t)(cap < max_seq_len ? cap : max_seq_len);
+  a.key_mask = key_mask;
+  a.key_mask_stride = key_mask_stride;
+  a.scale = scale;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.out = out;
+  a.ws_o = ws_o;
+  a.ws_ml = ws_ml;
+  a.part_tokens = t;
+  a.num_parts = (int32_t)(parts < 1 ? 1 : parts);
+  if (append) {
+    a.k_new = static_cast<const uint8_t*>(k_new);
+    a.v_new = static_cast<const uint8_t*>(v_new);
+    a.in_dtype = in_dtype;
+  }
+  rc = kvattn::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,71 +300,22 @@ int kvattn_attn_decode(const kvattn_cache* cache, int32_t batch, int32_t num_q_h
                        int32_t q_dtype, const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
                        int32_t max_blocks, const uint8_t* key_mask, int64_t key_mask_stride, float scale,
                        float* out, void* workspace, size_t workspace_bytes, int32_t part_tokens, void* stream) {
-  const char* who = "kvattn_attn_decode";
-  if (batch < 0 || batch > 65535) return fail(KVATTN_EINVAL, "%s: batch %d out of range", who, batch);
-  kvattn::CacheView view;
-  int64_t cap = 0;
-  int rc = make_view(who, cache, batch, block_table, max_blocks, &view, &cap);
-  if (rc) return rc;
-  if (!group_ok(num_q_heads, cache->num_kv_heads))
-    return fail(KVATTN_EUNSUPPORTED, "%s: %d query heads over %d KV heads: group must be 1, 2, 4 or 8", who,
-                num_q_heads, cache->num_kv_heads);
-  const int32_t want_q = (cache->dtype == KVATTN_F32) ? KVATTN_F32 : KVATTN_BF16;
-  if (q_dtype != want_q)
-    return fail(KVATTN_EUNSUPPORTED, "%s: q dtype %d; this cache needs %s queries", who, q_dtype,
-                want_q == KVATTN_F32 ? "f32" : "bf16");
-  if (max_seq_len < 0) return fail(KVATTN_EINVAL, "%s: max_seq_len < 0", who);
-  if (batch == 0) return ok();
-  if (!q || !seq_lens || !out) return fail(KVATTN_EINVAL, "%s: q, seq_lens and out are required", who);
-  if (!aligned16(q) || !aligned16(out)) return fail(KVATTN_EINVAL, "%s: q/out not 16-byte aligned", who);
-  if (key_mask && key_mask_stride < max_seq_len)
-    return fail(KVATTN_EINVAL, "%s: key_mask_stride %lld < max_seq_len %d", who, (long long)key_mask_stride,
-                max_seq_len);
-  const int32_t group = num_q_heads / cache->num_kv_heads;
-  int32_t t = part_tokens;
-  if (t == 0) t = default_part_tokens(cache->dtype, batch, num_q_heads, cache->num_kv_heads, max_seq_len);
-  // the fp8 matrix-core pass (group >= 4) keeps no per-key scores in LDS
-  const bool scores_in_lds = !fp8_mfma_pass(cache->dtype, group);
-  if (t < 64 || t > kMaxPartTokens || t % 64 != 0 || (scores_in_lds && t * group > kMaxPartScores))
-    return fail(KVATTN_EINVAL, "%s: part_tokens %d: need a multiple of 64 in [64, %d] with part_tokens*group <= %d",
-                who, t, kMaxPartTokens, kMaxPartScores);
-  const int64_t parts = ((int64_t)max_seq_len + t - 1) / t;
-  if (parts > 65535) return fail(KVATTN_EINVAL, "%s: too many partitions (%lld)", who, (long long)parts);
-  float* ws_o = nullptr;
-  float* ws_ml = nullptr;
-  if (parts > 1) {
-    const size_t need = kvattn_decode_workspace_bytes(cache->dtype, batch, num_q_heads, cache->num_kv_heads,
-                                                      cache->head_dim, max_seq_len, t);
-    if (!workspace || workspace_bytes < need)
-      return fail(KVATTN_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", who, workspace ? workspace_bytes : 0,
-                  need);
-    if (!aligned16(workspace)) return fail(KVATTN_EINVAL, "%s: workspace not 16-byte aligned", who);
-    ws_o = static_cast<float*>(workspace);
-    ws_ml = ws_o + (size_t)batch * num_q_heads * parts * cache->head_dim;
-  }
-  kvattn::DecodeLaunch a{};
-  a.c = view;
-  a.cache_dtype = cache->dtype;
-  a.head_dim = cache->head_dim;
-  a.batch = batch;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.q = static_cast<const uint8_t*>(q);
-  a.seq_lens = seq_lens;
-  a.ctx_limit = (int32_t)(cap < max_seq_len ? cap : max_seq_len);
-  a.key_mask = key_mask;
-  a.key_mask_stride = key_mask_stride;
-  a.scale = scale;
-  a.k_scale = cache->k_scale;
-  a.v_scale = cache->v_scale;
-  a.out = out;
-  a.ws_o = ws_o;
-  a.ws_ml = ws_ml;
-  a.part_tokens = t;
-  a.num_parts = (int32_t)(parts < 1 ? 1 : parts);
-  rc = kvattn::launch_decode(a, static_cast<hipStream_t>(stream));
-  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
-  return ok();
+  return attn_decode_impl("kvattn_attn_decode", cache, batch, num_q_heads, q, q_dtype, nullptr, nullptr, -1,
+                          seq_lens, max_seq_len, block_table, max_blocks, key_mask, key_mask_stride, scale, out,
+                          workspace, workspace_bytes, part_tokens, stream);
+}
+
+int kvattn_attn_decode_append(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, const void* q,
+                              int32_t q_dtype, const void* k_new, const void* v_new, int32_t in_dtype,
+                              const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                              int32_t max_blocks, const uint8_t* key_mask, int64_t key_mask_stride, float scale,
+                              float* out, void* workspace, size_t workspace_bytes, int32_t part_tokens,
+                              void* stream) {
+  if (in_dtype < 0)
+    return fail(KVATTN_EINVAL, "kvattn_attn_decode_append: input dtype must be f32 or bf16");
+  return attn_decode_impl("kvattn_attn_decode_append", cache, batch, num_q_heads, q, q_dtype, k_new, v_new,
+                          in_dtype, seq_lens, max_seq_len, block_table, max_blocks, key_mask, key_mask_stride, scale,
+                          out, workspace, workspace_bytes, part_tokens, stream);
 }
 
 int kvattn_attn_prefill(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -143,3 +143,22 @@ def test_prefill_host_errors():
     assert call(q=FAKE + 2) == _lib.EINVAL
     assert call(cache=_cache(hkv=4)) == _lib.EINVAL  # shape mismatch
     assert call(n=0) == _lib.OK
+
+
+def test_decode_append_host_errors():
+    L = _lib.lib()
+
+    def call(c=None, k_new=FAKE, v_new=FAKE, in_dtype=_lib.BF16, batch=4, ws=None, wsb=0):
+        c = c if c is not None else _cache()
+        return L.kvattn_attn_decode_append(ctypes.byref(c), batch, 32, FAKE, _lib.BF16, k_new, v_new, in_dtype, FAKE,
+                                           100, FAKE, 64, None, 0, 0.1, FAKE, ws, wsb, 512, None)
+
+    assert call(in_dtype=_lib.F32) == _lib.EUNSUPPORTED    # f32 rows into a bf16 cache
+    assert call(in_dtype=_lib.FP8_E4M3) == _lib.EINVAL     # rows must be f32 or bf16
+    assert call(in_dtype=-1) == _lib.EINVAL
+    assert call(k_new=None) == _lib.EINVAL
+    assert call(v_new=FAKE + 4) == _lib.EINVAL             # misaligned
+    assert call(c=_cache(head_dim=96)) == _lib.EUNSUPPORTED
+    assert call(batch=0) == _lib.OK                        # nothing to do, nothing launched
+    assert call(batch=0, k_new=None) == _lib.OK
+    assert _lib.lib().kvattn_last_error().decode() == ""
