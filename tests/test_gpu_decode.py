@@ -273,3 +273,69 @@ def test_fp8_gqa_key_mask_nan_codes_and_edge_lengths(G, d):
         got = c.run(part).cpu().numpy()
         assert np.isfinite(got).all()
         assert max_abs(got, c.oracle(quantised=True)) <= TOL
+
+
+def test_workspace_contents_on_entry_do_not_matter():
+    """Workspace contents on entry are ignored: a workspace full of garbage
+    (or of another call's partials) gives the same bits."""
+    c = Case(3, 16, 4, 128, [900, 77, 1500], seed=50)
+    lens = torch.from_numpy(c.lens).to(DEV)
+    q = c.q.to(DEV)
+    ws = K.decode_workspace(c.cache, 3, 16, c.maxlen, 64)
+    ws.zero_()
+    first = K.attn_decode(c.cache, q, lens, c.maxlen, block_table=c.table, workspace=ws, part_tokens=64).cpu()
+    assert max_abs(first.numpy(), c.oracle()) <= TOL
+    g = torch.Generator().manual_seed(7)
+    for fill in ("random", "ones", "reuse"):
+        if fill == "random":
+            ws.copy_(torch.randint(-2 ** 31, 2 ** 31 - 1, ws.shape, generator=g, dtype=torch.int32).view(torch.float32))
+        elif fill == "ones":
+            ws.view(torch.int32).fill_(-1)
+        again = K.attn_decode(c.cache, q, lens, c.maxlen, block_table=c.table, workspace=ws, part_tokens=64).cpu()
+        assert torch.equal(again, first), fill
+
+
+def test_merge_of_many_partitions():
+    """938 partitions of one sequence (G = 8): the merge's long partition
+    loop; same tolerance as ever, and a 59-partition split agrees."""
+    c = Case(1, 8, 1, 64, [60001], seed=51)
+    got = c.run(64).cpu().numpy()   # 938 partitions x 8 heads
+    assert max_abs(got, c.oracle()) <= TOL
+    ref = c.run(1024).cpu().numpy()  # 59 partitions: staged
+    assert max_abs(got, ref) <= 1e-5
+
+
+def test_graph_replay_matches_eager():
+    """The decode and the fused decode step captured in a HIP graph: every
+    replay (with eager work in between) equals the eager call bit for bit."""
+    from tests.test_gpu_decode_append import StepCase
+    c = StepCase(4, 32, 8, 128, [1000, 33, 700, 2048], seed=52)
+    lens = torch.from_numpy(c.lens).to(DEV)
+    q = c.q.to(DEV)
+    k1, v1 = c.k1.to(DEV), c.v1.to(DEV)
+    out = torch.empty((4, 32, 128), dtype=torch.float32, device=DEV)
+    ws = K.decode_workspace(c.cache, 4, 32, c.maxlen, 64)  # also fits the part-128 calls
+    eager_cache = c.clone_cache()
+    want = K.attn_decode_append(eager_cache, q, k1, v1, lens, c.maxlen, block_table=c.table, workspace=ws,
+                                part_tokens=128).clone()
+    graph_cache = c.clone_cache()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        K.attn_decode_append(graph_cache, q, k1, v1, lens, c.maxlen, block_table=c.table, out=out, workspace=ws,
+                             part_tokens=128)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        K.attn_decode_append(graph_cache, q, k1, v1, lens, c.maxlen, block_table=c.table, out=out, workspace=ws,
+                             part_tokens=128)
+    for r in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), r
+        # eager work on the same workspace between replays
+        K.attn_decode(eager_cache, q, lens, c.maxlen, block_table=c.table, workspace=ws, part_tokens=64)
+        torch.cuda.synchronize()
+    np.testing.assert_array_equal(storage(graph_cache.k), storage(eager_cache.k))
