@@ -192,6 +192,16 @@ __device__ void store_new_rows(const DecodeLaunch& p, int b, int g, int tn) {
   }
 }
 
+// Values the compiler cannot prove wave-uniform (LDS reads at one address,
+// the wave index) moved to scalar registers, so branches on them are scalar
+// and the load addresses are scalar base + lane offset.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // K and V bytes are read exactly once per call: load them non-temporally so
 // the stream does not displace reusable lines (q, block table, partials)
 // from the caches.
@@ -203,17 +213,6 @@ __device__ __forceinline__ Raw stream_load(const Raw* p) {
   } else {
     typedef unsigned v2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(Raw, __builtin_nontemporal_load(reinterpret_cast<const v2*>(p)));
-  }
-}
-
-template <typename Raw, int NI, int TPI, int ROWB>
-__device__ __forceinline__ void load_block(Raw* r, const uint8_t* base, int64_t off) {
-  if (off >= 0) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) r[i] = stream_load(reinterpret_cast<const Raw*>(base + off + i * TPI * ROWB));
-  } else {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) r[i] = Raw{};
   }
 }
 
@@ -232,7 +231,8 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   // KV head fastest in the grid: neighbouring workgroups read the heads of
   // the same 16-token blocks, which sit side by side in the paged pool.
   const int g = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
   const int col = lane % LPT, row = lane / LPT;
   const int T = p.part_tokens;
   const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
@@ -254,7 +254,12 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   int64_t* offs = reinterpret_cast<int64_t*>(lds);        // [T/16] block byte offsets (-1: outside)
   float* s_lds = lds + decode_off_floats(T);              // [T][G] scores -> weights
   float* stat = lds + decode_lds_floats(T, G, D) - 2 * G;  // [G][2] (max, sum)
+  uint8_t* mflag = reinterpret_cast<uint8_t*>(lds + decode_lds_floats(T, G, D));  // [T] mask (MASK only)
   for (int i = tid; i < nblk; i += 256) offs[i] = block_offset(p.c, b, g, j0 + i);
+  if constexpr (MASK) {
+    const uint8_t* mask_row = p.key_mask + (int64_t)b * p.key_mask_stride + t0;
+    for (int t = tid; t < n; t += 256) mflag[t] = mask_row[t];
+  }
   // fused append: the partition that ends the sequence stores the new key
   const bool app = p.k_new != nullptr && t1 == ctx && p.seq_lens[b] == ctx;
   if (app) store_new_rows<KVT, D>(p, b, g, ctx - 1);
@@ -263,23 +268,29 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   q.load(p.q, (int64_t)b * p.num_q_heads + hq0, D, col);
   float zscale = p.scale * kLog2e;
   if constexpr (KVT == KVATTN_FP8_E4M3) zscale *= p.k_scale[g];
-  const uint8_t* mask_row = MASK ? p.key_mask + (int64_t)b * p.key_mask_stride : nullptr;
   const uint8_t* kbase = p.c.k + row * ROWB + col * (int)sizeof(Raw);
   const uint8_t* vbase = p.c.v + row * ROWB + col * (int)sizeof(Raw);
   __syncthreads();  // also publishes the fused append's stores to every wave
 
+  // Byte offset to load block jb from: its own, or (outside the partition or
+  // the cache) offset 0, a valid address whose bytes are never used, so that
+  // every iteration issues the same loads and the prefetches stay in flight.
+  auto load_block = [&](int jb, const uint8_t* base, Raw* r) {
+    int64_t o = 0;
+    if (jb < nblk) o = offs[jb];
+    const int64_t off = uniform64(o >= 0 ? o : 0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) r[i] = stream_load(reinterpret_cast<const Raw*>(base + off + i * TPI * ROWB));
+  };
+
   // ---- phase 1: scores of every key of the partition ----
-  // Wave w handles blocks w, w + 4, ...; the next block's loads are issued
-  // before the current block is consumed, so two blocks are in flight.
-  Raw cur[NI], nxt[NI];
-  if (wave < nblk) load_block<Raw, NI, TPI, ROWB>(cur, kbase, offs[wave]);
-  for (int jb = wave; jb < nblk; jb += kWaves) {
-    const int64_t off = offs[jb];
-    if (jb + kWaves < nblk) load_block<Raw, NI, TPI, ROWB>(nxt, kbase, offs[jb + kWaves]);
-    const int j = j0 + jb;
+  // Wave w handles blocks w, w + 4, ...; two register sets alternate so the
+  // next block's loads are in flight while one is consumed.
+  auto scores = [&](int jb, const Raw* cur) {
+    const bool in_cache = uniform64(offs[jb]) >= 0;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int tok = j * kBlockTokens + i * TPI + row;
+      const int t = kBlockTokens * jb + i * TPI + row;  // partition-relative key
       float acc[G];
       if constexpr (KVT == KVATTN_BF16) {
 #pragma unroll
@@ -292,20 +303,31 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) acc[h] = group_sum<LPT>(acc[h]);
-      if (tok < t1) {
-        bool valid = off >= 0;
-        if constexpr (MASK) valid = valid && mask_row[tok] != 0;
+      if (t < n) {
+        bool valid = in_cache;
+        if constexpr (MASK) valid = valid && mflag[t] != 0;
         if (col == 0) {
 #pragma unroll
-          for (int h = 0; h < G; ++h) s_lds[(tok - t0) * G + h] = valid ? acc[h] * zscale : -INFINITY;
+          for (int h = 0; h < G; ++h) s_lds[t * G + h] = valid ? acc[h] * zscale : -INFINITY;
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) cur[i] = nxt[i];
+  };
+  {
+    Raw ka[NI], kb[NI];
+    load_block(wave, kbase, ka);
+    for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
+      load_block(jb + kWaves, kbase, kb);
+      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for ka
+      scores(jb, ka);
+      load_block(jb + 2 * kWaves, kbase, ka);
+      __builtin_amdgcn_sched_barrier(0);
+      if (jb + kWaves < nblk) scores(jb + kWaves, kb);
+    }
   }
   // The first V block is fetched while the softmax statistics are formed.
-  if (wave < nblk) load_block<Raw, NI, TPI, ROWB>(cur, vbase, offs[wave]);
+  Raw va[NI], vb[NI];
+  load_block(wave, vbase, va);
   __syncthreads();
 
   // ---- phase 2: per-head max and sum; scores -> weights exp2(z - max) ----
@@ -335,29 +357,27 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
 
-  for (int jb = wave; jb < nblk; jb += kWaves) {
-    const int64_t off = offs[jb];
-    if (jb + kWaves < nblk) load_block<Raw, NI, TPI, ROWB>(nxt, vbase, offs[jb + kWaves]);
-    const int j = j0 + jb;
+  auto accumulate = [&](int jb, const Raw* cur) {
     // A block wholly inside the partition with no key mask has only live
     // keys; otherwise a key with zero weight for every head is dropped so
     // that non-finite bytes in padding or stale slots cannot reach o.  A
     // block outside the cache was fully masked (all weights 0).
-    const bool full = !MASK && off >= 0 && (j + 1) * kBlockTokens <= t1;
+    if (uniform64(offs[jb]) < 0) return;
+    const bool full = !MASK && kBlockTokens * (jb + 1) <= n;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int tok = j * kBlockTokens + i * TPI + row;
+      const int t = kBlockTokens * jb + i * TPI + row;
       float w[G];
       bool live = true;
       if (full) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) w[h] = s_lds[(tok - t0) * G + h];
+        for (int h = 0; h < G; ++h) w[h] = s_lds[t * G + h];
       } else {
         live = false;
-        const bool in = tok < t1 && off >= 0;
+        const bool in = t < n;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          w[h] = in ? s_lds[(tok - t0) * G + h] : 0.f;
+          w[h] = in ? s_lds[t * G + h] : 0.f;
           live = live || (w[h] != 0.f);
         }
       }
@@ -372,8 +392,14 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(w[h], vf[e], o[h][e]);
     }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) cur[i] = nxt[i];
+  };
+  for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
+    load_block(jb + kWaves, vbase, vb);
+    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for va
+    accumulate(jb, va);
+    load_block(jb + 2 * kWaves, vbase, va);
+    __builtin_amdgcn_sched_barrier(0);
+    if (jb + kWaves < nblk) accumulate(jb + kWaves, vb);
   }
 
   // reduce over the TPI rows of the wave (lanes sharing col)
@@ -401,6 +427,275 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) acc += red[(w * G + h) * D + d];
     acc *= vscale;
+    const int hq = hq0 + h;
+    const float l = stat[2 * h + 1];
+    if (nparts_b == 1) {
+      p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = (l > 0.f) ? acc / l : 0.f;
+    } else {
+      const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.num_parts + part;
+      p.ws_o[slot * D + d] = acc;
+      if (d == 0) {
+        p.ws_ml[slot * 2] = stat[2 * h];
+        p.ws_ml[slot * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 cache with G >= 4 query heads per KV head: the partition pass with
+// both contractions on v_mfma_f32_16x16x16_bf16 and the same three phases.
+//   phase 1  S^T[key][h] = K Q^T per 16-token block.  A = K as loaded, no
+//            conversion: lane l holds key l%16, 16-byte chunks c at row
+//            bytes 64c + 16(l/16) (k-step 2c + u takes half u of chunk c);
+//            B = q of head l%16 in the same d order (zero for heads >= G).
+//            Lane l gets keys 4(l/16) + r of head l%16, stored head-major.
+//   phase 2  as in decode_partition: per head max, exp2 weights and sum.
+//   phase 3  O^T += V^T P^T.  A = V^T: lane l loads 8 bytes (d 4(l%16)..+3
+//            of a 64-wide half) of keys 4(l/16)..+3 and transposes the 4x4
+//            block of 16-bit values with v_perm_b32, so output tile (half,
+//            j) row l%16 holds d = 64*half + 4*(l%16) + j.  B = the lane's
+//            own 4 weights (keys 4(l/16) + r of head l%16, contiguous in
+//            LDS), split into bf16 hi + lo parts (two MFMAs) so P keeps
+//            about 16 bits.
+// Per 16-token block a wave issues 8 (D = 128) MFMAs for the scores and 16
+// for the output instead of the vector pass's per-element dot products,
+// lane reductions and multiply-adds.
+template <int D, int G, bool MASK>
+__global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLaunch p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  constexpr int ROWB = 2 * D;       // bytes per token row
+  constexpr int KC = ROWB / 64;     // 16-byte K chunks per lane and block
+  constexpr int KS = 2 * KC;        // k-steps of 4 bf16
+  constexpr int HALVES = D / 64;    // 64-wide d halves of the V^T tiles
+  constexpr int NT = 4 * HALVES;    // output tiles of 16 d rows
+  static_assert(G >= 1 && G <= 16 && KC >= 1, "shape");
+
+  extern __shared__ float lds[];
+  const int g = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int r16 = lane & 15, lg = lane >> 4;
+  const int T = p.part_tokens;
+  const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
+  const int hq0 = g * G;
+  const int t0 = part * T;
+  if (t0 >= ctx) {
+    if (part == 0)
+      for (int i = tid; i < G * D; i += 256) p.out[((int64_t)b * p.num_q_heads + hq0) * D + i] = 0.f;
+    return;
+  }
+  const int t1 = min(t0 + T, ctx);
+  const int n = t1 - t0;
+  const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
+  const int j0 = t0 / kBlockTokens;
+
+  int64_t* offs = reinterpret_cast<int64_t*>(lds);
+  float* s_lds = lds + decode_off_floats(T);               // [G][T] scores -> weights
+  float* stat = lds + decode_lds_floats(T, G, D) - 2 * G;  // [G][2] (max, sum)
+  uint8_t* mflag = reinterpret_cast<uint8_t*>(lds + decode_lds_floats(T, G, D));  // [T] mask (MASK only)
+  for (int i = tid; i < nblk; i += 256) offs[i] = block_offset(p.c, b, g, j0 + i);
+  if constexpr (MASK) {
+    const uint8_t* mask_row = p.key_mask + (int64_t)b * p.key_mask_stride + t0;
+    for (int t = tid; t < n; t += 256) mflag[t] = mask_row[t];
+  }
+  // fused append (as in decode_partition)
+  const bool app = p.k_new != nullptr && t1 == ctx && p.seq_lens[b] == ctx;
+  if (app) store_new_rows<KVATTN_BF16, D>(p, b, g, ctx - 1);
+
+  // q of head r16 in the k order of the K chunks: k-step s = 2c + u uses
+  // d 32c + 8*lg + 4u + 0..3 (zero for heads >= G)
+  uint32_t qb[KS][2];
+  {
+    const int hr = r16 < G ? r16 : 0;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)b * p.num_q_heads + hq0 + hr) * D;
+#pragma unroll
+    for (int sd = 0; sd < KS; ++sd) {
+      const uint2 w = *reinterpret_cast<const uint2*>(qrow + 32 * (sd / 2) + 8 * lg + 4 * (sd % 2));
+      qb[sd][0] = r16 < G ? w.x : 0u;
+      qb[sd][1] = r16 < G ? w.y : 0u;
+    }
+  }
+  const float zscale = p.scale * kLog2e;
+  __syncthreads();  // also publishes the fused append's stores to every wave
+
+  // Key t of the partition is attended (inside it and not masked).
+  auto key_ok = [&](int t) -> bool {
+    if (t >= n) return false;
+    if constexpr (MASK) return mflag[t] != 0;
+    return true;
+  };
+  // Byte offset to load block jb from: its own, or (outside the partition or
+  // the cache) offset 0, a valid address whose bytes are never used, so that
+  // every iteration issues the same loads and the prefetches stay in flight.
+  auto load_off = [&](int jb) -> int64_t {
+    int64_t o = 0;
+    if (jb < nblk) o = offs[jb];
+    return uniform64(o >= 0 ? o : 0);
+  };
+
+  // ---- phase 1: scores; blocks jb = wave + 4i, two in flight (ping-pong) ----
+  // K chunk c of lane (r16, lg): bytes 64c + 16*lg of key r16's row, so one
+  // load instruction reads 64 contiguous bytes of each of 16 rows (a 128-byte
+  // line is read by two instructions back to back, never in quarters).
+  const uint8_t* kbase = p.c.k + r16 * ROWB + 16 * lg;
+  auto load_k = [&](int jb, U4* kr) {
+    const int64_t off = load_off(jb);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kr[c] = stream_load(reinterpret_cast<const U4*>(kbase + off + 64 * c));
+  };
+  auto scores = [&](int jb, const U4* kr) {
+    const bool in_cache = uniform64(offs[jb]) >= 0;
+    v4f sacc = v4f{0.f, 0.f, 0.f, 0.f}, sacc2 = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const v4s a0 = __builtin_bit_cast(v4s, v2u{kr[c].x, kr[c].y});
+      const v4s a1 = __builtin_bit_cast(v4s, v2u{kr[c].z, kr[c].w});
+      const v4s b0 = __builtin_bit_cast(v4s, v2u{qb[2 * c][0], qb[2 * c][1]});
+      const v4s b1 = __builtin_bit_cast(v4s, v2u{qb[2 * c + 1][0], qb[2 * c + 1][1]});
+      sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, b0, sacc, 0, 0, 0);
+      sacc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, b1, sacc2, 0, 0, 0);
+    }
+    sacc += sacc2;
+    if (r16 < G) {
+      const int tk = kBlockTokens * jb + 4 * lg;  // partition-relative key of r = 0
+      float4 z;
+      z.x = (in_cache && key_ok(tk + 0)) ? sacc[0] * zscale : -INFINITY;
+      z.y = (in_cache && key_ok(tk + 1)) ? sacc[1] * zscale : -INFINITY;
+      z.z = (in_cache && key_ok(tk + 2)) ? sacc[2] * zscale : -INFINITY;
+      z.w = (in_cache && key_ok(tk + 3)) ? sacc[3] * zscale : -INFINITY;
+      *reinterpret_cast<float4*>(s_lds + r16 * T + tk) = z;
+    }
+  };
+  {
+    U4 ka[KC], kb[KC];
+    load_k(wave, ka);
+    for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
+      load_k(jb + kWaves, kb);
+      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for ka
+      scores(jb, ka);
+      load_k(jb + 2 * kWaves, ka);
+      __builtin_amdgcn_sched_barrier(0);
+      if (jb + kWaves < nblk) scores(jb + kWaves, kb);
+    }
+  }
+  // V: 8 bytes (d 64*hf + 4*r16 ..+3) of each of keys 4*lg + i
+  const uint8_t* vbase = p.c.v + (4 * lg) * ROWB + 8 * r16;
+  auto load_v = [&](int jb, uint2 (*vr)[4]) {
+    const int64_t off = load_off(jb);
+#pragma unroll
+    for (int hf = 0; hf < HALVES; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vr[hf][i] = __builtin_bit_cast(
+            uint2, __builtin_nontemporal_load(reinterpret_cast<const v2u*>(vbase + off + i * ROWB + 128 * hf)));
+  };
+  // The first V block is fetched while the softmax statistics are formed.
+  uint2 va[HALVES][4], vb[HALVES][4];
+  load_v(wave, va);
+  __syncthreads();
+
+  // ---- phase 2: per-head max and sum; scores -> weights exp2(z - max) ----
+  for (int h = wave; h < G; h += kWaves) {
+    float* sh = s_lds + h * T;
+    float m = -INFINITY;
+    for (int t = lane; t < n; t += kWave) m = fmaxf(m, sh[t]);
+    m = group_max<64>(m);
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    float l = 0.f;
+    for (int t = lane; t < n; t += kWave) {
+      const float e = exp2f(sh[t] - mref);
+      sh[t] = e;
+      l += e;
+    }
+    l = group_sum<64>(l);
+    if (lane == 0) {
+      stat[2 * h] = m;
+      stat[2 * h + 1] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: O^T += V^T P^T ----
+  v4f o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto accumulate = [&](int jb, const uint2 (*vr)[4]) {
+    if (uniform64(offs[jb]) < 0) return;  // block outside the cache: every weight is 0
+    const int tk = kBlockTokens * jb + 4 * lg;
+    bool live[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) live[r] = key_ok(tk + r);
+    float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r16 < G) w = *reinterpret_cast<const float4*>(s_lds + r16 * T + tk);
+    const float pw[4] = {live[0] ? w.x : 0.f, live[1] ? w.y : 0.f, live[2] ? w.z : 0.f, live[3] ? w.w : 0.f};
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 h01, h23, l01, l23;
+    h01[0] = (__bf16)pw[0];
+    h01[1] = (__bf16)pw[1];
+    h23[0] = (__bf16)pw[2];
+    h23[1] = (__bf16)pw[3];
+    l01[0] = (__bf16)(pw[0] - (float)h01[0]);
+    l01[1] = (__bf16)(pw[1] - (float)h01[1]);
+    l23[0] = (__bf16)(pw[2] - (float)h23[0]);
+    l23[1] = (__bf16)(pw[3] - (float)h23[1]);
+    const v4s phi = __builtin_bit_cast(v4s, v2u{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
+    const v4s plo = __builtin_bit_cast(v4s, v2u{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+#pragma unroll
+    for (int hf = 0; hf < HALVES; ++hf) {
+      uint2 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = live[i] ? vr[hf][i] : uint2{0u, 0u};  // dead keys never reach O
+      // 4 keys x 4 d (16-bit) -> per d j the 4 keys' values
+      const uint32_t x01l = __builtin_amdgcn_perm(a[1].x, a[0].x, 0x05040100u);
+      const uint32_t x23l = __builtin_amdgcn_perm(a[3].x, a[2].x, 0x05040100u);
+      const uint32_t x01h = __builtin_amdgcn_perm(a[1].x, a[0].x, 0x07060302u);
+      const uint32_t x23h = __builtin_amdgcn_perm(a[3].x, a[2].x, 0x07060302u);
+      const uint32_t y01l = __builtin_amdgcn_perm(a[1].y, a[0].y, 0x05040100u);
+      const uint32_t y23l = __builtin_amdgcn_perm(a[3].y, a[2].y, 0x05040100u);
+      const uint32_t y01h = __builtin_amdgcn_perm(a[1].y, a[0].y, 0x07060302u);
+      const uint32_t y23h = __builtin_amdgcn_perm(a[3].y, a[2].y, 0x07060302u);
+      const v4s av[4] = {__builtin_bit_cast(v4s, v2u{x01l, x23l}), __builtin_bit_cast(v4s, v2u{x01h, x23h}),
+                         __builtin_bit_cast(v4s, v2u{y01l, y23l}), __builtin_bit_cast(v4s, v2u{y01h, y23h})};
+      // hi parts of the four tiles, then the lo parts: no back-to-back
+      // MFMAs on one accumulator
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], phi, o[4 * hf + j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], plo, o[4 * hf + j], 0, 0, 0);
+    }
+  };
+  for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
+    load_v(jb + kWaves, vb);
+    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for va
+    accumulate(jb, va);
+    load_v(jb + 2 * kWaves, va);
+    __builtin_amdgcn_sched_barrier(0);
+    if (jb + kWaves < nblk) accumulate(jb + kWaves, vb);
+  }
+
+  __syncthreads();  // every wave is done reading weights; reuse LDS
+  float* red = s_lds;  // [kWaves][G][D]
+  if (r16 < G) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int hf = t / 4, j = t % 4;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) red[(wave * G + r16) * D + 64 * hf + 4 * (4 * lg + rr) + j] = o[t][rr];
+    }
+  }
+  __syncthreads();
+
+  const int nparts_b = (ctx + T - 1) / T;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx - h * D;
+    float acc = red[(0 * G + h) * D + d];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) acc += red[(w * G + h) * D + d];
     const int hq = hq0 + h;
     const float l = stat[2 * h + 1];
     if (nparts_b == 1) {
@@ -770,8 +1065,11 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
   if constexpr (KVT == KVATTN_FP8_E4M3 && G >= 4) {
     const size_t lds = (size_t)(decode_off_floats(a.part_tokens) + kWaves * G * D + kWaves * G * 2) * sizeof(float);
     hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
+  } else if constexpr (KVT == KVATTN_BF16 && G >= 4) {
+    const size_t lds = (size_t)(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
+    hipLaunchKernelGGL((decode_partition_bf16_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
   } else {
-    const size_t lds = (size_t)decode_lds_floats(a.part_tokens, G, D) * sizeof(float);
+    const size_t lds = (size_t)(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
     hipLaunchKernelGGL((decode_partition<KVT, D, G, MASK>), grid, dim3(256), lds, s, a);
   }
   if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
