@@ -717,15 +717,18 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
 // With 8 heads per KV head an fp8 byte costs 8 multiply-adds on each of K and
 // V, more than the vector ALUs can issue at HBM speed, so both contractions
 // of a 16-token block go to v_mfma_f32_16x16x16_bf16 (fp8 -> bf16 is exact):
-//   S^T[key][h] = K Q^T   A = K rows (lane l: key l%16, d (D/4)g + 4s + i
-//                         with g = l/16, step s), B = q of head l%16 (bf16, zero
-//                         for heads >= G).  The accumulator gives lane l keys
-//                         4g + r of head l%16.
-//   O^T += V^T P^T        B = the lane's own 4 weights (keys 4g + r), so no
-//                         data moves between lanes; A = V^T: lane l loads
-//                         4 bytes (d 4*(l%16) + 0..3) of each of keys 4g..4g+3
-//                         and byte-transposes them with v_perm_b32, so output
-//                         tile (half, j) row r16 holds d = 64*half + 4*r16 + j.
+//   S^T[key][h] = K Q^T   A = K rows: lane l holds key l%16, 16-byte chunks
+//                         c at row bytes 64c + 16(l/16) (one load reads 64
+//                         contiguous bytes of 16 rows); k-step 4c + u takes
+//                         word u of chunk c.  B = q of head l%16 in the same
+//                         d order (zero for heads >= G).  The accumulator
+//                         gives lane l keys 4(l/16) + r of head l%16.
+//   O^T += V^T P^T        B = the lane's own 4 weights (keys 4(l/16) + r), so
+//                         no data moves between lanes; A = V^T: lane l loads
+//                         bytes D/16 * (l%16) .. + D/16 of keys 4(l/16)..+3
+//                         (16 lanes read a whole row) and byte-transposes
+//                         them with v_perm_b32, so output tile t row l%16
+//                         holds d = D/16 * (l%16) + t.
 // The weights are split into bf16 hi + lo parts (two MFMAs), so P keeps about
 // 16 bits.  Each wave keeps its own running (max, sum, O) over its blocks with
 // a lazily raised maximum; the four waves are combined through LDS.
@@ -733,16 +736,20 @@ template <int D, int G, bool MASK>
 __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLaunch p) {
   typedef short v4s __attribute__((ext_vector_type(4)));
   typedef float v4f __attribute__((ext_vector_type(4)));
-  constexpr int KS = D / 16;        // QK steps; lane group g covers d [(D/4)g, (D/4)(g+1))
-  constexpr int GD = D / 4;         // d per lane group
-  constexpr int HALVES = D / 64;    // 64-wide d halves of the V^T tiles
-  constexpr int NT = 4 * HALVES;    // output tiles of 16 d rows
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  constexpr int KC = D / 64;        // 16-byte K chunks per lane and block
+  constexpr int KS = 4 * KC;        // k-steps of 4 codes
+  constexpr int VW = D / 64;        // 4-byte V words per lane and key
+  constexpr int VB = 4 * VW;        // V bytes per lane and key
+  constexpr int NT = VB;            // output tiles of 16 d rows
   constexpr float kRescale = 8.f;
-  static_assert(G >= 4 && G <= 16, "group");
+  static_assert(G >= 4 && G <= 16 && KC >= 1, "shape");
+  typedef uint32_t VRow[VW];
 
   extern __shared__ float lds[];
   const int g = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
   const int r16 = lane & 15, lg = lane >> 4;
   const int T = p.part_tokens;
   const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
@@ -754,33 +761,36 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     return;
   }
   const int t1 = min(t0 + T, ctx);
-  const int nblk = (t1 - t0 + kBlockTokens - 1) / kBlockTokens;
+  const int n = t1 - t0;
+  const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
   const int j0 = t0 / kBlockTokens;
 
   int64_t* offs = reinterpret_cast<int64_t*>(lds);
   float* red = lds + decode_off_floats(T);  // [kWaves][G][D] outputs, then [kWaves][G][2]
+  float* wstat = red + kWaves * G * D;
+  uint8_t* mflag = reinterpret_cast<uint8_t*>(wstat + kWaves * G * 2);  // [T] mask (MASK only)
   for (int i = tid; i < nblk; i += 256) offs[i] = block_offset(p.c, b, g, j0 + i);
+  if constexpr (MASK) {
+    const uint8_t* mask_row = p.key_mask + (int64_t)b * p.key_mask_stride + t0;
+    for (int t = tid; t < n; t += 256) mflag[t] = mask_row[t];
+  }
   // fused append (as in decode_partition)
   const bool app = p.k_new != nullptr && t1 == ctx && p.seq_lens[b] == ctx;
   if (app) store_new_rows<KVATTN_FP8_E4M3, D>(p, b, g, ctx - 1);
 
-  // q of head r16 as bf16 pairs: step s uses d GD*lg + 4s + 0..3
+  // q of head r16 as bf16 pairs: k-step s uses d 64(s/4) + 16*lg + 4(s%4) + 0..3
   uint32_t qb[KS][2];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)b * p.num_q_heads + hq0 + r16) * D;
+    const int hr = r16 < G ? r16 : 0;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)b * p.num_q_heads + hq0 + hr) * D;
 #pragma unroll
     for (int sd = 0; sd < KS; ++sd) {
-      if (r16 < G) {
-        const uint2 w = *reinterpret_cast<const uint2*>(qrow + GD * lg + 4 * sd);
-        qb[sd][0] = w.x;
-        qb[sd][1] = w.y;
-      } else {
-        qb[sd][0] = qb[sd][1] = 0u;
-      }
+      const uint2 w = *reinterpret_cast<const uint2*>(qrow + 64 * (sd / 4) + 16 * lg + 4 * (sd % 4));
+      qb[sd][0] = r16 < G ? w.x : 0u;
+      qb[sd][1] = r16 < G ? w.y : 0u;
     }
   }
   const float zscale = p.scale * kLog2e * p.k_scale[g];
-  const uint8_t* mask_row = MASK ? p.key_mask + (int64_t)b * p.key_mask_stride : nullptr;
   __syncthreads();  // also publishes the fused append's stores to every wave
 
   v4f o[NT];
@@ -800,146 +810,146 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     lo = __builtin_bit_cast(uint32_t, a);
     hi = __builtin_bit_cast(uint32_t, c);
   };
-  // K: GD bytes of key r16's row at d GD*lg
-  // V: 4 bytes at d 64*half + 4*r16 of each of keys 4*lg + i
-  auto load_k = [&](int64_t off, U4* kr) {
-#pragma unroll
-    for (int c = 0; c < D / 64; ++c)
-      kr[c] = (off >= 0) ? stream_load(reinterpret_cast<const U4*>(p.c.k + off + r16 * D + GD * lg + 16 * c)) : U4{};
+  auto key_ok = [&](int t) -> bool {
+    if (t >= n) return false;
+    if constexpr (MASK) return mflag[t] != 0;
+    return true;
   };
-  auto load_v = [&](int64_t off, uint32_t (*vr)[4]) {
+  // Block jb's K chunks and V words; a block outside the partition or the
+  // cache loads from offset 0 (a valid address whose bytes are never used),
+  // so that every iteration issues the same loads and prefetches stay in
+  // flight.
+  const uint8_t* kbase = p.c.k + r16 * D + 16 * lg;
+  const uint8_t* vbase = p.c.v + (4 * lg) * D + VB * r16;
+  auto load = [&](int jb, U4* kr, VRow* vr) {
+    int64_t o0 = 0;
+    if (jb < nblk) o0 = offs[jb];
+    const int64_t off = uniform64(o0 >= 0 ? o0 : 0);
 #pragma unroll
-    for (int hf = 0; hf < HALVES; ++hf)
+    for (int c = 0; c < KC; ++c) kr[c] = stream_load(reinterpret_cast<const U4*>(kbase + off + 64 * c));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vr[hf][i] = (off >= 0) ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
-                                     p.c.v + off + (4 * lg + i) * D + 64 * hf + 4 * r16))
-                               : 0u;
-  };
-
-  U4 kr[D / 64], kn[D / 64];
-  uint32_t vr[HALVES][4], vn[HALVES][4];
-  if (wave < nblk) {
-    load_k(offs[wave], kr);
-    load_v(offs[wave], vr);
-  }
-  for (int jb = wave; jb < nblk; jb += kWaves) {
-    const int64_t off = offs[jb];
-    if (jb + kWaves < nblk) {
-      load_k(offs[jb + kWaves], kn);
-      load_v(offs[jb + kWaves], vn);
-    }
-    const int tok0 = (j0 + jb) * kBlockTokens;
-    if (off >= 0) {
-      // ---- scores S^T (keys 4*lg + r, head r16) ----
-      // two accumulation chains (even / odd steps) so consecutive MFMAs are
-      // independent
-      v4f sacc = v4f{0.f, 0.f, 0.f, 0.f}, sacc2 = v4f{0.f, 0.f, 0.f, 0.f};
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(kr);
-#pragma unroll
-      for (int sd = 0; sd < KS; ++sd) {
-        uint32_t a0, a1;
-        cvt4(kw[sd], a0, a1);
-        const v4s av = __builtin_bit_cast(v4s, (uint2){a0, a1});
-        const v4s bv = __builtin_bit_cast(v4s, (uint2){qb[sd][0], qb[sd][1]});
-        if (sd & 1)
-          sacc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, sacc2, 0, 0, 0);
-        else
-          sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, sacc, 0, 0, 0);
-      }
-      sacc += sacc2;
-      // ---- mask, block max, lazily raised running max ----
-      const bool full = !MASK && tok0 + kBlockTokens <= t1;
-      float z[4];
-      bool live[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = tok0 + 4 * lg + r;
-        bool ok = full || tok < t1;
-        if (MASK && ok) ok = mask_row[tok] != 0;
-        live[r] = ok;
-        z[r] = ok ? sacc[r] * zscale : -INFINITY;
-      }
-      float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      {
-        auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
-        bm = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-        auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
-        bm = fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-      }
-      const bool need = bm > mrun + kRescale;
-      if (__any(need)) {
-        const float mnew = need ? bm : mrun;
-        const float alpha = need ? exp2f(mrun - mnew) : 1.f;  // 0 when mrun = -inf
-#pragma unroll
-        for (int t = 0; t < NT; ++t) o[t] *= alpha;
-        lsum *= alpha;
-        mrun = mnew;
-      }
-      const float msub = (mrun == -INFINITY) ? 0.f : mrun;
-      float pw[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pw[r] = __builtin_amdgcn_exp2f(z[r] - msub);
-        lsum += pw[r];
-      }
-      // weights as bf16 hi + lo (B operand: keys 4*lg + i)
-      typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-      bf2 h01, h23, l01, l23;
-      h01[0] = (__bf16)pw[0];
-      h01[1] = (__bf16)pw[1];
-      h23[0] = (__bf16)pw[2];
-      h23[1] = (__bf16)pw[3];
-      l01[0] = (__bf16)(pw[0] - (float)h01[0]);
-      l01[1] = (__bf16)(pw[1] - (float)h01[1]);
-      l23[0] = (__bf16)(pw[2] - (float)h23[0]);
-      l23[1] = (__bf16)(pw[3] - (float)h23[1]);
-      const v4s phi = __builtin_bit_cast(v4s, (uint2){__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
-      const v4s plo = __builtin_bit_cast(v4s, (uint2){__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
-      // ---- V^T tiles: transpose 4 keys x 4 d per half, zero dead keys ----
-#pragma unroll
-      for (int hf = 0; hf < HALVES; ++hf) {
-        uint32_t a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = live[i] ? vr[hf][i] : 0u;  // keys with no weight never reach O
-        const uint32_t t01l = __builtin_amdgcn_perm(a[1], a[0], 0x05010400u);
-        const uint32_t t01h = __builtin_amdgcn_perm(a[1], a[0], 0x07030602u);
-        const uint32_t t23l = __builtin_amdgcn_perm(a[3], a[2], 0x05010400u);
-        const uint32_t t23h = __builtin_amdgcn_perm(a[3], a[2], 0x07030602u);
-        const uint32_t tj[4] = {__builtin_amdgcn_perm(t23l, t01l, 0x05040100u),
-                                __builtin_amdgcn_perm(t23l, t01l, 0x07060302u),
-                                __builtin_amdgcn_perm(t23h, t01h, 0x05040100u),
-                                __builtin_amdgcn_perm(t23h, t01h, 0x07060302u)};
-        v4s av[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t b0, b1;
-          cvt4(tj[j], b0, b1);
-          av[j] = __builtin_bit_cast(v4s, (uint2){b0, b1});
-        }
-        // hi parts of the four tiles, then the lo parts: no back-to-back
-        // MFMAs on one accumulator
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], phi, o[4 * hf + j], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], plo, o[4 * hf + j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (VW == 2) {
+        const uint2 w = __builtin_bit_cast(
+            uint2, __builtin_nontemporal_load(reinterpret_cast<const v2u*>(vbase + off + i * D)));
+        vr[i][0] = w.x;
+        vr[i][VW - 1] = w.y;
+      } else {
+        vr[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vbase + off + i * D));
       }
     }
+  };
+  auto process = [&](int jb, const U4* kr, const VRow* vr) {
+    if (uniform64(offs[jb]) < 0) return;  // block outside the cache: fully masked
+    // ---- scores S^T (keys 4*lg + r, head r16), two accumulation chains ----
+    v4f sacc = v4f{0.f, 0.f, 0.f, 0.f}, sacc2 = v4f{0.f, 0.f, 0.f, 0.f};
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(kr);
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) kr[c] = kn[c];
+    for (int sd = 0; sd < KS; ++sd) {
+      uint32_t a0, a1;
+      cvt4(kw[sd], a0, a1);
+      const v4s av = __builtin_bit_cast(v4s, v2u{a0, a1});
+      const v4s bv = __builtin_bit_cast(v4s, v2u{qb[sd][0], qb[sd][1]});
+      if (sd & 1)
+        sacc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, sacc2, 0, 0, 0);
+      else
+        sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, sacc, 0, 0, 0);
+    }
+    sacc += sacc2;
+    // ---- mask, block max, lazily raised running max ----
+    const int tk = kBlockTokens * jb + 4 * lg;
+    float z[4];
+    bool live[4];
 #pragma unroll
-    for (int hf = 0; hf < HALVES; ++hf)
+    for (int r = 0; r < 4; ++r) {
+      live[r] = key_ok(tk + r);
+      z[r] = live[r] ? sacc[r] * zscale : -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    {
+      auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      bm = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      bm = fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+    }
+    const bool need = bm > mrun + kRescale;
+    if (__any(need)) {
+      const float mnew = need ? bm : mrun;
+      const float alpha = need ? exp2f(mrun - mnew) : 1.f;  // 0 when mrun = -inf
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vr[hf][i] = vn[hf][i];
+      for (int t = 0; t < NT; ++t) o[t] *= alpha;
+      lsum *= alpha;
+      mrun = mnew;
+    }
+    const float msub = (mrun == -INFINITY) ? 0.f : mrun;
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pw[r] = __builtin_amdgcn_exp2f(z[r] - msub);
+      lsum += pw[r];
+    }
+    // weights as bf16 hi + lo (B operand: keys 4*lg + i)
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 h01, h23, l01, l23;
+    h01[0] = (__bf16)pw[0];
+    h01[1] = (__bf16)pw[1];
+    h23[0] = (__bf16)pw[2];
+    h23[1] = (__bf16)pw[3];
+    l01[0] = (__bf16)(pw[0] - (float)h01[0]);
+    l01[1] = (__bf16)(pw[1] - (float)h01[1]);
+    l23[0] = (__bf16)(pw[2] - (float)h23[0]);
+    l23[1] = (__bf16)(pw[3] - (float)h23[1]);
+    const v4s phi = __builtin_bit_cast(v4s, v2u{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
+    const v4s plo = __builtin_bit_cast(v4s, v2u{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+    // ---- V^T tiles: transpose 4 keys x 4 d per word, zero dead keys ----
+#pragma unroll
+    for (int w = 0; w < VW; ++w) {
+      uint32_t a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = live[i] ? vr[i][w] : 0u;  // keys with no weight never reach O
+      const uint32_t t01l = __builtin_amdgcn_perm(a[1], a[0], 0x05010400u);
+      const uint32_t t01h = __builtin_amdgcn_perm(a[1], a[0], 0x07030602u);
+      const uint32_t t23l = __builtin_amdgcn_perm(a[3], a[2], 0x05010400u);
+      const uint32_t t23h = __builtin_amdgcn_perm(a[3], a[2], 0x07030602u);
+      const uint32_t tj[4] = {__builtin_amdgcn_perm(t23l, t01l, 0x05040100u),
+                              __builtin_amdgcn_perm(t23l, t01l, 0x07060302u),
+                              __builtin_amdgcn_perm(t23h, t01h, 0x05040100u),
+                              __builtin_amdgcn_perm(t23h, t01h, 0x07060302u)};
+      v4s av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t b0, b1;
+        cvt4(tj[j], b0, b1);
+        av[j] = __builtin_bit_cast(v4s, v2u{b0, b1});
+      }
+      // hi parts of the four tiles, then the lo parts: no back-to-back
+      // MFMAs on one accumulator
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[4 * w + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], phi, o[4 * w + j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[4 * w + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], plo, o[4 * w + j], 0, 0, 0);
+    }
+  };
+  {
+    U4 ka[KC], kb[KC];
+    VRow va[4], vb[4];
+    load(wave, ka, va);
+    for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
+      load(jb + kWaves, kb, vb);
+      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for block jb
+      process(jb, ka, va);
+      load(jb + 2 * kWaves, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      if (jb + kWaves < nblk) process(jb + kWaves, kb, vb);
+    }
   }
 
   // ---- combine the four waves: per head, M = max of the wave maxima ----
   // the wave's row sum of head r16 is spread over its four lane groups
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  float* wstat = red + kWaves * G * D;  // [kWaves][G][2]
   if (lg == 0 && r16 < G) {
     wstat[(wave * G + r16) * 2] = mrun;
     wstat[(wave * G + r16) * 2 + 1] = lsum;
@@ -951,14 +961,9 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
   const float mine = (mrun == -INFINITY || M == -INFINITY) ? 0.f : exp2f(mrun - M);
   if (r16 < G) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int hf = t / 4, j = t % 4;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d = 64 * hf + 4 * (4 * lg + rr) + j;
-        red[(wave * G + r16) * D + d] = o[t][rr] * mine;
-      }
-    }
+      for (int rr = 0; rr < 4; ++rr) red[(wave * G + r16) * D + VB * (4 * lg + rr) + t] = o[t][rr] * mine;
   }
   __syncthreads();
   const int nparts_b = (ctx + T - 1) / T;
@@ -1063,7 +1068,8 @@ template <int KVT, int D, int G, bool MASK>
 int launch_typed(const DecodeLaunch& a, hipStream_t s) {
   const dim3 grid(a.num_kv_heads, a.num_parts, a.batch);
   if constexpr (KVT == KVATTN_FP8_E4M3 && G >= 4) {
-    const size_t lds = (size_t)(decode_off_floats(a.part_tokens) + kWaves * G * D + kWaves * G * 2) * sizeof(float);
+    const size_t lds = (size_t)(decode_off_floats(a.part_tokens) + kWaves * G * D + kWaves * G * 2 +
+                                (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
     hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
   } else if constexpr (KVT == KVATTN_BF16 && G >= 4) {
     const size_t lds = (size_t)(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
