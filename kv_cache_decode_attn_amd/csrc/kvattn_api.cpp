@@ -102,7 +102,7 @@ constexpr int32_t kMaxPartScores = 8192;  // part_tokens * group, bounds the LDS
 // Default keys per partition, per partition kernel (measured on MI355X):
 //  - fp8 cache with G >= 4 (matrix-core pass): long partitions amortise the
 //    per-workgroup combine and shrink the merge; take the largest size that
-//    still gives >= 512 workgroups (2048 keys at 131K keys x 8 KV heads).
+//    still gives >= 256 workgroups (4096 keys at 131K keys x 8 KV heads).
 //  - vector-ALU pass: 512 keys for G >= 4, 256 for G <= 2, shrunk until the
 //    grid offers >= 2048 workgroups.
 bool fp8_mfma_pass(int32_t dtype, int32_t group) { return dtype == KVATTN_FP8_E4M3 && group >= 4; }
@@ -112,7 +112,7 @@ int32_t default_part_tokens(int32_t dtype, int32_t batch, int32_t hq, int32_t hk
   auto wgs = [&](int32_t t) { return (int64_t)batch * hkv * (((int64_t)max_seq_len + t - 1) / t); };
   if (fp8_mfma_pass(dtype, group)) {
     int32_t t = kMaxPartTokens;
-    while (t > 256 && wgs(t) < 512) t /= 2;
+    while (t > 256 && wgs(t) < 256) t /= 2;
     return t;
   }
   int32_t t = group >= 4 ? 512 : 256;

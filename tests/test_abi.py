@@ -57,7 +57,7 @@ def test_workspace_and_partition_sizing():
     assert L.kvattn_decode_default_part_tokens(_lib.BF16, 1, 3, 2, 100) == 0          # bad group
     assert L.kvattn_decode_default_part_tokens(9, 1, 8, 8, 100) == 0                  # bad dtype
     # the fp8 matrix-core pass takes long partitions for one long sequence
-    assert L.kvattn_decode_default_part_tokens(_lib.FP8_E4M3, 1, 64, 8, 131073) == 2048
+    assert L.kvattn_decode_default_part_tokens(_lib.FP8_E4M3, 1, 64, 8, 131073) == 4096
 
 
 FAKE = 0x10000  # an aligned non-null address; host validation never dereferences it
