@@ -202,6 +202,33 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Streams the blocks jb, jb + kWaves, ... (< nblk) of one wave through two
+// register sets: while one block is consumed the next one's loads are in
+// flight.  `a` already holds block jb when jb < nblk.  Every load is a real
+// block and every iteration issues the same loads, so the compiler's
+// load-count waits release exactly the block about to be consumed; the
+// scheduling barriers keep each prefetch ahead of the wait for the block
+// before it.
+template <typename Buf, typename LoadF, typename BodyF>
+__device__ __forceinline__ void stream_blocks(int jb, int nblk, Buf& a, Buf& b, const LoadF& load,
+                                              const BodyF& body) {
+  for (; jb + 2 * kWaves < nblk; jb += 2 * kWaves) {
+    load(jb + kWaves, b);
+    __builtin_amdgcn_sched_barrier(0);
+    body(jb, a);
+    load(jb + 2 * kWaves, a);
+    __builtin_amdgcn_sched_barrier(0);
+    body(jb + kWaves, b);
+  }
+  if (jb < nblk) {
+    const bool two = jb + kWaves < nblk;
+    if (two) load(jb + kWaves, b);
+    __builtin_amdgcn_sched_barrier(0);
+    body(jb, a);
+    if (two) body(jb + kWaves, b);
+  }
+}
+
 // K and V bytes are read exactly once per call: load them non-temporally so
 // the stream does not displace reusable lines (q, block table, partials)
 // from the caches.
@@ -272,20 +299,17 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   const uint8_t* vbase = p.c.v + row * ROWB + col * (int)sizeof(Raw);
   __syncthreads();  // also publishes the fused append's stores to every wave
 
-  // Byte offset to load block jb from: its own, or (outside the partition or
-  // the cache) offset 0, a valid address whose bytes are never used, so that
-  // every iteration issues the same loads and the prefetches stay in flight.
+  // Block jb's rows (jb < nblk); a block outside the cache is read at offset
+  // 0, a valid address whose bytes are never used (its keys are masked).
   auto load_block = [&](int jb, const uint8_t* base, Raw* r) {
-    int64_t o = 0;
-    if (jb < nblk) o = offs[jb];
+    const int64_t o = offs[jb];
     const int64_t off = uniform64(o >= 0 ? o : 0);
 #pragma unroll
     for (int i = 0; i < NI; ++i) r[i] = stream_load(reinterpret_cast<const Raw*>(base + off + i * TPI * ROWB));
   };
 
   // ---- phase 1: scores of every key of the partition ----
-  // Wave w handles blocks w, w + 4, ...; two register sets alternate so the
-  // next block's loads are in flight while one is consumed.
+  // Wave w handles blocks w, w + 4, ... (stream_blocks).
   auto scores = [&](int jb, const Raw* cur) {
     const bool in_cache = uniform64(offs[jb]) >= 0;
 #pragma unroll
@@ -315,19 +339,12 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   };
   {
     Raw ka[NI], kb[NI];
-    load_block(wave, kbase, ka);
-    for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
-      load_block(jb + kWaves, kbase, kb);
-      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for ka
-      scores(jb, ka);
-      load_block(jb + 2 * kWaves, kbase, ka);
-      __builtin_amdgcn_sched_barrier(0);
-      if (jb + kWaves < nblk) scores(jb + kWaves, kb);
-    }
+    if (wave < nblk) load_block(wave, kbase, ka);
+    stream_blocks(wave, nblk, ka, kb, [&](int jb, Raw* r) { load_block(jb, kbase, r); }, scores);
   }
   // The first V block is fetched while the softmax statistics are formed.
   Raw va[NI], vb[NI];
-  load_block(wave, vbase, va);
+  if (wave < nblk) load_block(wave, vbase, va);
   __syncthreads();
 
   // ---- phase 2: per-head max and sum; scores -> weights exp2(z - max) ----
@@ -393,14 +410,7 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
         for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(w[h], vf[e], o[h][e]);
     }
   };
-  for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
-    load_block(jb + kWaves, vbase, vb);
-    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for va
-    accumulate(jb, va);
-    load_block(jb + 2 * kWaves, vbase, va);
-    __builtin_amdgcn_sched_barrier(0);
-    if (jb + kWaves < nblk) accumulate(jb + kWaves, vb);
-  }
+  stream_blocks(wave, nblk, va, vb, [&](int jb, Raw* r) { load_block(jb, vbase, r); }, accumulate);
 
   // reduce over the TPI rows of the wave (lanes sharing col)
 #pragma unroll
@@ -527,16 +537,14 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
     if constexpr (MASK) return mflag[t] != 0;
     return true;
   };
-  // Byte offset to load block jb from: its own, or (outside the partition or
-  // the cache) offset 0, a valid address whose bytes are never used, so that
-  // every iteration issues the same loads and the prefetches stay in flight.
+  // Byte offset of block jb (jb < nblk); a block outside the cache is read at
+  // offset 0, a valid address whose bytes are never used (its keys are masked).
   auto load_off = [&](int jb) -> int64_t {
-    int64_t o = 0;
-    if (jb < nblk) o = offs[jb];
+    const int64_t o = offs[jb];
     return uniform64(o >= 0 ? o : 0);
   };
 
-  // ---- phase 1: scores; blocks jb = wave + 4i, two in flight (ping-pong) ----
+  // ---- phase 1: scores; blocks jb = wave + 4i (stream_blocks) ----
   // K chunk c of lane (r16, lg): bytes 64c + 16*lg of key r16's row, so one
   // load instruction reads 64 contiguous bytes of each of 16 rows (a 128-byte
   // line is read by two instructions back to back, never in quarters).
@@ -571,15 +579,8 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
   };
   {
     U4 ka[KC], kb[KC];
-    load_k(wave, ka);
-    for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
-      load_k(jb + kWaves, kb);
-      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for ka
-      scores(jb, ka);
-      load_k(jb + 2 * kWaves, ka);
-      __builtin_amdgcn_sched_barrier(0);
-      if (jb + kWaves < nblk) scores(jb + kWaves, kb);
-    }
+    if (wave < nblk) load_k(wave, ka);
+    stream_blocks(wave, nblk, ka, kb, load_k, scores);
   }
   // V: 8 bytes (d 64*hf + 4*r16 ..+3) of each of keys 4*lg + i
   const uint8_t* vbase = p.c.v + (4 * lg) * ROWB + 8 * r16;
@@ -594,7 +595,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
   };
   // The first V block is fetched while the softmax statistics are formed.
   uint2 va[HALVES][4], vb[HALVES][4];
-  load_v(wave, va);
+  if (wave < nblk) load_v(wave, va);
   __syncthreads();
 
   // ---- phase 2: per-head max and sum; scores -> weights exp2(z - max) ----
@@ -669,14 +670,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
         o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], plo, o[4 * hf + j], 0, 0, 0);
     }
   };
-  for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
-    load_v(jb + kWaves, vb);
-    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for va
-    accumulate(jb, va);
-    load_v(jb + 2 * kWaves, va);
-    __builtin_amdgcn_sched_barrier(0);
-    if (jb + kWaves < nblk) accumulate(jb + kWaves, vb);
-  }
+  stream_blocks(wave, nblk, va, vb, load_v, accumulate);
 
   __syncthreads();  // every wave is done reading weights; reuse LDS
   float* red = s_lds;  // [kWaves][G][D]
@@ -815,15 +809,18 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     if constexpr (MASK) return mflag[t] != 0;
     return true;
   };
-  // Block jb's K chunks and V words; a block outside the partition or the
-  // cache loads from offset 0 (a valid address whose bytes are never used),
-  // so that every iteration issues the same loads and prefetches stay in
-  // flight.
+  // Block jb's K chunks and V words (jb < nblk); a block outside the cache
+  // is read at offset 0, a valid address whose bytes are never used.
   const uint8_t* kbase = p.c.k + r16 * D + 16 * lg;
   const uint8_t* vbase = p.c.v + (4 * lg) * D + VB * r16;
-  auto load = [&](int jb, U4* kr, VRow* vr) {
-    int64_t o0 = 0;
-    if (jb < nblk) o0 = offs[jb];
+  struct Blk {
+    U4 k[KC];
+    VRow v[4];
+  };
+  auto load = [&](int jb, Blk& blk) {
+    U4* kr = blk.k;
+    VRow* vr = blk.v;
+    const int64_t o0 = offs[jb];
     const int64_t off = uniform64(o0 >= 0 ? o0 : 0);
 #pragma unroll
     for (int c = 0; c < KC; ++c) kr[c] = stream_load(reinterpret_cast<const U4*>(kbase + off + 64 * c));
@@ -839,7 +836,9 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
       }
     }
   };
-  auto process = [&](int jb, const U4* kr, const VRow* vr) {
+  auto process = [&](int jb, const Blk& blk) {
+    const U4* kr = blk.k;
+    const VRow* vr = blk.v;
     if (uniform64(offs[jb]) < 0) return;  // block outside the cache: fully masked
     // ---- scores S^T (keys 4*lg + r, head r16), two accumulation chains ----
     v4f sacc = v4f{0.f, 0.f, 0.f, 0.f}, sacc2 = v4f{0.f, 0.f, 0.f, 0.f};
@@ -933,17 +932,9 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     }
   };
   {
-    U4 ka[KC], kb[KC];
-    VRow va[4], vb[4];
-    load(wave, ka, va);
-    for (int jb = wave; jb < nblk; jb += 2 * kWaves) {
-      load(jb + kWaves, kb, vb);
-      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for block jb
-      process(jb, ka, va);
-      load(jb + 2 * kWaves, ka, va);
-      __builtin_amdgcn_sched_barrier(0);
-      if (jb + kWaves < nblk) process(jb + kWaves, kb, vb);
-    }
+    Blk ba, bb;
+    if (wave < nblk) load(wave, ba);
+    stream_blocks(wave, nblk, ba, bb, load, process);
   }
 
   // ---- combine the four waves: per head, M = max of the wave maxima ----
@@ -994,73 +985,88 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
   }
 }
 
-// Merge the split-K partials of one (sequence, query head), for 32 output
-// columns per workgroup: the partition maxima give M, each partition's
-// weight exp2(m_p - M) is staged in LDS (0 for an empty partition), and the
-// 256 threads (32 columns x 8 partition phases) sum w_p * o_p with several
-// independent loads in flight, then combine the phases through LDS.
-constexpr int kMergeCols = 32;
-constexpr int kMergePhases = 8;
-constexpr int kMergeStage = 2048;  // partitions whose weights are staged in LDS
-
+// Merge the split-K partials of one (sequence, query head).  256 threads =
+// D/4 float4 columns x phases; a phase thread takes partitions ph, ph + PH,
+// ... and issues all their loads (the (max, sum) pair and its float4 of the
+// output) before using any, keeping its own running max, sum and output
+// (each partition's weight exp2(m_p - M) relative to the running M); the
+// phases are then combined in order through LDS.  Fixed order throughout,
+// so the result is bitwise reproducible.
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge(const DecodeLaunch p) {
-  __shared__ float wts[kMergeStage];
-  __shared__ float red[2][4];
-  __shared__ float part[kMergePhases][kMergeCols];
-  const int hq = blockIdx.x, b = blockIdx.y, c0 = blockIdx.z * kMergeCols;
+  constexpr int NC = D / 4;       // float4 columns
+  constexpr int PH = 256 / NC;    // partition phases
+  constexpr int U = 4;            // partitions per batch of loads
+  __shared__ float4 pacc[PH][NC];
+  __shared__ float pm[PH], pl[PH];
+  const int hq = blockIdx.x, b = blockIdx.y;
   const int T = p.part_tokens;
   const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
   const int np = (ctx + T - 1) / T;
   if (np <= 1) return;  // written by the partition pass
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, c = tid % NC, ph = tid / NC;
   const int64_t slot0 = ((int64_t)b * p.num_q_heads + hq) * p.num_parts;
-  const float* ml = p.ws_ml + slot0 * 2;
-  const float* wo = p.ws_o + slot0 * D;
-  float M = -INFINITY;
-  for (int i = tid; i < np; i += 256) M = fmaxf(M, ml[2 * i]);
-  M = group_max<64>(M);
-  if (lane == 0) red[0][wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  float L = 0.f;
-  for (int i = tid; i < np; i += 256) {
-    const float m = ml[2 * i];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    if (i < kMergeStage) wts[i] = w;
-    L = fmaf(w, ml[2 * i + 1], L);
-  }
-  L = group_sum<64>(L);
-  if (lane == 0) red[1][wave] = L;
-  __syncthreads();
-  L = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-  const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  const int col = tid % kMergeCols, ph = tid / kMergeCols;
-  const float* src = wo + c0 + col;
-  auto weight = [&](int i) -> float {
-    if (i < kMergeStage) return wts[i];
-    const float m = ml[2 * i];
-    return (m == -INFINITY) ? 0.f : exp2f(m - M);
+  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + slot0;
+  const float4* wo = reinterpret_cast<const float4*>(p.ws_o + slot0 * D) + c;
+  float m = -INFINITY, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](float2 s, float4 x) {
+    if (s.x == -INFINITY) return;  // partition with no attended key
+    if (s.x > m) {
+      const float alpha = exp2f(m - s.x);  // 0 while m = -inf
+      acc.x *= alpha;
+      acc.y *= alpha;
+      acc.z *= alpha;
+      acc.w *= alpha;
+      l *= alpha;
+      m = s.x;
+    }
+    const float w = exp2f(s.x - m);
+    acc.x = fmaf(w, x.x, acc.x);
+    acc.y = fmaf(w, x.y, acc.y);
+    acc.z = fmaf(w, x.z, acc.z);
+    acc.w = fmaf(w, x.w, acc.w);
+    l = fmaf(w, s.y, l);
   };
-  float acc0 = 0.f, acc1 = 0.f;
   int i = ph;
-  for (; i + kMergePhases < np; i += 2 * kMergePhases) {
-    const float w0 = weight(i), w1 = weight(i + kMergePhases);
-    const float x0 = src[(int64_t)i * D], x1 = src[(int64_t)(i + kMergePhases) * D];
-    if (w0 != 0.f) acc0 = fmaf(w0, x0, acc0);
-    if (w1 != 0.f) acc1 = fmaf(w1, x1, acc1);
+  for (; i + (U - 1) * PH < np; i += U * PH) {
+    float2 s[U];
+    float4 x[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      s[k] = ml[i + k * PH];
+      x[k] = wo[(int64_t)(i + k * PH) * NC];
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) add(s[k], x[k]);
   }
-  if (i < np) {
-    const float w0 = weight(i);
-    if (w0 != 0.f) acc0 = fmaf(w0, src[(int64_t)i * D], acc0);
+  for (; i < np; i += PH) add(ml[i], wo[(int64_t)i * NC]);
+  pacc[ph][c] = acc;
+  if (c == 0) {
+    pm[ph] = m;
+    pl[ph] = l;
   }
-  part[ph][col] = acc0 + acc1;
   __syncthreads();
   if (ph == 0) {
-    float sum = part[0][col];
+    float M = -INFINITY;
 #pragma unroll
-    for (int k = 1; k < kMergePhases; ++k) sum += part[k][col];
-    p.out[((int64_t)b * p.num_q_heads + hq) * D + c0 + col] = sum * inv;
+    for (int k = 0; k < PH; ++k) M = fmaxf(M, pm[k]);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < PH; ++k) {
+      if (pm[k] == -INFINITY) continue;
+      const float w = exp2f(pm[k] - M);
+      const float4 y = pacc[k][c];
+      o.x = fmaf(w, y.x, o.x);
+      o.y = fmaf(w, y.y, o.y);
+      o.z = fmaf(w, y.z, o.z);
+      o.w = fmaf(w, y.w, o.w);
+      L = fmaf(w, pl[k], L);
+    }
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    reinterpret_cast<float4*>(p.out + ((int64_t)b * p.num_q_heads + hq) * D)[c] =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   }
 }
 
@@ -1080,7 +1086,7 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
   }
   if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
   if (a.num_parts > 1) {
-    hipLaunchKernelGGL((decode_merge<D>), dim3(a.num_q_heads, a.batch, D / kMergeCols), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_merge<D>), dim3(a.num_q_heads, a.batch), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
   }
   return KVATTN_OK;
