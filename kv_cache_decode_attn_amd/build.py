@@ -31,9 +31,17 @@ COMMON = [
 ]
 
 
+# Per-file extra flags.  The MFMA prefill kernel takes maxima of raw matrix
+# results; without NaN-preserving semantics the compiler drops one quieting
+# instruction per score.  NaN can only reach that kernel through padding
+# query rows (whose outputs are written as zeros) and masked keys (whose
+# scores are replaced by -inf before any maximum), so no result changes.
+EXTRA = {"prefill_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -9,23 +9,34 @@
 // (factory.pai-world.com), section "Flash Attention - tiling trick"), with
 // the exact running (max, sum) rescaling of its numerical-trick paragraph.
 // Prefill is compute bound ("KV Cache" (heepie.pages.dev), section "Prefill
-// and Decode"), so both products run on the matrix cores.  The 32x32x16
-// bf16 shape is used because it is the one that issues at the full matrix
-// rate on gfx950 (the 16x16x32 shape measured at about half of it).
+// and Decode"), so both products run on the matrix cores.
 //
-// Work split.  A workgroup of 4 waves owns HW = min(G, 4) query heads of one
-// KV head and a tile of 32 * 4 / HW query rows; each wave owns one head and
-// 32 query rows.  The heads of a GQA group share the K/V tiles staged in LDS.
-// Causal tiles are issued heaviest first.
+// Budget on gfx950 per compute unit: the 32x32x16 bf16 MFMA of one SIMD
+// needs 1 KB of operand from LDS per instruction if only one of its operands
+// lives in registers, which is all of the LDS read bandwidth (128 B/clock)
+// at the full matrix rate.  So every K and V^T fragment read from LDS here
+// feeds two MFMAs: a wave owns 64 query columns (two 32-column blocks) and
+// keeps their Q fragments in registers.  That needs about 400 registers,
+// i.e. one wave per SIMD, so the wave overlaps its own matrix and vector
+// work: the QK^T products of tile t+1 are issued while the softmax of tile t
+// runs on the vector ALU, and the global loads of tile t+2 fly meanwhile.
 //
-// Per 32-key tile, per wave (h = lane / 32):
+// Work split.  A workgroup of 4 waves owns HW = min(G, 8) query heads of one
+// KV head and 256 / HW query rows, cut into eight 32-row column blocks, two
+// per wave.  The heads of a GQA group share the K/V tiles staged in LDS
+// (three buffers: tile t+1 is read for QK^T while tile t is read for PV and
+// tile t+2 is written).  The KV head is the fastest grid dimension, so with
+// 8 KV heads every XCD (and its L2) serves one KV head; causal query tiles
+// are issued heaviest first.
+//
+// Per 64-key tile and column block (h = lane / 32):
 //   S^T[key][q] = K Q^T      A = K rows from LDS, B = Q (registers), fp32
 //                            accumulate.  The 32x32 accumulator gives lane l
 //                            query column l % 32 and keys 8*(r/4) + 4h + r%4
-//                            (r = 0..15): a query's 32 scores sit in two
-//                            lanes, so the row max is a local max plus one
-//                            cross-half swap, and P^T is already the B
-//                            operand of the second product.
+//                            (r = 0..15) of each 32-key half: a query's
+//                            scores sit in two lanes, so the row max is a
+//                            local max plus one cross-half swap, and P^T is
+//                            already the B operand of the second product.
 //   P = exp2(S*c - m)        c = scale*log2(e); m is a per-query running
 //                            maximum that is only raised (with rescaling of
 //                            the accumulators) when the tile maximum exceeds
@@ -33,11 +44,13 @@
 //   O^T[d][q] += V^T P^T     A = V^T from LDS.  V is transposed while it is
 //                            staged into LDS; inside a V^T row the keys are
 //                            ordered like P^T's operand slots.
-//   l[q] += 1 . P^T          an MFMA against a ones operand, so the row sum
-//                            is the sum of the same bf16 weights used for O.
+//   l[q] += P . 1            bf16 dot products of the rounded weights, so the
+//                            row sum is the sum of the same weights used for O.
 // Masked keys (causal, beyond q_len, key_mask) get P = 0 and their V rows are
 // staged as zeros, so non-finite padding never reaches O.
 #include <math.h>
+
+#include <type_traits>
 
 #include "launch.h"
 
@@ -46,14 +59,20 @@ namespace kvattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKeys = 64;      // keys per tile (two 32-key score sub-tiles)
-constexpr int kSub = kKeys / 32;
-constexpr int kWaveQ = 32;     // query rows per wave
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kKeys = 32;      // keys per tile
+constexpr int kThreads = 256;  // 4 waves, one per SIMD
+constexpr int kBlocks = 8;     // 32-row query column blocks per workgroup
+constexpr int kBufs = 8;       // LDS tile buffers (a ring)
+constexpr int kAhead = 5;      // tiles loaded ahead of the one being scored
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescale = 8.0f;  // log2 headroom before the running max moves
+// log2 headroom before the running max moves: weights stay below 2^64, far
+// inside the range of bf16 weights and fp32 sums, so a moved maximum (and
+// the rescaling of the accumulators it needs) is rare.
+constexpr float kRescale = 64.0f;
 
 __device__ __forceinline__ f32x16 mfma(const U4& a, const U4& b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -61,281 +80,630 @@ __device__ __forceinline__ f32x16 mfma(const U4& a, const U4& b, f32x16 c) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v;
   v[0] = (__bf16)lo;  // round to nearest even
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// LDS geometry (bytes), two buffers.  K rows are padded to D/2 + 4 dwords
-// and V^T rows to kKeys/2 + 4 dwords, so that 16 lanes reading 16
-// consecutive rows at one column touch 16 disjoint groups of 4 banks.
-template <int D>
-struct Geo {
-  static constexpr int KROW = D * 2 + 16;
-  static constexpr int VROW = kKeys * 2 + 16;
-  static constexpr int KBYTES = kKeys * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int MBYTES = kKeys;  // per-key valid flags of the tile
-  static constexpr int BUF = KBYTES + VBYTES + MBYTES;
-};
-
-// Position of key k (0..kKeys-1) inside a V^T row.  The PV product for keys
-// 16m .. 16m+15 of a 32-key sub-tile takes, in lane half h, operand slot j =
-// key 16m + 8*(j/4) + 4h + j%4 (the key order of the score accumulator), so
-// keys are stored at 16m + 8h + j to make each slot group one 16-byte read.
-__device__ __forceinline__ int vpos(int k) {
-  return 32 * (k >> 5) + 16 * ((k >> 4) & 1) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
+// The PV MFMAs are written as inline assembly so that the 128 O^T
+// accumulator registers of a wave stay in the accumulation register file,
+// out of the vector register file that holds the scores, weights and
+// operands; the accumulators are only ever touched by these instructions
+// and by acc_ready()-guarded code.  The compiler does not model this
+// instruction, so the code around it provides what it needs: two wait
+// states after a vector write of an operand (the s_nop 1), none between
+// back-to-back accumulations into the same registers, and acc_ready()
+// before any other access to the accumulators.
+//
+// acc += a * b, acc in accumulation registers.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const U4& a, const U4& b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+a"(acc)
+               : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b)));
+#endif
+}
+// Wait states before acc, last written by mfma_acc, is read or written by
+// anything else (the matrix result latency of a 32x32x16 MFMA).
+__device__ __forceinline__ void acc_ready(f32x16& acc) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+#endif
 }
 
+// An empty statement that needs x in accumulation registers.
+__device__ __forceinline__ void settle_acc(const U4& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  asm volatile("" ::"a"(__builtin_bit_cast(u32x4, x)));
+#endif
+}
+
+// An empty statement that redefines x: what uses x stays after it.
+__device__ __forceinline__ void anchor(float& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+}
+
+__device__ __forceinline__ void anchor(U4& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v = __builtin_bit_cast(u32x4, x);
+  asm volatile("" : "+v"(v));
+  x = __builtin_bit_cast(U4, v);
+#endif
+}
+
+// An empty statement that needs x: what computes x stays before it.
+__device__ __forceinline__ void settle(const U4& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  asm volatile("" ::"v"(__builtin_bit_cast(u32x4, x)));
+#endif
+}
+__device__ __forceinline__ void settle(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
+
+// sum of the two bf16 weights of w, accumulated in fp32
+__device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
+  const uint32_t one2 = 0x3F803F80u;  // two bf16 1.0
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, one2), acc,
+                                         false);
+}
+
+// LDS geometry (bytes) of one tile buffer: K and V rows of D*2 bytes in
+// 16-byte chunks, unpadded.  The LDS
+// serves 256 bytes per clock: 16 lanes of a 16-byte read, or 32 lanes of
+// an 8-byte read, must touch 16 distinct 16-byte slots modulo 256 bytes.
+// So the chunk index of row r is XOR-swizzled:
+//   K (16-byte reads, 16 lanes = rows r .. r+15 at one chunk):
+//     d = 128 (256-byte rows): c ^ (r % 16);
+//     d = 64 (128-byte rows, two per 256 bytes): c ^ ((r / 2) % 8);
+//   V (transposing 8-byte reads, 32 lanes = 4 rows x 2 d halves x 4 pieces):
+//     d = 128: c ^ 4 (r % 4);  d = 64: c ^ 4 ((r / 2) % 2).
+template <int D>
+struct Geo {
+  static constexpr int RB = D * 2;  // row bytes
+  static constexpr int NC = D / 8;  // 16-byte chunks per row
+  static constexpr int KBYTES = kKeys * RB;
+  static constexpr int VBYTES = kKeys * RB;
+  static constexpr int BUF = KBYTES + VBYTES;
+  static constexpr int LOADS = kKeys * NC / 64 / 4;  // 1 KB wave loads per wave, per operand
+  static_assert(LOADS >= 1 && LOADS * 4 * 64 == kKeys * NC, "tile split over the waves");
+  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
+
+// gfx950 memory operations used below, as small wrappers whose bodies exist
+// in the device pass only (the host pass compiles the kernel for its launch
+// stub and never runs it).
+//
+// A buffer resource (the four descriptor words) over `bytes` bytes at
+// `base`: loads at offsets past the end return zeros.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)p, (int)(uint32_t)((p >> 32) & 0xffffu), bytes, 0x00020000};
+}
+// 16 bytes per lane from rsrc + voffset straight into LDS at lds + 16 * lane
+// (lds uniform over the wave).  Issued as inline assembly: the compiler
+// then does not treat the transfer as a pending LDS store, which would make
+// it wait for every load in flight before any LDS read of the tile ring;
+// completion is awaited explicitly (finish_tile) before a barrier publishes
+// the tile.
+__device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint8_t* lds, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+#endif
+}
+// ds_read_b64_tr_b16 of 4 16-bit values at an LDS address.
+__device__ __forceinline__ s16x4 read_tr16(const uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)lds);
+#else
+  return s16x4{};
+#endif
+}
+
+// Scheduling groups (masks of __builtin_amdgcn_sched_group_barrier).
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
+
 template <int D, bool CAUSAL, bool MASK>
-__global__ void __launch_bounds__(kThreads, 2) prefill_mfma_kernel(const PrefillLaunch a, int hw) {
+__global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const PrefillLaunch a, int hw) {
   using GE = Geo<D>;
   constexpr int DK = D / 16;  // 16-wide d chunks of the QK^T contraction
   constexpr int DT = D / 32;  // 32-row d tiles of the output
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave
   const int hh = lane >> 5, lc = lane & 31;
   const int b = blockIdx.z;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int qw_per_head = 4 / hw;                  // 32-row sub-tiles per head
-  const int wg_rows = kWaveQ * qw_per_head;
-  const int qtile = gridDim.x - 1 - blockIdx.x;    // heaviest (causal) first
-  const int h = blockIdx.y * hw + (wave % hw);
-  const int g = (blockIdx.y * hw) / G;
-  const int q_wg = qtile * wg_rows;
-  const int q0 = q_wg + kWaveQ * (wave / hw);      // this wave's first row
+  const int rows_wg = 32 * kBlocks / hw;  // query rows of the workgroup
+  const int bph = rows_wg / 32;           // column blocks per head
+  const int qtile = gridDim.y - 1 - blockIdx.y;  // heaviest (causal) first
+  const int h0 = blockIdx.x * hw;
+  const int g = h0 / G;
+  const int q_wg = qtile * rows_wg;
   const int n_max = a.n_max;
   const int qlen = a.q_lens ? min(max(a.q_lens[b], 0), n_max) : n_max;
   const int P = a.positions ? max(a.positions[b], 0) : 0;
 
-  float* out_h = a.out + ((int64_t)b * a.num_q_heads + h) * n_max * D;
+  // this wave's two column blocks: head hb[cb], first row rb[cb]
+  int hb[2], rb[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int j = 2 * wave + cb;
+    hb[cb] = h0 + j / bph;
+    rb[cb] = q_wg + 32 * (j % bph);
+  }
+  const int row_lo = min(rb[0], rb[1]), row_hi = max(rb[0], rb[1]) + 32;
+
   if (q_wg >= qlen) {  // the whole tile is padding rows: zeros
-    for (int r = 0; r < kWaveQ; ++r) {
-      const int t = q0 + r;
-      if (t < n_max)
-        for (int d = lane; d < D; d += 64) out_h[(int64_t)t * D + d] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float* out_h = a.out + ((int64_t)b * a.num_q_heads + hb[cb]) * n_max * D;
+      for (int r = 0; r < 32; ++r) {
+        const int t = rb[cb] + r;
+        if (t < n_max)
+          for (int d = lane; d < D; d += 64) out_h[(int64_t)t * D + d] = 0.f;
+      }
     }
     return;
   }
-  const int key_end = CAUSAL ? min(qlen, q_wg + wg_rows) : qlen;  // workgroup bound
-  const int wave_end = CAUSAL ? min(qlen, q0 + kWaveQ) : qlen;     // this wave's bound
+  const int key_end = CAUSAL ? min(qlen, q_wg + rows_wg) : qlen;  // workgroup bound
+  const int wave_end = CAUSAL ? min(qlen, row_hi) : qlen;          // this wave's bound
   const int ntiles = (key_end + kKeys - 1) / kKeys;
+  const int wave_tiles = (wave_end + kKeys - 1) / kKeys;
+  // Tiles below fast_end need no mask: every key is real and causally
+  // visible to every query of the wave.
+  const int fast_end = MASK ? 0 : min(wave_tiles, (CAUSAL ? min(qlen, row_lo + 1) : qlen) / kKeys);
 
-  const uint8_t* kg = a.k + ((int64_t)b * a.num_kv_heads + g) * n_max * D * 2;
-  const uint8_t* vg = a.v + ((int64_t)b * a.num_kv_heads + g) * n_max * D * 2;
-  const uint8_t* qg = a.q + ((int64_t)b * a.num_q_heads + h) * n_max * D * 2;
+  const int64_t head_bytes = (int64_t)n_max * D * 2;
+  const uint8_t* kg = a.k + ((int64_t)b * a.num_kv_heads + g) * head_bytes;
+  const uint8_t* vg = a.v + ((int64_t)b * a.num_kv_heads + g) * head_bytes;
   const uint8_t* mrow = MASK ? a.key_mask + (int64_t)b * a.key_mask_stride : nullptr;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): row q0 + lc, d 16c + 8hh ----
-  const int tq = q0 + lc;
-  U4 qf[DK];
+  // ---- Q fragments (B operand of S^T = K Q^T): row rb + lc, d 16c + 8hh ----
+  int tq[2];
+  U4 qf[2][DK];
 #pragma unroll
-  for (int c = 0; c < DK; ++c)
-    qf[c] = (tq < n_max) ? *reinterpret_cast<const U4*>(qg + ((int64_t)tq * D + 16 * c + 8 * hh) * 2) : U4{0, 0, 0, 0};
+  for (int cb = 0; cb < 2; ++cb) {
+    tq[cb] = rb[cb] + lc;
+    const uint8_t* qg = a.q + ((int64_t)b * a.num_q_heads + hb[cb]) * n_max * D * 2;
+#pragma unroll
+    for (int c = 0; c < DK; ++c)
+    {
+      qf[cb][c] = (tq[cb] < n_max) ? *reinterpret_cast<const U4*>(qg + ((int64_t)tq[cb] * D + 16 * c + 8 * hh) * 2)
+                                   : U4{0, 0, 0, 0};
+    }
+  }
+  // Q lands (in accumulation registers) before the tile loop: the loop then
+  // carries no compiler-tracked vector-memory loads, so no wait in it counts
+  // the tile transfers in flight.
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int c = 0; c < DK; ++c) settle_acc(qf[cb][c]);
 
-  // ---- staging of one K/V tile: global -> registers -> LDS ----
-  // K: kKeys rows x D*2 bytes in 16-byte chunks, KCH per thread.
-  constexpr int KCH = kKeys * D / 8 / kThreads;
-  // V: a thread handles key pairs (2m, 2m+1) x 8 columns d in [8 dg, 8 dg+8);
-  // kKeys/2 pairs x D/8 column groups = VCH items per thread.
-  constexpr int VITEMS = (kKeys / 2) * (D / 8);
-  constexpr int VCH = VITEMS / kThreads;
-  static_assert(VCH * kThreads == VITEMS && KCH * kThreads == kKeys * D / 8, "staging split");
-  U4 kreg[KCH], vreg[VCH][2];
-  uint32_t mflag = 0;  // threads 0..kKeys-1: valid flag of key kt0 + tid
-
-  // A key is valid if it is a real token (< q_len) and, with a key mask,
-  // its mask byte (at absolute position P + key) is nonzero.
+  // ---- staging of one K/V tile: global -> LDS directly ----
+  // Each wave moves GE::LOADS 1 KB pieces of K and of V per tile with
+  // buffer loads that write LDS (lane i fills bytes 16i .. 16i+15 of the
+  // piece); a lane fetches the global chunk whose swizzled slot that is.
+  // The buffer resource of a tile starts at its first key and holds only
+  // the keys below min(q_len, end of the workgroup's last tile): loads past
+  // it return zeros, so rows of absent keys are staged as zeros.  With a key
+  // mask, rows of masked keys are zeroed by the loading wave once its loads
+  // have landed, so no non-finite padding reaches the PV product.
+  const int key_lim = min(qlen, ntiles * kKeys);
+  int koff[GE::LOADS], voff[GE::LOADS], lrow[GE::LOADS];  // per lane, tile independent
+#pragma unroll
+  for (int i = 0; i < GE::LOADS; ++i) {
+    const int slot = (wave * GE::LOADS + i) * 64 + lane;  // 16-byte slot in the tile
+    const int r = slot / GE::NC, cs = slot % GE::NC;
+    lrow[i] = r;
+    koff[i] = r * GE::RB + (cs ^ GE::swz_k(r)) * 16;
+    voff[i] = r * GE::RB + (cs ^ GE::swz_v(r)) * 16;
+  }
+  // A key is valid if it is a real token (< q_len) and, with a key mask, its
+  // mask byte (at absolute position P + key) is nonzero.  The byte is read at
+  // a clamped index and the terms are combined bitwise, so the test has no
+  // branch (a branchy form of this test was miscompiled).
+  const int mask_last = MASK ? (int)min<int64_t>(a.key_mask_stride, (int64_t)INT32_MAX) - 1 : 0;
   auto key_valid = [&](int key) -> bool {
     bool ok = key < qlen;
-    if (MASK && ok) ok = (P + key < a.key_mask_stride) && mrow[P + key] != 0;
+    if (MASK) {
+      const uint8_t mb = mrow[min(P + key, mask_last)];  // always inside the mask row
+      ok = ok & (P + key <= mask_last) & (mb != 0);
+    }
     return ok;
   };
-  auto load_tile = [&](int kt0) {
-    if (tid < kKeys) mflag = key_valid(kt0 + tid) ? 1u : 0u;
+  // With a key mask, per lane and tile in flight: bit i = this lane's V
+  // piece of load i belongs to a masked key.  A queue, oldest tile in the
+  // low byte: load_tile appends at byte `slot` (the number of tiles already
+  // queued), finish_tile pops the low byte.
+  uint64_t pending = 0;
+  auto load_tile = [&](int t, int slot) {
+    const int kt0 = t * kKeys;
+    uint8_t* kl = smem + (t % kBufs) * GE::BUF;
+    uint8_t* vl = kl + GE::KBYTES;
+    if (MASK) {
+      uint32_t info = 0;
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int ch = tid + c * kThreads;
-      const int key = kt0 + ch / (D / 8);
-      const int col = ch % (D / 8);
-      kreg[c] = (key < n_max) ? *reinterpret_cast<const U4*>(kg + ((int64_t)key * D + col * 8) * 2) : U4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int item = tid + c * kThreads;
-      const int vm = item % (kKeys / 2), vdg = item / (kKeys / 2);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int key = kt0 + 2 * vm + e;
-        vreg[c][e] = key_valid(key) ? *reinterpret_cast<const U4*>(vg + ((int64_t)key * D + 8 * vdg) * 2)
-                                    : U4{0, 0, 0, 0};
+      for (int i = 0; i < GE::LOADS; ++i) {
+        const int key = kt0 + lrow[i];
+        if (key < key_lim && !key_valid(key)) info |= 1u << i;
       }
+      pending |= (uint64_t)info << (8 * slot);
+    }
+    const int nbytes = max(key_lim - kt0, 0) * GE::RB;
+    const i32x4 kr = make_rsrc(kg + (int64_t)kt0 * GE::RB, nbytes);
+    const i32x4 vr = make_rsrc(vg + (int64_t)kt0 * GE::RB, nbytes);
+#pragma unroll
+    for (int i = 0; i < GE::LOADS; ++i) {
+      const int piece = wave * GE::LOADS + i;
+      load_lds16(kr, kl + piece * 1024, koff[i]);
+      load_lds16(vr, vl + piece * 1024, voff[i]);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint8_t* kl = smem + buf * GE::BUF;
-    uint8_t* vl = kl + GE::KBYTES;
-    if (tid < kKeys) vl[GE::VBYTES + tid] = (uint8_t)mflag;
+  // Waits until at most `younger` tiles' loads of this wave are in flight
+  // (so the oldest pending tile, t, has landed), then (key mask) zeroes its
+  // masked V rows.
+  auto finish_tile = [&](int t, auto younger) {
+    constexpr int vm = decltype(younger)::value * 2 * GE::LOADS;  // loads per tile: K and V
+    static_assert(vm < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8));  // vmcnt(vm)
+    if (MASK) {
+      uint8_t* vl = smem + (t % kBufs) * GE::BUF + GE::KBYTES;
+      const uint32_t info = (uint32_t)pending & 0xffu;
+      pending >>= 8;
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int ch = tid + c * kThreads;
-      *reinterpret_cast<U4*>(kl + (ch / (D / 8)) * GE::KROW + (ch % (D / 8)) * 16) = kreg[c];
+      for (int i = 0; i < GE::LOADS; ++i)
+        if (info & (1u << i)) *reinterpret_cast<U4*>(vl + (wave * GE::LOADS + i) * 1024 + lane * 16) = U4{0, 0, 0, 0};
     }
+  };
+
+  // S^T of the tile in buffer `buf`, both column blocks: keys
+  // kt0 + 8*(r/4) + 4hh + r%4, query rb[cb] + lc.  Each K fragment feeds the
+  // two column blocks.
+  auto scores = [&](int buf, f32x16 (&s)[2]) {
+    const uint8_t* kl = smem + buf * GE::BUF;
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int item = tid + c * kThreads;
-      const int vm = item % (kKeys / 2), vdg = item / (kKeys / 2);
-      // transpose 2 keys x 8 columns into 8 dwords (key 2m low, 2m+1 high)
-      const uint32_t x0[4] = {vreg[c][0].x, vreg[c][0].y, vreg[c][0].z, vreg[c][0].w};
-      const uint32_t x1[4] = {vreg[c][1].x, vreg[c][1].y, vreg[c][1].z, vreg[c][1].w};
-      const int pos = vpos(2 * vm);
+    for (int cc = 0; cc < DK; ++cc) {
+      const U4 kf = *reinterpret_cast<const U4*>(kl + lc * GE::RB + ((2 * cc + hh) ^ GE::swz_k(lc)) * 16);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = __builtin_amdgcn_perm(x1[i], x0[i], 0x05040100u);  // column 2i
-        const uint32_t hi = __builtin_amdgcn_perm(x1[i], x0[i], 0x07060302u);  // column 2i+1
-        *reinterpret_cast<uint32_t*>(vl + (8 * vdg + 2 * i) * GE::VROW + pos * 2) = lo;
-        *reinterpret_cast<uint32_t*>(vl + (8 * vdg + 2 * i + 1) * GE::VROW + pos * 2) = hi;
-      }
+      for (int cb = 0; cb < 2; ++cb) s[cb] = mfma(kf, qf[cb][cc], cc == 0 ? f32x16{} : s[cb]);
     }
   };
 
   // ---- accumulators ----
-  f32x16 o[DT], lsum;
+  f32x16 o[2][DT];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    lsum[r] = 0.f;
+  for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt][r] = 0.f;
-  }
-  float mrun = -INFINITY;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[cb][dt][r] = 0.f;
+  float mrun[2] = {-INFINITY, -INFINITY};
+  float lpart[2] = {0.f, 0.f};  // this lane's half of the row sum
   const float c = a.scale * kLog2e;
-  const uint32_t one2 = 0x3F803F80u;  // two bf16 1.0
-  const U4 ones = U4{one2, one2, one2, one2};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int kt0 = it * kKeys;
-    const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile(kt0 + kKeys);
-    if (kt0 < wave_end) {
-      const uint8_t* kl = smem + buf * GE::BUF;
-      const uint8_t* vl = kl + GE::KBYTES;
-      // S^T of the two 32-key sub-tiles: keys kt0 + 32 st + 8*(r/4) + 4hh +
-      // r%4, query q0 + lc; the two accumulation chains interleave.
-      f32x16 s[kSub];
+  // Softmax of the scores of the tile at kt0 into bf16 weights pf (and the
+  // row-sum halves); alpha receives the factor by which o must be rescaled
+  // once the previous tile's PV product is in, and `resc` whether any lane
+  // of the wave needs it.
+  auto softmax = [&](auto masked, int kt0, int buf, f32x16 (&s)[2], U4 (&pf)[2][2], float (&alpha)[2], bool& resc) {
+    if constexpr (decltype(masked)::value) {
+      // causal edge, keys beyond q_len, key mask (keys kt0 + 8gq + 4hh + e)
 #pragma unroll
-      for (int st = 0; st < kSub; ++st)
+      for (int gq = 0; gq < 4; ++gq)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * gq + e;
+          const int key = kt0 + 8 * gq + 4 * hh + e;
+          const bool kok = key_valid(key);
 #pragma unroll
-      for (int cc = 0; cc < DK; ++cc) {
-#pragma unroll
-        for (int st = 0; st < kSub; ++st) {
-          const U4 kf = *reinterpret_cast<const U4*>(kl + (32 * st + lc) * GE::KROW + (16 * cc + 8 * hh) * 2);
-          s[st] = mfma(kf, qf[cc], s[st]);
-        }
-      }
-      // masking: causal edge, keys beyond q_len, key mask.  The tile's key
-      // flags come from LDS as words of 4 keys (keys 32st + 8g + 4hh + 0..3).
-      const bool edge = (kt0 + kKeys > qlen) || (CAUSAL && kt0 + kKeys - 1 > q0);
-      if (MASK || edge) {
-        const uint32_t* mw = reinterpret_cast<const uint32_t*>(vl + GE::VBYTES);
-#pragma unroll
-        for (int st = 0; st < kSub; ++st)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const uint32_t w = mw[8 * st + 2 * gq + hh];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * gq + e;
-              const int key = kt0 + 32 * st + 8 * gq + 4 * hh + e;
-              const bool ok = ((w >> (8 * e)) & 0xffu) != 0 && (!CAUSAL || key <= tq);
-              s[st][r] = ok ? s[st][r] : -INFINITY;
-            }
+          for (int cb = 0; cb < 2; ++cb) {
+            const bool ok = kok & (!CAUSAL || key <= tq[cb]);
+            s[cb][r] = ok ? s[cb][r] : -INFINITY;
           }
-      }
+        }
+    }
+    bool any_need = false;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
       // running maximum of this query (log2 domain), raised lazily
-      float tm = s[0][0];
+      float tm = fmaxf(s[cb][0], s[cb][1]);
 #pragma unroll
-      for (int st = 0; st < kSub; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[st][r]);
+      for (int r = 2; r < 16; r += 2) tm = fmaxf(tm, fmaxf(s[cb][r], s[cb][r + 1]));
       {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
         tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
       }
-      const bool need = tm > mrun + kRescale;
-      if (__any(need)) {
-        const float mnew = need ? tm : mrun;
-        const float alpha = need ? exp2f(mrun - mnew) : 1.f;  // 0 when mrun = -inf
+      const bool need = tm > mrun[cb] + kRescale;
+      const float mnew = need ? tm : mrun[cb];
+      alpha[cb] = need ? exp2f(mrun[cb] - mnew) : 1.f;
+      any_need |= need && mrun[cb] != -INFINITY;  // nothing accumulated yet: nothing to rescale
+      mrun[cb] = mnew;
+      const float msub = (mnew == -INFINITY) ? 0.f : mnew;
+      float l = lpart[cb] * alpha[cb];
+      float p[16];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-        lsum *= alpha;
-        mrun = mnew;
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[cb][r], c, -msub));
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        pf[cb][m] = U4{pack_bf16(p[8 * m], p[8 * m + 1]), pack_bf16(p[8 * m + 2], p[8 * m + 3]),
+                       pack_bf16(p[8 * m + 4], p[8 * m + 5]), pack_bf16(p[8 * m + 6], p[8 * m + 7])};
+        l = dot2_ones(pf[cb][m].x, l);
+        l = dot2_ones(pf[cb][m].y, l);
+        l = dot2_ones(pf[cb][m].z, l);
+        l = dot2_ones(pf[cb][m].w, l);
       }
-      const float msub = (mrun == -INFINITY) ? 0.f : mrun;
-      U4 pf[kSub][2];
-#pragma unroll
-      for (int st = 0; st < kSub; ++st) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[st][r], c, -msub));
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-          pf[st][m] = U4{pack_bf16(p[8 * m], p[8 * m + 1]), pack_bf16(p[8 * m + 2], p[8 * m + 3]),
-                         pack_bf16(p[8 * m + 4], p[8 * m + 5]), pack_bf16(p[8 * m + 6], p[8 * m + 7])};
-      }
-      // O^T += V^T P^T ; l += 1 . P^T   (consecutive MFMAs hit different
-      // accumulators)
-#pragma unroll
-      for (int st = 0; st < kSub; ++st)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const U4 vf =
-                *reinterpret_cast<const U4*>(vl + (32 * dt + lc) * GE::VROW + (32 * st + 16 * m + 8 * hh) * 2);
-            o[dt] = mfma(vf, pf[st][m], o[dt]);
-          }
-          lsum = mfma(ones, pf[st][m], lsum);
-        }
+      lpart[cb] = l;
     }
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
+    resc = __any(any_need);
+  };
+
+  // O^T += V^T P^T for the tile in buffer `buf`; each V^T fragment feeds
+  // the two column blocks.  V^T fragments come from row-major V with
+  // ds_read_b64_tr_b16: in each group of 16 lanes, lane j reads 4 values of
+  // d at row j / 4 and receives, per element e, the value that lane
+  // 4e + i/4 read at position i % 4 (i = its own index in the group), so
+  // lane i ends with rows kb + 0..3 at one d.  Lane l of the A operand needs
+  // d = 32 dt + l % 32 and the 8 keys of its operand slots, 4h + 0..3 and
+  // 8 + 4h + 0..3 of the 16-key slab (h = l / 32): two reads.
+  const int tr_e = (lane & 15) >> 2, tr_q = lane & 3, tr_dh = (lane >> 4) & 1;
+  // One K fragment (A operand of the QK^T product, d chunk cc) and one V^T
+  // fragment (A operand of the PV product, key slab m, d tile dt).
+  auto k_frag = [&](const uint8_t* kl, int cc) -> U4 {
+    return *reinterpret_cast<const U4*>(kl + lc * GE::RB + ((2 * cc + hh) ^ GE::swz_k(lc)) * 16);
+  };
+  auto v_frag = [&](const uint8_t* vl, int m, int dt) -> U4 {
+    const int ch = 4 * dt + 2 * tr_dh + (tr_q >> 1);  // 16-byte chunk of d
+    s16x4 half[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 16 * m + 8 * u + 4 * hh + tr_e;
+      half[u] = read_tr16(vl + r * GE::RB + ((ch ^ GE::swz_v(r)) * 16) + 8 * (tr_q & 1));
+    }
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 h0 = __builtin_bit_cast(u32x2, half[0]), h1 = __builtin_bit_cast(u32x2, half[1]);
+    return U4{h0[0], h0[1], h1[0], h1[1]};
+  };
+  auto pv = [&](int buf, const U4 (&pf)[2][2], f32x16 (&o)[2][DT]) {
+    const uint8_t* vl = smem + buf * GE::BUF + GE::KBYTES;
+#pragma unroll
+    for (int f = 0; f < 2 * DT; ++f) {
+      const U4 vf = v_frag(vl, f / DT, f % DT);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) mfma_acc(o[cb][f % DT], vf, pf[cb][f / DT]);
+    }
+  };
+
+  auto rescale = [&](const float (&alpha)[2], f32x16 (&o)[2][DT]) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        acc_ready(o[cb][dt]);
+        o[cb][dt] *= alpha[cb];
+      }
+  };
+
+  // Step it: scores of tile it + 1, softmax of tile it and the PV product of
+  // tile it - 1.  Tile it + kAhead is loaded meanwhile and tile it + 2,
+  // loaded kAhead - 2 steps earlier, is published by the barrier that ends
+  // the step.  Buffers t % 8 hold tiles it - 1 .. it + kAhead.  Every wave
+  // runs the same number of steps (ntiles + 1), so the barriers match.
+  //
+  // Fast step (tiles 1 <= it < fast_end: no mask, a predecessor): the three
+  // parts are independent, so the step is written out as NS slots, each one
+  // MFMA (QK^T and PV alternating) followed by a share of the softmax on the
+  // vector ALU, with scheduling barriers between slots so that the matrix
+  // cores run while the vector ALU works.  It does not rescale o: when its
+  // softmax moves a running maximum the fast loop ends and the rescale runs
+  // before the next PV product.
+  constexpr int NQ = 2 * DK;      // QK^T MFMAs of a tile
+  constexpr int NP = 2 * 2 * DT;  // PV MFMAs of a tile
+  constexpr int NS = NQ + NP;     // slots
+  static_assert(NQ == NP, "QK^T and PV MFMAs alternate");
+  constexpr int kExpFrom = 5;     // first slot with exponentials
+  auto fast_step = [&](int it, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const U4 (&p_prev)[2][2],
+                       U4 (&p_cur)[2][2], float (&alpha)[2], bool& resc, f32x16 (&oa)[2][DT]) {
+    load_tile(it + kAhead, kAhead - 2);
+    const uint8_t* kl = smem + ((it + 1) % kBufs) * GE::BUF;
+    const uint8_t* vl = smem + ((it + kBufs - 1) % kBufs) * GE::BUF + GE::KBYTES;
+    U4 kf[DK], vf[2 * DT];
+    float tm[2], msub[2], l[2], p[2][16];
+    bool need[2];
+    kf[0] = k_frag(kl, 0);
+    vf[0] = v_frag(vl, 0, 0);
+    kf[1] = k_frag(kl, 1);
+    vf[1] = v_frag(vl, 1 / DT, 1 % DT);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      // fragments two groups ahead: K chunk cc is used by slots 4cc, 4cc + 2,
+      // V fragment f by slots 4f + 1, 4f + 3
+      if (k % 4 == 0 && k / 4 + 2 < DK) {
+        const int f = k / 4 + 2;
+        kf[f] = k_frag(kl, f);
+        vf[f] = v_frag(vl, f / DT, f % DT);
+      }
+      if (k % 2 == 0) {
+        const int q = k / 2, cc = q / 2, cb = q % 2;
+        U4 ka = kf[cc];
+        anchor(ka);  // issued in this slot, not earlier
+        s_nxt[cb] = mfma(ka, qf[cb][cc], cc == 0 ? f32x16{} : s_nxt[cb]);
+      } else {
+        const int q = k / 2, f = q / 2, cb = q % 2;
+        mfma_acc(oa[cb][f % DT], vf[f], p_prev[cb][f / DT]);
+      }
+      // vector share of the softmax of tile it
+      if (k < 4) {  // row maxima: a quarter of the scores per slot
+        const int cb = k / 2, r0 = 8 * (k % 2);
+        float s0 = s_cur[cb][r0];
+        anchor(s0);
+        float t = fmaxf(s0, s_cur[cb][r0 + 1]);
+#pragma unroll
+        for (int r = r0 + 2; r < r0 + 8; r += 2) t = fmaxf(t, fmaxf(s_cur[cb][r], s_cur[cb][r + 1]));
+        tm[cb] = (k % 2) ? fmaxf(tm[cb], t) : t;
+        settle(tm[cb]);
+      } else if (k == 4) {  // the lazily raised running maxima
+        bool any_need = false;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm[cb]), __float_as_uint(tm[cb]), false, false);
+          const float t = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+          need[cb] = t > mrun[cb] + kRescale;
+          const float mnew = need[cb] ? t : mrun[cb];
+          alpha[cb] = need[cb] ? exp2f(mrun[cb] - mnew) : 1.f;
+          any_need |= need[cb];  // a running maximum is finite here: tile 0 set it
+          mrun[cb] = mnew;
+          msub[cb] = (mnew == -INFINITY) ? 0.f : mnew;
+          l[cb] = lpart[cb] * alpha[cb];
+          settle(msub[cb]);
+        }
+        resc = __any(any_need);
+      }
+      // exponentials j = 0..31 (block j / 16, score j % 16) spread over the
+      // slots from kExpFrom; a pair is packed and summed with its second
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if (kExpFrom + (j * (NS - kExpFrom)) / 32 != k) continue;
+        const int cb = j / 16, r = j % 16;
+        float sv = s_cur[cb][r];
+        anchor(sv);  // computed in this slot, not earlier
+        p[cb][r] = __builtin_amdgcn_exp2f(fmaf(sv, c, -msub[cb]));
+        if (r % 2 == 1) {
+          const int m = r / 8, w = (r % 8) / 2;
+          const uint32_t pk = pack_bf16(p[cb][r - 1], p[cb][r]);
+          if (w == 0) p_cur[cb][m].x = pk;
+          if (w == 1) p_cur[cb][m].y = pk;
+          if (w == 2) p_cur[cb][m].z = pk;
+          if (w == 3) p_cur[cb][m].w = pk;
+          l[cb] = dot2_ones(pk, l[cb]);
+          settle(l[cb]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the softmax results are due here, not sunk past the wait below
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      settle(p_cur[cb][0]);
+      settle(p_cur[cb][1]);
+      settle(l[cb]);
+    }
+    lpart[0] = l[0];
+    lpart[1] = l[1];
+    finish_tile(it + 2, std::integral_constant<int, kAhead - 2>{});
     __syncthreads();
+  };
+  // General step: masked softmax, the parts this step has, and the rescale.
+  auto slow_step = [&](int it, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const U4 (&p_prev)[2][2],
+                       U4 (&p_cur)[2][2], f32x16 (&o)[2][DT]) {
+    load_tile(it + kAhead, kAhead - 2);
+    float alpha[2] = {1.f, 1.f};
+    bool resc = false;
+    if (it + 1 < wave_tiles) scores((it + 1) % kBufs, s_nxt);
+    if (it < wave_tiles) softmax(std::true_type{}, it * kKeys, it % kBufs, s_cur, p_cur, alpha, resc);
+    if (it >= 1 && it - 1 < wave_tiles) pv((it + kBufs - 1) % kBufs, p_prev, o);
+    finish_tile(it + 2, std::integral_constant<int, kAhead - 2>{});
+    if (resc) rescale(alpha, o);
+    __syncthreads();
+  };
+
+  // prologue: tiles 0 .. kAhead - 1 in flight, tiles 0 and 1 published,
+  // scores of tile 0
+#pragma unroll
+  for (int t = 0; t < kAhead; ++t) load_tile(t, t);
+  finish_tile(0, std::integral_constant<int, kAhead - 1>{});
+  finish_tile(1, std::integral_constant<int, kAhead - 2>{});
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  U4 pA[2][2], pB[2][2];
+  if (wave_tiles > 0) scores(0, sA);
+  slow_step(0, sA, sB, pA, pB, o);  // the first real tile never rescales (and has no PV)
+  // here sB holds the scores of tile 1 and pB the weights of tile 0
+  int it = 1;
+  bool resc = false;
+  float alpha[2] = {1.f, 1.f};
+  auto advance = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      sA[cb] = sB[cb];
+      pA[cb][0] = pB[cb][0];
+      pA[cb][1] = pB[cb][1];
+    }
+  };
+  advance();
+  // nothing the compiler tracks may be in flight in the fast loop: its waits
+  // would then also wait for the tile transfers
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int c = 0; c < DK; ++c) settle_acc(qf[cb][c]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  while (it < fast_end) {
+    fast_step(it, sA, sB, pA, pB, alpha, resc, o);
+    advance();
+    ++it;
+    if (resc) break;
+  }
+  if (resc) rescale(alpha, o);
+  for (; it <= ntiles; ++it) {
+    slow_step(it, sA, sB, pA, pB, o);
+    advance();
   }
 
   // ---- epilogue: O^T[d][q] / l[q] -> out[q][d]; rows >= q_len are 0 ----
-  if (tq < n_max) {
-    const float l = lsum[0];
-    const bool live = tq < qlen;
-    const float inv = (live && l > 0.f) ? 1.f / l : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+  for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        float4 w;
-        w.x = live ? o[dt][4 * rg] * inv : 0.f;
-        w.y = live ? o[dt][4 * rg + 1] * inv : 0.f;
-        w.z = live ? o[dt][4 * rg + 2] * inv : 0.f;
-        w.w = live ? o[dt][4 * rg + 3] * inv : 0.f;
-        *reinterpret_cast<float4*>(out_h + (int64_t)tq * D + 32 * dt + 8 * rg + 4 * hh) = w;
-      }
+    for (int dt = 0; dt < DT; ++dt) acc_ready(o[cb][dt]);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart[cb]), __float_as_uint(lpart[cb]), false, false);
+    const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (tq[cb] < n_max) {
+      float* out_h = a.out + ((int64_t)b * a.num_q_heads + hb[cb]) * n_max * D;
+      const bool live = tq[cb] < qlen;
+      const float inv = (live && l > 0.f) ? 1.f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          float4 w;
+          w.x = live ? o[cb][dt][4 * rg] * inv : 0.f;
+          w.y = live ? o[cb][dt][4 * rg + 1] * inv : 0.f;
+          w.z = live ? o[cb][dt][4 * rg + 2] * inv : 0.f;
+          w.w = live ? o[cb][dt][4 * rg + 3] * inv : 0.f;
+          *reinterpret_cast<float4*>(out_h + (int64_t)tq[cb] * D + 32 * dt + 8 * rg + 4 * hh) = w;
+        }
+    }
   }
 }
 
 template <int D, bool CAUSAL, bool MASK>
 int launch_typed(const PrefillLaunch& a, hipStream_t s) {
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int hw = G < 4 ? G : 4;
-  const int rows = kWaveQ * (4 / hw);
-  const dim3 grid((a.n_max + rows - 1) / rows, a.num_q_heads / hw, a.batch);
-  const size_t lds = 2 * Geo<D>::BUF;
+  const int hw = G < kBlocks ? G : kBlocks;
+  const int rows = 32 * kBlocks / hw;
+  const dim3 grid(a.num_q_heads / hw, (a.n_max + rows - 1) / rows, a.batch);
+  const size_t lds = kBufs * Geo<D>::BUF;
   hipLaunchKernelGGL((prefill_mfma_kernel<D, CAUSAL, MASK>), grid, dim3(kThreads), lds, s, a, hw);
   return hipGetLastError() == hipSuccess ? KVATTN_OK : KVATTN_ELAUNCH;
 }
@@ -352,6 +720,7 @@ bool prefill_mfma_supports(const PrefillLaunch& a) {
   if (a.dtype != KVATTN_BF16) return false;
   if (a.head_dim != 64 && a.head_dim != 128) return false;
   if (a.has_cache && a.attend_prefix) return false;  // cached prefix: general kernel
+  if ((int64_t)a.n_max * a.head_dim * 2 >= ((int64_t)1 << 31) - 4096) return false;  // 32-bit buffer offsets
   const int G = a.num_q_heads / a.num_kv_heads;
   return G == 1 || G == 2 || G == 4 || G == 8;
 }
