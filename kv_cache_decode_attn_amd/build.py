@@ -31,11 +31,15 @@ COMMON = [
 ]
 
 
-# Per-file extra flags.  The MFMA prefill kernel takes maxima of raw matrix
-# results; without NaN-preserving semantics the compiler drops one quieting
-# instruction per score.  NaN can only reach that kernel through padding
-# query rows (whose outputs are written as zeros) and masked keys (whose
-# scores are replaced by -inf before any maximum), so no result changes.
+# Per-file extra flags for the MFMA prefill kernel:
+#  - it takes maxima of raw matrix results; without NaN-preserving semantics
+#    the compiler drops one quieting instruction per score.  NaN can only
+#    reach that kernel through padding query rows (whose outputs are written
+#    as zeros) and masked keys (whose scores are replaced by -inf before any
+#    maximum), so no result changes;
+#  - its matrix results live in vector registers (the scores are read by the
+#    softmax right away), which keeps its register allocation free of copies
+#    between the two register files.
 EXTRA = {"prefill_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

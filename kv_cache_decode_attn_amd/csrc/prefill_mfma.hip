@@ -11,39 +11,48 @@
 // Prefill is compute bound ("KV Cache" (heepie.pages.dev), section "Prefill
 // and Decode"), so both products run on the matrix cores.
 //
-// Budget on gfx950 per compute unit: the 32x32x16 bf16 MFMA of one SIMD
-// needs 1 KB of operand from LDS per instruction if only one of its operands
-// lives in registers, which is all of the LDS read bandwidth (128 B/clock)
-// at the full matrix rate.  So every K and V^T fragment read from LDS here
-// feeds two MFMAs: a wave owns 64 query columns (two 32-column blocks) and
-// keeps their Q fragments in registers.  That needs about 400 registers,
-// i.e. one wave per SIMD, so the wave overlaps its own matrix and vector
-// work: the QK^T products of tile t+1 are issued while the softmax of tile t
-// runs on the vector ALU, and the global loads of tile t+2 fly meanwhile.
+// Budget on gfx950 per compute unit (measured): the matrix cores reach
+// ~1.9 PFLOP/s on back-to-back 32x32x16 bf16 MFMAs, the LDS serves ~256
+// bytes per clock for 16-byte reads, and exp2 issues at a quarter of the
+// vector rate.  A wave owns 64 query columns (two 32-column blocks) so that
+// every K and V^T fragment read from LDS feeds two MFMAs; with Q, the
+// accumulators and two steps of scores in registers that is one wave per
+// SIMD, so each wave overlaps its own matrix and vector work (below).
 //
 // Work split.  A workgroup of 4 waves owns HW = min(G, 8) query heads of one
 // KV head and 256 / HW query rows, cut into eight 32-row column blocks, two
-// per wave.  The heads of a GQA group share the K/V tiles staged in LDS
-// (three buffers: tile t+1 is read for QK^T while tile t is read for PV and
-// tile t+2 is written).  The KV head is the fastest grid dimension, so with
-// 8 KV heads every XCD (and its L2) serves one KV head; causal query tiles
-// are issued heaviest first.
+// per wave.  The heads of a GQA group share the K/V tiles staged in LDS.
+// The KV head is the fastest grid dimension, so with 8 KV heads every XCD
+// (and its L2) serves one KV head; causal query tiles are issued heaviest
+// first.
 //
-// Per 64-key tile and column block (h = lane / 32):
+// Staging.  32-key tiles of K and V go from global memory straight into an
+// 8-tile LDS ring (buffer loads that write LDS), 5 tiles ahead of the one
+// being scored; each wave waits only for its own transfers of the tile it
+// publishes, and one barrier per step publishes it.  V stays row-major in
+// LDS and its MFMA operand is read with the transposing LDS read.
+//
+// Pipeline.  Step t runs the QK^T product of tile t+1, the softmax of tile
+// t and the PV product of tile t-1.  Away from the causal diagonal and the
+// sequence end, the three parts are independent and the step is written
+// out as 32 slots of one MFMA (QK^T and PV alternating) plus a share of
+// the softmax, so the vector ALU works while the matrix cores run.
+//
+// Per 32-key tile and column block (h = lane / 32):
 //   S^T[key][q] = K Q^T      A = K rows from LDS, B = Q (registers), fp32
 //                            accumulate.  The 32x32 accumulator gives lane l
 //                            query column l % 32 and keys 8*(r/4) + 4h + r%4
-//                            (r = 0..15) of each 32-key half: a query's
-//                            scores sit in two lanes, so the row max is a
-//                            local max plus one cross-half swap, and P^T is
-//                            already the B operand of the second product.
+//                            (r = 0..15): a query's scores sit in two lanes,
+//                            so the row max is a local max plus one
+//                            cross-half swap, and P^T is already the B
+//                            operand of the second product.
 //   P = exp2(S*c - m)        c = scale*log2(e); m is a per-query running
 //                            maximum that is only raised (with rescaling of
 //                            the accumulators) when the tile maximum exceeds
-//                            it by more than 8, so P <= 2^8; P rounded to bf16.
-//   O^T[d][q] += V^T P^T     A = V^T from LDS.  V is transposed while it is
-//                            staged into LDS; inside a V^T row the keys are
-//                            ordered like P^T's operand slots.
+//                            it by more than 64, so P <= 2^64; P rounded to
+//                            bf16.
+//   O^T[d][q] += V^T P^T     A = V^T, read from row-major V in LDS so that
+//                            its operand slots hold the keys in P^T's order.
 //   l[q] += P . 1            bf16 dot products of the rounded weights, so the
 //                            row sum is the sum of the same weights used for O.
 // Masked keys (causal, beyond q_len, key_mask) get P = 0 and their V rows are
@@ -86,33 +95,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// The PV MFMAs are written as inline assembly so that the 128 O^T
-// accumulator registers of a wave stay in the accumulation register file,
-// out of the vector register file that holds the scores, weights and
-// operands; the accumulators are only ever touched by these instructions
-// and by acc_ready()-guarded code.  The compiler does not model this
-// instruction, so the code around it provides what it needs: two wait
-// states after a vector write of an operand (the s_nop 1), none between
-// back-to-back accumulations into the same registers, and acc_ready()
-// before any other access to the accumulators.
+// Empty inline-assembly statements (they emit no instruction) that pin the
+// place of a computation in the instruction stream: the fast loop below is
+// written slot by slot, and without them the compiler would gather all
+// vector work of a step in one place (or sink it past the loop's wait),
+// which leaves the matrix cores idle meanwhile.
 //
-// acc += a * b, acc in accumulation registers.
-__device__ __forceinline__ void mfma_acc(f32x16& acc, const U4& a, const U4& b) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-               : "+a"(acc)
-               : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b)));
-#endif
-}
-// Wait states before acc, last written by mfma_acc, is read or written by
-// anything else (the matrix result latency of a 32x32x16 MFMA).
-__device__ __forceinline__ void acc_ready(f32x16& acc) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
-#endif
-}
-
 // An empty statement that needs x in accumulation registers.
 __device__ __forceinline__ void settle_acc(const U4& x) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -489,7 +477,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     for (int f = 0; f < 2 * DT; ++f) {
       const U4 vf = v_frag(vl, f / DT, f % DT);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) mfma_acc(o[cb][f % DT], vf, pf[cb][f / DT]);
+      for (int cb = 0; cb < 2; ++cb) o[cb][f % DT] = mfma(vf, pf[cb][f / DT], o[cb][f % DT]);
     }
   };
 
@@ -497,10 +485,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        acc_ready(o[cb][dt]);
-        o[cb][dt] *= alpha[cb];
-      }
+      for (int dt = 0; dt < DT; ++dt) o[cb][dt] *= alpha[cb];
   };
 
   // Step it: scores of tile it + 1, softmax of tile it and the PV product of
@@ -549,7 +534,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
         s_nxt[cb] = mfma(ka, qf[cb][cc], cc == 0 ? f32x16{} : s_nxt[cb]);
       } else {
         const int q = k / 2, f = q / 2, cb = q % 2;
-        mfma_acc(oa[cb][f % DT], vf[f], p_prev[cb][f / DT]);
+        oa[cb][f % DT] = mfma(vf[f], p_prev[cb][f / DT], oa[cb][f % DT]);
       }
       // vector share of the softmax of tile it
       if (k < 4) {  // row maxima: a quarter of the scores per slot
@@ -670,10 +655,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   }
 
   // ---- epilogue: O^T[d][q] / l[q] -> out[q][d]; rows >= q_len are 0 ----
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc_ready(o[cb][dt]);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart[cb]), __float_as_uint(lpart[cb]), false, false);
