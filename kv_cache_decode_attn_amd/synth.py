@@ -83,3 +83,17 @@ def random_mask(shape, keep, seed):
 def fp8_scales(n, seed, lo=0.5, hi=2.0):
     """Per-head fp32 dequantisation scales drawn from U[lo, hi]."""
     return rng(*seed).uniform(lo, hi, size=n).astype(np.float32)
+
+
+def chat_lengths(n, seed, max_len=4096, prefix=0, prompt_median=256.0, output_median=200.0, sigma=1.0):
+    """Prompt and completion lengths (int64 [n] each) of n synthetic chat
+    completions: log-normal lengths with the given medians and log-space
+    sigma, rounded, then clipped so that every prompt holds the shared
+    prefix plus at least one token, every completion has at least one
+    token, and prompt + completion <= max_len."""
+    r = rng(*seed)
+    p = np.rint(prompt_median * np.exp(sigma * r.standard_normal(n))).astype(np.int64)
+    o = np.rint(output_median * np.exp(sigma * r.standard_normal(n))).astype(np.int64)
+    p = np.clip(p, prefix + 1, max_len - 1)
+    o = np.clip(o, 1, max_len - p)
+    return p, o

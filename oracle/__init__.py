@@ -23,9 +23,13 @@ Modules:
   cache      - logical KV cache with the append contract, physical pool
                prediction for contiguous / 16-token paged layouts, byte
                closed forms, op counts
+  paging     - block-table batch/beam reorder, block copies, a reference
+               block pool (free list, reference counts, copy-on-write) and
+               the contiguous vs paged reserved-memory closed forms
 
-Every function is pinned by tests/test_oracle_pins.py against values the
+Every function is pinned by tests/test_oracle_pins.py and
+tests/test_oracle_paging.py against values the
 pages print, closed forms, library routines or brute force.  Parity pinned
 everywhere; no function here is "parity unpinned".
 """
-from . import codec, attention, cache  # noqa: F401
+from . import codec, attention, cache, paging  # noqa: F401
