@@ -14,8 +14,9 @@ HBM bytes per step / step time, in GB/s.  The same step as two calls
 Other workloads run in the same invocation and are reported under
 "workloads": the padded 32-layer MHA decode (batch 8, 4096-position
 contiguous cache, key padding mask), the 80-layer fp8 long-context decode
-(batch 1, 64/8 heads, 131,073 keys per layer) and the causal 8192-token
-prefill that writes the paged cache.
+(batch 1, 64/8 heads, 131,073 keys per layer), the causal 8192-token
+prefill that writes the paged cache, a copy-on-write fan-out of 4096 paged
+blocks and a contiguous beam reorder (32 rows of 4096 positions).
 
 Timing: W untimed warm-up steps, then K steps bracketed by synchronize +
 HIP events on the stream the library launches on (torch's current stream).
@@ -335,6 +336,78 @@ class CausalPrefill:
                 "head_dim": self.D, "dtype": "bf16", "causal": True, "writes_paged_cache": True}
 
 
+class CowBlockCopy:
+    """Copy-on-write fan-out: 4096 whole-block copies in a Llama-3-8B-shaped
+    bf16 paged pool (8 KV heads x 16 positions x 128 = 32 KiB per block per
+    pool), K and V, one kvattn_copy_blocks launch per step."""
+
+    name = "cow-block-copy-4096-llama3-8b"
+
+    def __init__(self, wid=6, replicas=4):
+        self.nblk, self.n, self.Hkv, self.D = 16384, 4096, 8, 128
+        self.caches, self.src, self.dst = [], [], []
+        for r in range(replicas):
+            c = K.KVCache.paged(self.nblk, self.Hkv, self.D, K.BF16, DEV)
+            synth.normal_device(c.k.shape, (wid, synth.T_K, r), out=c.k)
+            synth.normal_device(c.v.shape, (wid, synth.T_V, r), out=c.v)
+            perm = synth.rng(wid, synth.T_PERM, r).permutation(self.nblk).astype(np.int32)
+            self.caches.append(c)
+            self.src.append(torch.from_numpy(perm[:self.n].copy()).to(DEV))
+            self.dst.append(torch.from_numpy(perm[self.n:2 * self.n].copy()).to(DEV))
+        torch.cuda.synchronize()
+
+    def step_bytes(self):
+        block = self.Hkv * 16 * self.D * 2
+        return 2 * 2 * self.n * block + 8 * self.n  # K and V, read + write, plus the id pairs
+
+    def step(self, i, ev=None):
+        r = i % len(self.caches)
+        K.copy_blocks(self.caches[r], self.src[r], self.dst[r])
+
+    def config(self):
+        return {"workload": self.name, "pairs": self.n, "pool_blocks": self.nblk, "kv_heads": self.Hkv,
+                "head_dim": self.D, "kv_dtype": "bf16", "block_bytes_per_pool": self.Hkv * 16 * self.D * 2}
+
+
+class BeamReorder:
+    """Beam reorder of a contiguous Llama-3-8B-shaped bf16 cache layer: 32
+    rows (8 prompts x 4 beams, each beam's parent drawn from its prompt's
+    beams), 8 KV heads, capacity 4096, d 128, lengths U[1024, 4096]; one
+    kvattn_reorder_cache launch per step copies each row's stored
+    positions."""
+
+    name = "beam-reorder-contiguous-32x4096-llama3-8b"
+
+    def __init__(self, wid=7, replicas=3):
+        self.rows, self.Hkv, self.cap, self.D = 32, 8, 4096, 128
+        self.lens_np = synth.uniform_lengths(self.rows, 1024, self.cap, (wid, synth.T_LENS))
+        r = synth.rng(wid, synth.T_PERM)
+        self.perm_np = np.concatenate([4 * p + r.integers(0, 4, size=4) for p in range(8)]).astype(np.int32)
+        self.lens = torch.from_numpy(self.lens_np).to(DEV)
+        self.perm = torch.from_numpy(self.perm_np).to(DEV)
+        self.out_lens = torch.empty(self.rows, dtype=torch.int32, device=DEV)
+        self.pairs = []
+        for k in range(replicas):
+            s = K.KVCache.contiguous(self.rows, self.Hkv, self.cap, self.D, K.BF16, DEV)
+            d = K.KVCache.contiguous(self.rows, self.Hkv, self.cap, self.D, K.BF16, DEV)
+            synth.normal_device(s.k.shape, (wid, synth.T_K, k), out=s.k)
+            synth.normal_device(s.v.shape, (wid, synth.T_V, k), out=s.v)
+            self.pairs.append((s, d))
+        torch.cuda.synchronize()
+
+    def step_bytes(self):
+        moved = int(np.minimum(self.lens_np[self.perm_np], self.cap).sum())
+        return 2 * 2 * moved * self.Hkv * self.D * 2 + 4 * 3 * self.rows  # K and V, read + write; perm, lengths
+
+    def step(self, i, ev=None):
+        s, d = self.pairs[i % len(self.pairs)]
+        K.reorder_cache(s, d, self.perm, self.lens, self.out_lens)
+
+    def config(self):
+        return {"workload": self.name, "rows": self.rows, "kv_heads": self.Hkv, "capacity": self.cap,
+                "head_dim": self.D, "kv_dtype": "bf16", "lengths": "U[1024,4096]", "beams_per_prompt": 4}
+
+
 def time_steps(w, steps, warmup, per_launch=False):
     for i in range(warmup):
         w.step(i)
@@ -359,8 +432,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode8b,padded32,longctx70b,prefill8k",
-                    help="comma list: decode8b (headline), padded32, longctx70b, prefill8k")
+    ap.add_argument("--workloads", default="decode8b,padded32,longctx70b,prefill8k,cowcopy,beamreorder",
+                    help="comma list: decode8b (headline), padded32, longctx70b, prefill8k, cowcopy, beamreorder")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the headline workload the oracle runs")
     args = ap.parse_args(argv)
@@ -445,6 +518,17 @@ def main(argv=None):
                                            "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                            "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
         del pf
+        torch.cuda.empty_cache()
+    for key, cls_ in (("cowcopy", CowBlockCopy), ("beamreorder", BeamReorder)):
+        if key not in names:
+            continue
+        cw = cls_()
+        msc, _ = time_steps(cw, max(10, args.steps), args.warmup)
+        gbs = cw.step_bytes() / (msc * 1e-3) / 1e9
+        extra[key] = {"config": cw.config(), "ms_per_launch": msc, "GB/s": gbs, "bytes_per_launch": cw.step_bytes(),
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+        del cw
         torch.cuda.empty_cache()
     if extra:
         line["workloads"] = extra

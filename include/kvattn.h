@@ -13,7 +13,9 @@
  * kvattn_attn_decode_append (both in one launch sequence: the decode step)
  * and kvattn_attn_prefill (many new tokens, causal/padding masked,
  * optionally writing the cache).  Plus sizing, validation and status
- * helpers.
+ * helpers, and the block-table operations of a paged cache: batch/beam
+ * reorder, copy-on-write block copies and a host block pool with reference
+ * counts.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -64,7 +66,8 @@ typedef enum kvattn_status {
   KVATTN_EINVAL = -1,       /* null pointer, bad size, bad enum, misalignment */
   KVATTN_EUNSUPPORTED = -2, /* valid request this build has no kernel for   */
   KVATTN_EWORKSPACE = -3,   /* decode workspace missing or too small        */
-  KVATTN_ELAUNCH = -4       /* the HIP runtime refused a kernel launch      */
+  KVATTN_ELAUNCH = -4,      /* the HIP runtime refused a kernel launch      */
+  KVATTN_ENOSPACE = -5      /* a block pool has too few free blocks         */
 } kvattn_status;
 
 typedef enum kvattn_dtype {
@@ -304,6 +307,178 @@ int kvattn_validate(const kvattn_cache* cache, int32_t batch,
                     const int32_t* positions,
                     const int32_t* block_table, int32_t max_blocks,
                     int32_t* err_word, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Cache reorder and sharing.
+ *
+ * A paged cache moves and shares whole 16-token blocks by editing block
+ * tables; only a write into a shared block needs a byte copy first
+ * (copy-on-write).  "KV Cache, Flash Attention and Inference Optimization",
+ * section "PagedAttention": the page table maps logical positions to
+ * physical blocks, which lets beam-search and parallel-sampling branches
+ * share KV and frees the cache from fragmentation; "KV Cache Fully
+ * Explained", section "(4) PagedAttention": requests with a common prefix
+ * point at the same physical blocks (copy-on-write).
+ * ------------------------------------------------------------------------- */
+
+/* kvattn_reorder_rows - batch/beam reorder of a paged cache.
+ *
+ * When the batch or beam order changes, every cache row must follow the
+ * same permutation ("Transformer Attention Masks and KV-Cache Inference",
+ * section "Batch and beam reorder": [A0, A1, B0] sorted to [B0, A1, A0] is
+ * the permutation [2, 1, 0]).  With a block table a row is its table row
+ * and its length, so only ids move:
+ *   dst_table[i * max_blocks + j] = src_table[perm[i] * max_blocks + j]
+ *   dst_lens[i]                   = src_lens[perm[i]]
+ * A perm entry outside [0, src_rows) gives an empty row (all -1, length 0).
+ * A perm with repeats leaves rows naming the same blocks: they are then
+ * shared, and the host pool's references must follow (kvattn_pool_reorder
+ * computes the same rows on the host and moves the references).
+ *
+ *  n_rows     rows of the result (0 <= n_rows <= 65535; 0 is a no-op)
+ *  perm       device int32 [n_rows]
+ *  src_rows   rows of src_table / src_lens (>= 0)
+ *  src_table  device int32 [src_rows, max_blocks]
+ *  src_lens   device int32 [src_rows], or NULL together with dst_lens
+ *  max_blocks entries per table row, >= 1
+ *  dst_table  device int32 [n_rows, max_blocks]; must not overlap src_table
+ *  dst_lens   device int32 [n_rows] or NULL; must not overlap src_lens
+ * Errors: KVATTN_EINVAL for a NULL required pointer or a size out of range. */
+int kvattn_reorder_rows(int32_t n_rows, const int32_t* perm, int32_t src_rows,
+                        const int32_t* src_table, const int32_t* src_lens,
+                        int32_t max_blocks, int32_t* dst_table,
+                        int32_t* dst_lens, void* stream);
+
+/* kvattn_reorder_cache - batch/beam reorder of a contiguous cache: the rows
+ * of `src` gathered into `dst` with the beam permutation ("Transformer
+ * Attention Masks and KV-Cache Inference", section "Batch and beam
+ * reorder"), for K and V and every KV head:
+ *   dst[i, g, p, :] = src[perm[i], g, p, :]   for p < L,
+ *   L = min(src_lens[perm[i]], capacity), or capacity when src_lens is NULL.
+ * Positions >= L of dst row i keep their bytes.  A perm entry outside
+ * [0, src->num_rows) leaves dst row i untouched.  dst_lens[i] =
+ * src_lens[perm[i]] (0 for an out-of-range entry) when both are given.  The
+ * bytes are copied as stored: fp8 codes stay codes, so dst is read with
+ * src's scales (the scale pointers of both descriptors are not used here).
+ *
+ *  src, dst   contiguous caches with equal dtype, num_kv_heads, head_dim and
+ *             capacity; dst->num_rows >= n_rows; their k/v memory must not
+ *             overlap (the reorder is out of place)
+ *  n_rows     0 <= n_rows <= 65535
+ *  perm       device int32 [n_rows]
+ *  src_lens   device int32 [src->num_rows] or NULL
+ *  dst_lens   device int32 [n_rows] or NULL (needs src_lens); must not
+ *             overlap src_lens
+ * Errors: KVATTN_EINVAL (NULL pointer, mismatched caches, paged layout,
+ * sizes). */
+int kvattn_reorder_cache(const kvattn_cache* src, const kvattn_cache* dst,
+                         int32_t n_rows, const int32_t* perm,
+                         const int32_t* src_lens, int32_t* dst_lens,
+                         void* stream);
+
+/* kvattn_copy_blocks - copy whole physical blocks of a paged cache, the
+ * copy half of copy-on-write ("KV Cache Fully Explained", section
+ * "(4) PagedAttention": shared prefix blocks are copied before a holder
+ * writes into them).  For every pair i, in the K pool and in the V pool:
+ *   pool[dst_blocks[i], :, :, :] = pool[src_blocks[i], :, :, :]
+ * (all KV heads, all 16 positions).  A pair with an id outside
+ * [0, cache->num_blocks) is skipped.  The destinations must be distinct and
+ * none may also be a source in the same call, so that the order of the
+ * copies cannot matter; the pairs kvattn_pool_prepare_append returns meet
+ * this.
+ *
+ *  cache                   paged cache (any dtype; bytes are copied)
+ *  n                       pairs, 0 <= n <= 2^24 (0 is a no-op)
+ *  src_blocks, dst_blocks  device int32 [n]
+ * Errors: KVATTN_EINVAL (NULL pointer, contiguous layout, n out of range). */
+int kvattn_copy_blocks(const kvattn_cache* cache, int32_t n,
+                       const int32_t* src_blocks, const int32_t* dst_blocks,
+                       void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block pool.
+ *
+ * The free list of a paged cache's physical blocks with a reference count
+ * per block: "KV Cache, Flash Attention and Inference Optimization",
+ * section "Exercises" (a toy PagedAttention with fixed 16-token blocks and
+ * a free list; a finished sequence returns its blocks to the pool), with the
+ * sharing of section "PagedAttention" and the copy-on-write prefix sharing
+ * of "KV Cache Fully Explained", section "(4) PagedAttention".
+ *
+ * Host memory only: the block tables passed to these calls are host int32
+ * arrays [rows, max_blocks] (-1 = no block) that the caller uploads for
+ * the device calls.  A row of length L uses its first ceil(L / 16) entries.
+ * A block's reference count is the number of table rows that name it; the
+ * block is free at 0, and the free list hands out the lowest free id first.
+ * Every call is all-or-nothing: on error neither the pool nor the caller's
+ * arrays change.  Calls on one pool are serialised by a lock inside it.
+ * ------------------------------------------------------------------------- */
+typedef struct kvattn_pool kvattn_pool;
+
+/* A pool of num_blocks free blocks (1 <= num_blocks <= 2^31 - 1), or NULL
+ * with kvattn_last_error() set.  The caller destroys it. */
+kvattn_pool* kvattn_pool_create(int64_t num_blocks);
+void kvattn_pool_destroy(kvattn_pool* pool);
+int64_t kvattn_pool_num_blocks(const kvattn_pool* pool);
+int64_t kvattn_pool_num_free(const kvattn_pool* pool);
+/* Reference count of one block; -1 for an id outside the pool. */
+int32_t kvattn_pool_refcount(const kvattn_pool* pool, int32_t block);
+
+/* Take n free blocks (count 1 each) into ids[n], lowest ids first.
+ * KVATTN_ENOSPACE if fewer than n are free. */
+int kvattn_pool_alloc(kvattn_pool* pool, int32_t n, int32_t* ids);
+/* Add one reference to each listed block (all must be allocated). */
+int kvattn_pool_retain(kvattn_pool* pool, int32_t n, const int32_t* ids);
+/* Drop one reference per listing; a block reaching 0 returns to the free
+ * list.  KVATTN_EINVAL if a block is listed more often than it is held. */
+int kvattn_pool_release(kvattn_pool* pool, int32_t n, const int32_t* ids);
+
+/* Share a prefix: dst_row names the first ceil(length / 16) blocks of
+ * src_row (one more reference each) and -1 after them.  For a new beam or
+ * sample branch, or a request that reuses a cached prefix. */
+int kvattn_pool_fork(kvattn_pool* pool, const int32_t* src_row,
+                     int32_t* dst_row, int32_t max_blocks, int32_t length);
+
+/* A sequence of `length` positions ends: its blocks lose one reference each
+ * and its row becomes -1. */
+int kvattn_pool_free_seq(kvattn_pool* pool, int32_t* row, int32_t max_blocks,
+                         int32_t length);
+
+/* Make positions cur_lens[b] .. new_lens[b] - 1 of every row writable,
+ * rows in order, before kvattn_kv_append / kvattn_attn_decode_append write
+ * them:
+ *  - if cur_lens[b] % 16 != 0 and new_lens[b] > cur_lens[b], the partly
+ *    filled block at entry cur_lens[b] / 16 is written; if another row also
+ *    holds it, the row gets a fresh block instead, the pair (old, fresh) is
+ *    appended to copy_src / copy_dst, and the old block loses this row's
+ *    reference (copy-on-write: run kvattn_copy_blocks on the pairs before
+ *    the write);
+ *  - entries ceil(cur_lens[b] / 16) .. ceil(new_lens[b] / 16) - 1 get fresh
+ *    blocks.
+ *  tables      host int32 [rows, max_blocks], updated in place
+ *  cur_lens    host int32 [rows]: positions already stored
+ *  new_lens    host int32 [rows]: positions stored after the write,
+ *              cur_lens[b] <= new_lens[b] <= 16 * max_blocks
+ *  copy_src, copy_dst  host int32 [rows] (at most one pair per row)
+ *  n_copies    host: number of pairs written
+ * KVATTN_ENOSPACE if the pool runs out (nothing changes). */
+int kvattn_pool_prepare_append(kvattn_pool* pool, int32_t rows, int32_t* tables,
+                               int32_t max_blocks, const int32_t* cur_lens,
+                               const int32_t* new_lens, int32_t* copy_src,
+                               int32_t* copy_dst, int32_t* n_copies);
+
+/* Host side of kvattn_reorder_rows: the same dst rows and lengths, with the
+ * references moved along (each dst row adds one reference to the blocks it
+ * names, then every src row drops its own; rows no longer named return
+ * their blocks to the free list, rows named twice share them).
+ *  perm        host int32 [n_rows]
+ *  src_tables  host int32 [src_rows, max_blocks]; src_lens host int32 [src_rows]
+ *  dst_tables  host int32 [n_rows, max_blocks], must not overlap src_tables;
+ *  dst_lens    host int32 [n_rows] */
+int kvattn_pool_reorder(kvattn_pool* pool, int32_t n_rows, const int32_t* perm,
+                        int32_t src_rows, const int32_t* src_tables,
+                        const int32_t* src_lens, int32_t max_blocks,
+                        int32_t* dst_tables, int32_t* dst_lens);
 
 #ifdef __cplusplus
 }

@@ -7,7 +7,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 # built for a performance experiment); the default is the in-tree build.
 LIB_PATH = os.environ.get("KVATTN_LIB") or os.path.join(_PKG, "libkvattn.so")
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH, ENOSPACE = 0, -1, -2, -3, -4, -5
 F32, BF16, FP8_E4M3 = 0, 1, 2
 CONTIGUOUS, PAGED = 0, 1
 BLOCK_TOKENS = 16
@@ -18,6 +18,10 @@ EXPORTS = (
     "kvattn_version", "kvattn_status_string", "kvattn_last_error", "kvattn_cache_bytes",
     "kvattn_kv_append", "kvattn_decode_workspace_bytes", "kvattn_decode_default_part_tokens",
     "kvattn_attn_decode", "kvattn_attn_decode_append", "kvattn_attn_prefill", "kvattn_validate",
+    "kvattn_reorder_rows", "kvattn_reorder_cache", "kvattn_copy_blocks",
+    "kvattn_pool_create", "kvattn_pool_destroy", "kvattn_pool_num_blocks", "kvattn_pool_num_free",
+    "kvattn_pool_refcount", "kvattn_pool_alloc", "kvattn_pool_retain", "kvattn_pool_release", "kvattn_pool_fork",
+    "kvattn_pool_free_seq", "kvattn_pool_prepare_append", "kvattn_pool_reorder",
 )
 
 
@@ -68,6 +72,21 @@ _SIGS = {
     "kvattn_attn_prefill": (ctypes.c_int, [_CP, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P,
                                            _P, _I32, _P, _I64, _I32, _I32, _F, _P, _P]),
     "kvattn_validate": (ctypes.c_int, [_CP, _I32, _P, _I32, _P, _P, _I32, _P, _P]),
+    "kvattn_reorder_rows": (ctypes.c_int, [_I32, _P, _I32, _P, _P, _I32, _P, _P, _P]),
+    "kvattn_reorder_cache": (ctypes.c_int, [_CP, _CP, _I32, _P, _P, _P, _P]),
+    "kvattn_copy_blocks": (ctypes.c_int, [_CP, _I32, _P, _P, _P]),
+    "kvattn_pool_create": (_P, [_I64]),
+    "kvattn_pool_destroy": (None, [_P]),
+    "kvattn_pool_num_blocks": (_I64, [_P]),
+    "kvattn_pool_num_free": (_I64, [_P]),
+    "kvattn_pool_refcount": (_I32, [_P, _I32]),
+    "kvattn_pool_alloc": (ctypes.c_int, [_P, _I32, _P]),
+    "kvattn_pool_retain": (ctypes.c_int, [_P, _I32, _P]),
+    "kvattn_pool_release": (ctypes.c_int, [_P, _I32, _P]),
+    "kvattn_pool_fork": (ctypes.c_int, [_P, _P, _P, _I32, _I32]),
+    "kvattn_pool_free_seq": (ctypes.c_int, [_P, _P, _I32, _I32]),
+    "kvattn_pool_prepare_append": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
+    "kvattn_pool_reorder": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P, _I32, _P, _P]),
 }
 
 

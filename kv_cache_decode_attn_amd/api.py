@@ -9,6 +9,7 @@ no fallback: without the built library or on CPU tensors these raise.
 import ctypes
 import math
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -266,3 +267,131 @@ def validate(cache, seq_lens, max_seq_len, positions=None, block_table=None):
     check(lib().kvattn_validate(ctypes.byref(cache.desc()), seq_lens.shape[0], _ptr(seq_lens), int(max_seq_len),
                                 _ptr(positions), _ptr(block_table), mb, _ptr(err), _stream(seq_lens.device)))
     return int(err.item())
+
+
+# ------------------------------------------------ cache reorder and sharing ---
+
+def reorder_rows(perm, src_table, src_lens=None, dst_table=None, dst_lens=None):
+    """Batch/beam reorder of a paged cache's block table (kvattn_reorder_rows):
+    row i of the result is row perm[i].  Device int32 tensors; returns
+    (dst_table, dst_lens or None)."""
+    _i32(perm, "perm")
+    _i32(src_table, "src_table")
+    _i32(src_lens, "src_lens")
+    n = perm.shape[0]
+    rows, mb = src_table.shape
+    if dst_table is None:
+        dst_table = torch.empty((n, mb), dtype=torch.int32, device=src_table.device)
+    if src_lens is not None and dst_lens is None:
+        dst_lens = torch.empty(n, dtype=torch.int32, device=src_table.device)
+    _i32(dst_table, "dst_table")
+    _i32(dst_lens, "dst_lens")
+    check(lib().kvattn_reorder_rows(n, _ptr(perm), rows, _ptr(src_table), _ptr(src_lens), mb, _ptr(dst_table),
+                                    _ptr(dst_lens), _stream(src_table.device)))
+    return dst_table, dst_lens
+
+
+def reorder_cache(src, dst, perm, src_lens=None, dst_lens=None):
+    """Batch/beam reorder of a contiguous cache (kvattn_reorder_cache): dst
+    row i receives the first src_lens[perm[i]] positions (all, without
+    src_lens) of src row perm[i].  Returns dst_lens (or None)."""
+    _i32(perm, "perm")
+    _i32(src_lens, "src_lens")
+    _i32(dst_lens, "dst_lens")
+    check(lib().kvattn_reorder_cache(ctypes.byref(src.desc()), ctypes.byref(dst.desc()), perm.shape[0], _ptr(perm),
+                                     _ptr(src_lens), _ptr(dst_lens), _stream(perm.device)))
+    return dst_lens
+
+
+def copy_blocks(cache, src_blocks, dst_blocks):
+    """Copy whole physical blocks of a paged cache, K and V
+    (kvattn_copy_blocks): block dst_blocks[i] receives block src_blocks[i]."""
+    _i32(src_blocks, "src_blocks")
+    _i32(dst_blocks, "dst_blocks")
+    if src_blocks.shape != dst_blocks.shape or src_blocks.dim() != 1:
+        raise ValueError("src_blocks and dst_blocks must be 1-D of one length")
+    check(lib().kvattn_copy_blocks(ctypes.byref(cache.desc()), src_blocks.shape[0], _ptr(src_blocks),
+                                   _ptr(dst_blocks), _stream(cache.device)))
+
+
+def _host_i32(a, name, writable=False):
+    if not isinstance(a, np.ndarray) or a.dtype != np.int32 or not a.flags.c_contiguous:
+        raise TypeError("%s must be a C-contiguous numpy int32 array" % name)
+    if writable and not a.flags.writeable:
+        raise ValueError("%s must be writable" % name)
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class BlockPool:
+    """Host block pool with reference counts (kvattn_pool_*).  Tables, lengths
+    and id lists are host numpy int32 arrays; tables are [rows, max_blocks]
+    with -1 for no block and are updated in place where the C call does."""
+
+    def __init__(self, num_blocks):
+        h = lib().kvattn_pool_create(int(num_blocks))
+        if not h:
+            raise _lib.KvattnError(_lib.EINVAL, lib().kvattn_last_error().decode())
+        self._h = ctypes.c_void_p(h)
+        self._destroy = lib().kvattn_pool_destroy  # kept for destruction at interpreter exit
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def num_blocks(self):
+        return int(lib().kvattn_pool_num_blocks(self._h))
+
+    def num_free(self):
+        return int(lib().kvattn_pool_num_free(self._h))
+
+    def refcount(self, block):
+        return int(lib().kvattn_pool_refcount(self._h, int(block)))
+
+    def alloc(self, n):
+        ids = np.empty(max(int(n), 1), dtype=np.int32)
+        check(lib().kvattn_pool_alloc(self._h, int(n), _host_i32(ids, "ids")))
+        return ids[:int(n)]
+
+    def retain(self, ids):
+        check(lib().kvattn_pool_retain(self._h, ids.shape[0], _host_i32(ids, "ids")))
+
+    def release(self, ids):
+        check(lib().kvattn_pool_release(self._h, ids.shape[0], _host_i32(ids, "ids")))
+
+    def fork(self, src_row, length, dst_row=None):
+        if dst_row is None:
+            dst_row = np.full(src_row.shape[0], -1, dtype=np.int32)
+        check(lib().kvattn_pool_fork(self._h, _host_i32(src_row, "src_row"), _host_i32(dst_row, "dst_row", True),
+                                     src_row.shape[0], int(length)))
+        return dst_row
+
+    def free_seq(self, row, length):
+        check(lib().kvattn_pool_free_seq(self._h, _host_i32(row, "row", True), row.shape[0], int(length)))
+
+    def prepare_append(self, tables, cur_lens, new_lens):
+        """Updates tables [rows, max_blocks] in place; returns the
+        copy-on-write pairs (src, dst) as two int32 arrays."""
+        rows, mb = tables.shape
+        cs = np.empty(max(rows, 1), dtype=np.int32)
+        cd = np.empty(max(rows, 1), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        check(lib().kvattn_pool_prepare_append(self._h, rows, _host_i32(tables, "tables", True), mb,
+                                               _host_i32(cur_lens, "cur_lens"), _host_i32(new_lens, "new_lens"),
+                                               _host_i32(cs, "copy_src", True), _host_i32(cd, "copy_dst", True),
+                                               ctypes.byref(n)))
+        return cs[:n.value], cd[:n.value]
+
+    def reorder(self, perm, src_tables, src_lens):
+        n = perm.shape[0]
+        rows, mb = src_tables.shape
+        dt = np.empty((n, mb), dtype=np.int32)
+        dl = np.empty(max(n, 1), dtype=np.int32)
+        check(lib().kvattn_pool_reorder(self._h, n, _host_i32(perm, "perm"), rows, _host_i32(src_tables, "src_tables"),
+                                        _host_i32(src_lens, "src_lens"), mb, _host_i32(dt, "dst_tables", True),
+                                        _host_i32(dl, "dst_lens", True)))
+        return dt, dl[:n]

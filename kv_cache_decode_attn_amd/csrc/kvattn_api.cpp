@@ -8,6 +8,7 @@
 #include <string>
 
 #include "kvattn.h"
+#include "block_pool.h"
 #include "launch.h"
 
 namespace {
@@ -225,6 +226,7 @@ const char* kvattn_status_string(int status) {
     case KVATTN_EUNSUPPORTED: return "unsupported configuration";
     case KVATTN_EWORKSPACE: return "workspace missing or too small";
     case KVATTN_ELAUNCH: return "kernel launch failed";
+    case KVATTN_ENOSPACE: return "block pool exhausted";
     default: return "unknown status";
   }
 }
@@ -417,6 +419,182 @@ int kvattn_validate(const kvattn_cache* cache, int32_t batch, const int32_t* seq
   rc = kvattn::launch_validate(a, static_cast<hipStream_t>(stream));
   if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
   return ok();
+}
+
+int kvattn_reorder_rows(int32_t n_rows, const int32_t* perm, int32_t src_rows, const int32_t* src_table,
+                        const int32_t* src_lens, int32_t max_blocks, int32_t* dst_table, int32_t* dst_lens,
+                        void* stream) {
+  const char* who = "kvattn_reorder_rows";
+  if (n_rows < 0 || n_rows > 65535) return fail(KVATTN_EINVAL, "%s: n_rows %d out of range", who, n_rows);
+  if (src_rows < 0) return fail(KVATTN_EINVAL, "%s: src_rows %d < 0", who, src_rows);
+  if (max_blocks < 1 || max_blocks > (1 << 26))
+    return fail(KVATTN_EINVAL, "%s: max_blocks %d out of range", who, max_blocks);
+  if (!src_lens != !dst_lens) return fail(KVATTN_EINVAL, "%s: give both src_lens and dst_lens or neither", who);
+  if (n_rows == 0) return ok();
+  if (!perm || !src_table || !dst_table) return fail(KVATTN_EINVAL, "%s: perm and both tables are required", who);
+  const int32_t* s0 = src_table;
+  const int32_t* s1 = src_table + (int64_t)src_rows * max_blocks;
+  if (src_rows && (const int32_t*)dst_table < s1 && s0 < (const int32_t*)dst_table + (int64_t)n_rows * max_blocks)
+    return fail(KVATTN_EINVAL, "%s: dst_table overlaps src_table", who);
+  kvattn::RowReorderLaunch a{n_rows, src_rows, max_blocks, perm, src_table, src_lens, dst_table, dst_lens};
+  const int rc = kvattn::launch_reorder_rows(a, static_cast<hipStream_t>(stream));
+  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
+  return ok();
+}
+
+int kvattn_reorder_cache(const kvattn_cache* src, const kvattn_cache* dst, int32_t n_rows, const int32_t* perm,
+                         const int32_t* src_lens, int32_t* dst_lens, void* stream) {
+  const char* who = "kvattn_reorder_cache";
+  if (n_rows < 0 || n_rows > 65535) return fail(KVATTN_EINVAL, "%s: n_rows %d out of range", who, n_rows);
+  kvattn::CacheView sv, dv;
+  int64_t cap = 0;
+  if (!src || !dst) return fail(KVATTN_EINVAL, "%s: cache descriptors are required", who);
+  if (src->layout != KVATTN_CONTIGUOUS || dst->layout != KVATTN_CONTIGUOUS)
+    return fail(KVATTN_EINVAL, "%s: both caches must be contiguous (a paged cache reorders its block table)", who);
+  int rc = make_view(who, src, 0, nullptr, 0, &sv, &cap);
+  if (rc) return rc;
+  rc = make_view(who, dst, n_rows, nullptr, 0, &dv, &cap);
+  if (rc) return rc;
+  if (src->dtype != dst->dtype || src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim ||
+      src->capacity != dst->capacity)
+    return fail(KVATTN_EINVAL, "%s: caches differ in dtype, num_kv_heads, head_dim or capacity", who);
+  if (dst_lens && !src_lens) return fail(KVATTN_EINVAL, "%s: dst_lens needs src_lens", who);
+  if (n_rows == 0) return ok();
+  if (!perm) return fail(KVATTN_EINVAL, "%s: perm is required", who);
+  const int64_t sbytes = src->num_rows * sv.seq_stride;
+  const int64_t dbytes = dst->num_rows * dv.seq_stride;
+  auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const uint8_t* x = static_cast<const uint8_t*>(a);
+    const uint8_t* y = static_cast<const uint8_t*>(b);
+    return x < y + nb && y < x + na;
+  };
+  if (overlap(src->k, sbytes, dst->k, dbytes) || overlap(src->k, sbytes, dst->v, dbytes) ||
+      overlap(src->v, sbytes, dst->k, dbytes) || overlap(src->v, sbytes, dst->v, dbytes))
+    return fail(KVATTN_EINVAL, "%s: src and dst cache memory overlap", who);
+  kvattn::CacheReorderLaunch a{};
+  a.src_k = sv.k;
+  a.src_v = sv.v;
+  a.dst_k = dv.k;
+  a.dst_v = dv.v;
+  a.pos_bytes = sv.row_stride;
+  a.capacity = (int32_t)src->capacity;
+  a.num_kv_heads = src->num_kv_heads;
+  a.n_rows = n_rows;
+  a.src_rows = (int32_t)(src->num_rows < INT32_MAX ? src->num_rows : INT32_MAX);
+  a.perm = perm;
+  a.src_lens = src_lens;
+  a.dst_lens = dst_lens;
+  rc = kvattn::launch_reorder_cache(a, static_cast<hipStream_t>(stream));
+  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
+  return ok();
+}
+
+int kvattn_copy_blocks(const kvattn_cache* cache, int32_t n, const int32_t* src_blocks, const int32_t* dst_blocks,
+                       void* stream) {
+  const char* who = "kvattn_copy_blocks";
+  if (n < 0 || n > (1 << 24)) return fail(KVATTN_EINVAL, "%s: n %d out of range", who, n);
+  if (!cache) return fail(KVATTN_EINVAL, "%s: cache descriptor is NULL", who);
+  if (cache->layout != KVATTN_PAGED) return fail(KVATTN_EINVAL, "%s: cache must be paged", who);
+  if (n == 0) return ok();
+  if (!src_blocks || !dst_blocks) return fail(KVATTN_EINVAL, "%s: src_blocks and dst_blocks are required", who);
+  kvattn::CacheView v;
+  int64_t cap = 0;
+  static const int32_t kNoTable = -1;  // make_view wants a table; block copies use none
+  int rc = make_view(who, cache, 0, &kNoTable, 1, &v, &cap);
+  if (rc) return rc;
+  kvattn::BlockCopyLaunch a{v.k, v.v, v.block_stride, v.num_blocks, n, src_blocks, dst_blocks};
+  rc = kvattn::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
+  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
+  return ok();
+}
+
+struct kvattn_pool {
+  explicit kvattn_pool(int32_t n) : p(n) {}
+  kvattn::BlockPool p;
+};
+
+kvattn_pool* kvattn_pool_create(int64_t num_blocks) {
+  if (num_blocks < 1 || num_blocks > INT32_MAX) {
+    fail(KVATTN_EINVAL, "kvattn_pool_create: num_blocks %lld out of range", (long long)num_blocks);
+    return nullptr;
+  }
+  try {
+    kvattn_pool* p = new kvattn_pool((int32_t)num_blocks);
+    ok();
+    return p;
+  } catch (...) {
+    fail(KVATTN_EINVAL, "kvattn_pool_create: out of host memory for %lld blocks", (long long)num_blocks);
+    return nullptr;
+  }
+}
+
+void kvattn_pool_destroy(kvattn_pool* pool) { delete pool; }
+
+int64_t kvattn_pool_num_blocks(const kvattn_pool* pool) { return pool ? pool->p.num_blocks() : 0; }
+
+int64_t kvattn_pool_num_free(const kvattn_pool* pool) { return pool ? pool->p.num_free() : 0; }
+
+int32_t kvattn_pool_refcount(const kvattn_pool* pool, int32_t block) { return pool ? pool->p.refcount(block) : -1; }
+
+}  // extern "C"
+
+namespace {
+// Runs one pool operation: NULL checks, status and message.
+template <typename F>
+int pool_call(const char* who, kvattn_pool* pool, bool args_ok, F f) {
+  if (!pool) return fail(KVATTN_EINVAL, "%s: pool is NULL", who);
+  if (!args_ok) return fail(KVATTN_EINVAL, "%s: a required array is NULL", who);
+  std::string err;
+  const int rc = f(&err);
+  if (rc) return fail(rc, "%s: %s", who, err.c_str());
+  return ok();
+}
+}  // namespace
+
+extern "C" {
+
+int kvattn_pool_alloc(kvattn_pool* pool, int32_t n, int32_t* ids) {
+  return pool_call("kvattn_pool_alloc", pool, ids || n == 0,
+                   [&](std::string* e) { return pool->p.alloc(n, ids, e); });
+}
+
+int kvattn_pool_retain(kvattn_pool* pool, int32_t n, const int32_t* ids) {
+  return pool_call("kvattn_pool_retain", pool, ids || n == 0,
+                   [&](std::string* e) { return pool->p.retain(n, ids, e); });
+}
+
+int kvattn_pool_release(kvattn_pool* pool, int32_t n, const int32_t* ids) {
+  return pool_call("kvattn_pool_release", pool, ids || n == 0,
+                   [&](std::string* e) { return pool->p.release(n, ids, e); });
+}
+
+int kvattn_pool_fork(kvattn_pool* pool, const int32_t* src_row, int32_t* dst_row, int32_t max_blocks,
+                     int32_t length) {
+  return pool_call("kvattn_pool_fork", pool, src_row && dst_row,
+                   [&](std::string* e) { return pool->p.fork(src_row, dst_row, max_blocks, length, e); });
+}
+
+int kvattn_pool_free_seq(kvattn_pool* pool, int32_t* row, int32_t max_blocks, int32_t length) {
+  return pool_call("kvattn_pool_free_seq", pool, row != nullptr,
+                   [&](std::string* e) { return pool->p.free_seq(row, max_blocks, length, e); });
+}
+
+int kvattn_pool_prepare_append(kvattn_pool* pool, int32_t rows, int32_t* tables, int32_t max_blocks,
+                               const int32_t* cur_lens, const int32_t* new_lens, int32_t* copy_src,
+                               int32_t* copy_dst, int32_t* n_copies) {
+  const bool args = n_copies && (rows == 0 || (tables && cur_lens && new_lens && copy_src && copy_dst));
+  return pool_call("kvattn_pool_prepare_append", pool, args, [&](std::string* e) {
+    return pool->p.prepare_append(rows, tables, max_blocks, cur_lens, new_lens, copy_src, copy_dst, n_copies, e);
+  });
+}
+
+int kvattn_pool_reorder(kvattn_pool* pool, int32_t n_rows, const int32_t* perm, int32_t src_rows,
+                        const int32_t* src_tables, const int32_t* src_lens, int32_t max_blocks,
+                        int32_t* dst_tables, int32_t* dst_lens) {
+  const bool args = (n_rows == 0 || (perm && dst_tables && dst_lens)) && (src_rows == 0 || (src_tables && src_lens));
+  return pool_call("kvattn_pool_reorder", pool, args, [&](std::string* e) {
+    return pool->p.reorder(n_rows, perm, src_rows, src_tables, src_lens, max_blocks, dst_tables, dst_lens, e);
+  });
 }
 
 }  // extern "C"

@@ -86,4 +86,44 @@ struct ValidateLaunch {
 };
 int launch_validate(const ValidateLaunch& a, hipStream_t stream);
 
+// Block-table row gather (batch/beam reorder of a paged cache).
+struct RowReorderLaunch {
+  int32_t n_rows, src_rows, max_blocks;
+  const int32_t* perm;
+  const int32_t* src_table;
+  const int32_t* src_lens;  // may be NULL (then dst_lens is NULL)
+  int32_t* dst_table;
+  int32_t* dst_lens;
+};
+int launch_reorder_rows(const RowReorderLaunch& a, hipStream_t stream);
+
+// Contiguous-cache row gather: for dst row i and KV head g, the first L
+// positions of src row perm[i] (L from src_lens, else the capacity).
+struct CacheReorderLaunch {
+  const uint8_t* src_k;
+  const uint8_t* src_v;
+  uint8_t* dst_k;
+  uint8_t* dst_v;
+  int64_t pos_bytes;   // bytes per position of one head: head_dim * element bytes
+  int32_t capacity;    // positions per head row
+  int32_t num_kv_heads;
+  int32_t n_rows, src_rows;
+  const int32_t* perm;
+  const int32_t* src_lens;  // may be NULL
+  int32_t* dst_lens;        // may be NULL
+};
+int launch_reorder_cache(const CacheReorderLaunch& a, hipStream_t stream);
+
+// Whole-block copies inside one paged cache (both pools).
+struct BlockCopyLaunch {
+  uint8_t* k;
+  uint8_t* v;
+  int64_t block_bytes;  // num_kv_heads * 16 * head_dim * element bytes
+  int64_t num_blocks;
+  int32_t n;
+  const int32_t* src;
+  const int32_t* dst;
+};
+int launch_copy_blocks(const BlockCopyLaunch& a, hipStream_t stream);
+
 }  // namespace kvattn

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = _lib.lib()
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert L.kvattn_status_string(code).decode() != "unknown status"
 
 
@@ -162,3 +162,41 @@ def test_decode_append_host_errors():
     assert call(batch=0) == _lib.OK                        # nothing to do, nothing launched
     assert call(batch=0, k_new=None) == _lib.OK
     assert _lib.lib().kvattn_last_error().decode() == ""
+
+
+def test_reorder_and_copy_host_errors():
+    L = _lib.lib()
+    P = FAKE
+
+    def rows(n=4, src_rows=4, mb=8, perm=P, st=P, sl=P, dt=FAKE + 0x100000, dl=FAKE + 0x200000):
+        return L.kvattn_reorder_rows(n, perm, src_rows, st, sl, mb, dt, dl, None)
+
+    assert rows(n=70000) == _lib.EINVAL
+    assert rows(mb=0) == _lib.EINVAL
+    assert rows(perm=None) == _lib.EINVAL
+    assert rows(dl=None) == _lib.EINVAL                # lengths in but not out
+    assert rows(dt=FAKE + 16) == _lib.EINVAL           # destination overlaps the source table
+    assert rows(n=0, perm=None) == _lib.OK
+
+    src = _cache(layout=_lib.CONTIGUOUS, rows=4)
+    dst = _cache(layout=_lib.CONTIGUOUS, rows=4)
+    dst.k, dst.v = FAKE + 0x4000000, FAKE + 0x8000000
+
+    def cache(s=src, d=dst, n=4, perm=P, sl=None, dl=None):
+        return L.kvattn_reorder_cache(ctypes.byref(s), ctypes.byref(d), n, perm, sl, dl, None)
+
+    assert cache(s=_cache()) == _lib.EINVAL            # paged source
+    assert cache(d=_cache(layout=_lib.CONTIGUOUS, rows=4)) == _lib.EINVAL   # dst memory == src memory
+    other = _cache(layout=_lib.CONTIGUOUS, rows=4, capacity=512)
+    other.k, other.v = dst.k, dst.v
+    assert cache(d=other) == _lib.EINVAL               # capacity differs
+    assert cache(n=8) == _lib.EINVAL                   # dst has 4 rows
+    assert cache(dl=FAKE) == _lib.EINVAL               # dst_lens without src_lens
+    assert cache(perm=None) == _lib.EINVAL
+    assert cache(n=0, perm=None) == _lib.OK
+
+    assert L.kvattn_copy_blocks(ctypes.byref(_cache(layout=_lib.CONTIGUOUS)), 4, P, P, None) == _lib.EINVAL
+    assert L.kvattn_copy_blocks(ctypes.byref(_cache()), 4, None, P, None) == _lib.EINVAL
+    assert L.kvattn_copy_blocks(ctypes.byref(_cache()), -1, P, P, None) == _lib.EINVAL
+    assert L.kvattn_copy_blocks(None, 4, P, P, None) == _lib.EINVAL
+    assert L.kvattn_copy_blocks(ctypes.byref(_cache()), 0, None, None, None) == _lib.OK
