@@ -52,15 +52,27 @@ METRIC = "decode-attn HBM GB/s (% of peak) & seqs/s; prefill TFLOP/s (% MFMA pea
 DEV = "cuda"
 
 
-DECODE_SOURCES = ("kv_cache_decode_attn_amd/csrc/decode.hip", "kv_cache_decode_attn_amd/csrc/common.h",
-                  "kv_cache_decode_attn_amd/csrc/launch.h")
+DECODE_SOURCES = ("kv_cache_decode_attn_amd/csrc/decode.hip", "kv_cache_decode_attn_amd/csrc/common.h")
+LAUNCH_HEADER = "kv_cache_decode_attn_amd/csrc/launch.h"
 
 
-def decode_source_sha():
+def _decode_struct(text):
+    """The DecodeLaunch declaration of launch.h: the only part of that
+    header the decode kernels compile against."""
+    i = text.index("struct DecodeLaunch {")
+    return text[i:text.index("};", i) + 2]
+
+
+def decode_source_sha(read=None):
+    """Hash of the sources the decode kernels are built from."""
+    if read is None:
+        def read(rel):
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                return f.read()
     h = hashlib.sha256()
     for rel in DECODE_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        h.update(read(rel))
+    h.update(_decode_struct(read(LAUNCH_HEADER).decode()).encode())
     return h.hexdigest()
 
 
