@@ -38,8 +38,9 @@ COMMON = [
 #    as zeros) and masked keys (whose scores are replaced by -inf before any
 #    maximum), so no result changes;
 #  - its matrix results live in vector registers (the scores are read by the
-#    softmax right away), which keeps its register allocation free of copies
-#    between the two register files.
+#    softmax right away); with no accumulation registers in use the compiler
+#    can give each of the two waves per SIMD all 256 registers, and the
+#    allocation has no copies between the two register files.
 EXTRA = {"prefill_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

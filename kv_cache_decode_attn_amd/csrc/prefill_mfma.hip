@@ -14,13 +14,16 @@
 // Budget on gfx950 per compute unit (measured): the matrix cores reach
 // ~1.9 PFLOP/s on back-to-back 32x32x16 bf16 MFMAs, the LDS serves ~256
 // bytes per clock for 16-byte reads, and exp2 issues at a quarter of the
-// vector rate.  A wave owns 64 query columns (two 32-column blocks) so that
-// every K and V^T fragment read from LDS feeds two MFMAs; with Q, the
-// accumulators and two steps of scores in registers that is one wave per
-// SIMD, so each wave overlaps its own matrix and vector work (below).
+// vector rate.  Per 32-key tile a wave's softmax costs about as much vector
+// ALU time as its 16 MFMAs take on the matrix core, so the kernel runs two
+// waves per SIMD: while one wave works through its softmax, the other's
+// MFMAs keep the matrix core busy.  That fixes the register budget at 256
+// per wave (all in vector registers: no accumulation registers are used, so
+// the compiler may give the wave the whole budget), which holds one 32-column
+// query block per wave: Q, O^T, two steps of scores and the weights.
 //
-// Work split.  A workgroup of 4 waves owns HW = min(G, 8) query heads of one
-// KV head and 256 / HW query rows, cut into eight 32-row column blocks, two
+// Work split.  A workgroup of 8 waves owns HW = min(G, 8) query heads of one
+// KV head and 256 / HW query rows, cut into eight 32-row column blocks, one
 // per wave.  The heads of a GQA group share the K/V tiles staged in LDS.
 // The KV head is the fastest grid dimension, so with 8 KV heads every XCD
 // (and its L2) serves one KV head; causal query tiles are issued heaviest
@@ -33,10 +36,9 @@
 // LDS and its MFMA operand is read with the transposing LDS read.
 //
 // Pipeline.  Step t runs the QK^T product of tile t+1, the softmax of tile
-// t and the PV product of tile t-1.  Away from the causal diagonal and the
-// sequence end, the three parts are independent and the step is written
-// out as 32 slots of one MFMA (QK^T and PV alternating) plus a share of
-// the softmax, so the vector ALU works while the matrix cores run.
+// t and the PV product of tile t-1: three independent parts that the
+// compiler interleaves.  Tiles away from the causal diagonal and the
+// sequence end take a step without mask tests.
 //
 // Per 32-key tile and column block (h = lane / 32):
 //   S^T[key][q] = K Q^T      A = K rows from LDS, B = Q (registers), fp32
@@ -73,8 +75,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKeys = 32;      // keys per tile
-constexpr int kThreads = 256;  // 4 waves, one per SIMD
-constexpr int kBlocks = 8;     // 32-row query column blocks per workgroup
+constexpr int kCB = 1;                 // 32-row query column blocks per wave
+constexpr int kWaves = 8;              // two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBlocks = kWaves * kCB;  // 32-row query column blocks per workgroup
 constexpr int kBufs = 8;       // LDS tile buffers (a ring)
 constexpr int kAhead = 5;      // tiles loaded ahead of the one being scored
 constexpr float kLog2e = 1.4426950408889634f;
@@ -95,46 +99,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Empty inline-assembly statements (they emit no instruction) that pin the
-// place of a computation in the instruction stream: the fast loop below is
-// written slot by slot, and without them the compiler would gather all
-// vector work of a step in one place (or sink it past the loop's wait),
-// which leaves the matrix cores idle meanwhile.
-//
-// An empty statement that needs x in accumulation registers.
-__device__ __forceinline__ void settle_acc(const U4& x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  asm volatile("" ::"a"(__builtin_bit_cast(u32x4, x)));
-#endif
-}
-
-// An empty statement that redefines x: what uses x stays after it.
-__device__ __forceinline__ void anchor(float& x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" : "+v"(x));
-#endif
-}
-
-__device__ __forceinline__ void anchor(U4& x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 v = __builtin_bit_cast(u32x4, x);
-  asm volatile("" : "+v"(v));
-  x = __builtin_bit_cast(U4, v);
-#endif
-}
-
-// An empty statement that needs x: what computes x stays before it.
+// An empty inline-assembly statement (it emits no instruction) that needs
+// x: the loads that produce x complete before it.  Used so that no load the
+// compiler tracks is still in flight inside the tile loop, whose waits would
+// otherwise also wait for the tile transfers.
 __device__ __forceinline__ void settle(const U4& x) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   asm volatile("" ::"v"(__builtin_bit_cast(u32x4, x)));
-#endif
-}
-__device__ __forceinline__ void settle(float x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" ::"v"(x));
 #endif
 }
 
@@ -162,8 +134,10 @@ struct Geo {
   static constexpr int KBYTES = kKeys * RB;
   static constexpr int VBYTES = kKeys * RB;
   static constexpr int BUF = KBYTES + VBYTES;
-  static constexpr int LOADS = kKeys * NC / 64 / 4;  // 1 KB wave loads per wave, per operand
-  static_assert(LOADS >= 1 && LOADS * 4 * 64 == kKeys * NC, "tile split over the waves");
+  static constexpr int PIECES = kKeys * NC / 64;                   // 1 KB pieces per operand
+  static constexpr int LOADS = PIECES >= kWaves ? PIECES / kWaves : 1;  // pieces per loading wave
+  static constexpr int LWAVES = PIECES / LOADS;                       // waves that load
+  static_assert(LOADS * LWAVES == PIECES && LWAVES <= kWaves, "tile split over the waves");
   static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
@@ -205,9 +179,6 @@ __device__ __forceinline__ s16x4 read_tr16(const uint8_t* lds) {
 #endif
 }
 
-// Scheduling groups (masks of __builtin_amdgcn_sched_group_barrier).
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
-
 template <int D, bool CAUSAL, bool MASK>
 __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const PrefillLaunch a, int hw) {
   using GE = Geo<D>;
@@ -231,18 +202,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   const int P = a.positions ? max(a.positions[b], 0) : 0;
 
   // this wave's two column blocks: head hb[cb], first row rb[cb]
-  int hb[2], rb[2];
+  int hb[kCB], rb[kCB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int j = 2 * wave + cb;
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int j = kCB * wave + cb;
     hb[cb] = h0 + j / bph;
     rb[cb] = q_wg + 32 * (j % bph);
   }
-  const int row_lo = min(rb[0], rb[1]), row_hi = max(rb[0], rb[1]) + 32;
+  const int row_lo = min(rb[0], rb[kCB - 1]), row_hi = max(rb[0], rb[kCB - 1]) + 32;
 
   if (q_wg >= qlen) {  // the whole tile is padding rows: zeros
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       float* out_h = a.out + ((int64_t)b * a.num_q_heads + hb[cb]) * n_max * D;
       for (int r = 0; r < 32; ++r) {
         const int t = rb[cb] + r;
@@ -266,10 +237,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   const uint8_t* mrow = MASK ? a.key_mask + (int64_t)b * a.key_mask_stride : nullptr;
 
   // ---- Q fragments (B operand of S^T = K Q^T): row rb + lc, d 16c + 8hh ----
-  int tq[2];
-  U4 qf[2][DK];
+  int tq[kCB];
+  U4 qf[kCB][DK];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     tq[cb] = rb[cb] + lc;
     const uint8_t* qg = a.q + ((int64_t)b * a.num_q_heads + hb[cb]) * n_max * D * 2;
 #pragma unroll
@@ -279,13 +250,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
                                    : U4{0, 0, 0, 0};
     }
   }
-  // Q lands (in accumulation registers) before the tile loop: the loop then
-  // carries no compiler-tracked vector-memory loads, so no wait in it counts
-  // the tile transfers in flight.
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int c = 0; c < DK; ++c) settle_acc(qf[cb][c]);
 
   // ---- staging of one K/V tile: global -> LDS directly ----
   // Each wave moves GE::LOADS 1 KB pieces of K and of V per tile with
@@ -328,6 +292,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     const int kt0 = t * kKeys;
     uint8_t* kl = smem + (t % kBufs) * GE::BUF;
     uint8_t* vl = kl + GE::KBYTES;
+    if (wave >= GE::LWAVES) return;
     if (MASK) {
       uint32_t info = 0;
 #pragma unroll
@@ -367,33 +332,37 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // S^T of the tile in buffer `buf`, both column blocks: keys
   // kt0 + 8*(r/4) + 4hh + r%4, query rb[cb] + lc.  Each K fragment feeds the
   // two column blocks.
-  auto scores = [&](int buf, f32x16 (&s)[2]) {
+  auto scores = [&](int buf, f32x16 (&s)[kCB]) {
     const uint8_t* kl = smem + buf * GE::BUF;
 #pragma unroll
     for (int cc = 0; cc < DK; ++cc) {
       const U4 kf = *reinterpret_cast<const U4*>(kl + lc * GE::RB + ((2 * cc + hh) ^ GE::swz_k(lc)) * 16);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) s[cb] = mfma(kf, qf[cb][cc], cc == 0 ? f32x16{} : s[cb]);
+      for (int cb = 0; cb < kCB; ++cb) s[cb] = mfma(kf, qf[cb][cc], cc == 0 ? f32x16{} : s[cb]);
     }
   };
 
   // ---- accumulators ----
-  f32x16 o[2][DT];
+  f32x16 o[kCB][DT];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[cb][dt][r] = 0.f;
-  float mrun[2] = {-INFINITY, -INFINITY};
-  float lpart[2] = {0.f, 0.f};  // this lane's half of the row sum
+  float mrun[kCB], lpart[kCB];  // lpart: this lane's half of the row sum
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    mrun[cb] = -INFINITY;
+    lpart[cb] = 0.f;
+  }
   const float c = a.scale * kLog2e;
 
   // Softmax of the scores of the tile at kt0 into bf16 weights pf (and the
   // row-sum halves); alpha receives the factor by which o must be rescaled
   // once the previous tile's PV product is in, and `resc` whether any lane
   // of the wave needs it.
-  auto softmax = [&](auto masked, int kt0, int buf, f32x16 (&s)[2], U4 (&pf)[2][2], float (&alpha)[2], bool& resc) {
+  auto softmax = [&](auto masked, int kt0, int buf, f32x16 (&s)[kCB], U4 (&pf)[kCB][2], float (&alpha)[kCB], bool& resc) {
     if constexpr (decltype(masked)::value) {
       // causal edge, keys beyond q_len, key mask (keys kt0 + 8gq + 4hh + e)
 #pragma unroll
@@ -404,7 +373,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
           const int key = kt0 + 8 * gq + 4 * hh + e;
           const bool kok = key_valid(key);
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
+          for (int cb = 0; cb < kCB; ++cb) {
             const bool ok = kok & (!CAUSAL || key <= tq[cb]);
             s[cb][r] = ok ? s[cb][r] : -INFINITY;
           }
@@ -412,7 +381,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     }
     bool any_need = false;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       // running maximum of this query (log2 domain), raised lazily
       float tm = fmaxf(s[cb][0], s[cb][1]);
 #pragma unroll
@@ -471,19 +440,19 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     const u32x2 h0 = __builtin_bit_cast(u32x2, half[0]), h1 = __builtin_bit_cast(u32x2, half[1]);
     return U4{h0[0], h0[1], h1[0], h1[1]};
   };
-  auto pv = [&](int buf, const U4 (&pf)[2][2], f32x16 (&o)[2][DT]) {
+  auto pv = [&](int buf, const U4 (&pf)[kCB][2], f32x16 (&o)[kCB][DT]) {
     const uint8_t* vl = smem + buf * GE::BUF + GE::KBYTES;
 #pragma unroll
     for (int f = 0; f < 2 * DT; ++f) {
       const U4 vf = v_frag(vl, f / DT, f % DT);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) o[cb][f % DT] = mfma(vf, pf[cb][f / DT], o[cb][f % DT]);
+      for (int cb = 0; cb < kCB; ++cb) o[cb][f % DT] = mfma(vf, pf[cb][f / DT], o[cb][f % DT]);
     }
   };
 
-  auto rescale = [&](const float (&alpha)[2], f32x16 (&o)[2][DT]) {
+  auto rescale = [&](const float (&alpha)[kCB], f32x16 (&o)[kCB][DT]) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[cb][dt] *= alpha[cb];
   };
@@ -492,116 +461,30 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // tile it - 1.  Tile it + kAhead is loaded meanwhile and tile it + 2,
   // loaded kAhead - 2 steps earlier, is published by the barrier that ends
   // the step.  Buffers t % 8 hold tiles it - 1 .. it + kAhead.  Every wave
-  // runs the same number of steps (ntiles + 1), so the barriers match.
+  // runs the same number of steps (ntiles + 1), so the barriers match.  The
+  // three parts are independent: the compiler interleaves them, and the
+  // other wave of the SIMD fills the matrix or vector units while this one
+  // waits.
   //
-  // Fast step (tiles 1 <= it < fast_end: no mask, a predecessor): the three
-  // parts are independent, so the step is written out as NS slots, each one
-  // MFMA (QK^T and PV alternating) followed by a share of the softmax on the
-  // vector ALU, with scheduling barriers between slots so that the matrix
-  // cores run while the vector ALU works.  It does not rescale o: when its
-  // softmax moves a running maximum the fast loop ends and the rescale runs
-  // before the next PV product.
-  constexpr int NQ = 2 * DK;      // QK^T MFMAs of a tile
-  constexpr int NP = 2 * 2 * DT;  // PV MFMAs of a tile
-  constexpr int NS = NQ + NP;     // slots
-  static_assert(NQ == NP, "QK^T and PV MFMAs alternate");
-  constexpr int kExpFrom = 5;     // first slot with exponentials
-  auto fast_step = [&](int it, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const U4 (&p_prev)[2][2],
-                       U4 (&p_cur)[2][2], float (&alpha)[2], bool& resc, f32x16 (&oa)[2][DT]) {
+  // Fast step (tiles 1 <= it < fast_end: no mask, a predecessor, all three
+  // parts).  It does not rescale o: when its softmax moves a running maximum
+  // the fast loop ends and the rescale runs before the next PV product.
+  auto fast_step = [&](int it, f32x16 (&s_cur)[kCB], f32x16 (&s_nxt)[kCB], const U4 (&p_prev)[kCB][2],
+                       U4 (&p_cur)[kCB][2], float (&alpha)[kCB], bool& resc, f32x16 (&o)[kCB][DT]) {
     load_tile(it + kAhead, kAhead - 2);
-    const uint8_t* kl = smem + ((it + 1) % kBufs) * GE::BUF;
-    const uint8_t* vl = smem + ((it + kBufs - 1) % kBufs) * GE::BUF + GE::KBYTES;
-    U4 kf[DK], vf[2 * DT];
-    float tm[2], msub[2], l[2], p[2][16];
-    bool need[2];
-    kf[0] = k_frag(kl, 0);
-    vf[0] = v_frag(vl, 0, 0);
-    kf[1] = k_frag(kl, 1);
-    vf[1] = v_frag(vl, 1 / DT, 1 % DT);
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      // fragments two groups ahead: K chunk cc is used by slots 4cc, 4cc + 2,
-      // V fragment f by slots 4f + 1, 4f + 3
-      if (k % 4 == 0 && k / 4 + 2 < DK) {
-        const int f = k / 4 + 2;
-        kf[f] = k_frag(kl, f);
-        vf[f] = v_frag(vl, f / DT, f % DT);
-      }
-      if (k % 2 == 0) {
-        const int q = k / 2, cc = q / 2, cb = q % 2;
-        U4 ka = kf[cc];
-        anchor(ka);  // issued in this slot, not earlier
-        s_nxt[cb] = mfma(ka, qf[cb][cc], cc == 0 ? f32x16{} : s_nxt[cb]);
-      } else {
-        const int q = k / 2, f = q / 2, cb = q % 2;
-        oa[cb][f % DT] = mfma(vf[f], p_prev[cb][f / DT], oa[cb][f % DT]);
-      }
-      // vector share of the softmax of tile it
-      if (k < 4) {  // row maxima: a quarter of the scores per slot
-        const int cb = k / 2, r0 = 8 * (k % 2);
-        float s0 = s_cur[cb][r0];
-        anchor(s0);
-        float t = fmaxf(s0, s_cur[cb][r0 + 1]);
-#pragma unroll
-        for (int r = r0 + 2; r < r0 + 8; r += 2) t = fmaxf(t, fmaxf(s_cur[cb][r], s_cur[cb][r + 1]));
-        tm[cb] = (k % 2) ? fmaxf(tm[cb], t) : t;
-        settle(tm[cb]);
-      } else if (k == 4) {  // the lazily raised running maxima
-        bool any_need = false;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm[cb]), __float_as_uint(tm[cb]), false, false);
-          const float t = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
-          need[cb] = t > mrun[cb] + kRescale;
-          const float mnew = need[cb] ? t : mrun[cb];
-          alpha[cb] = need[cb] ? exp2f(mrun[cb] - mnew) : 1.f;
-          any_need |= need[cb];  // a running maximum is finite here: tile 0 set it
-          mrun[cb] = mnew;
-          msub[cb] = (mnew == -INFINITY) ? 0.f : mnew;
-          l[cb] = lpart[cb] * alpha[cb];
-          settle(msub[cb]);
-        }
-        resc = __any(any_need);
-      }
-      // exponentials j = 0..31 (block j / 16, score j % 16) spread over the
-      // slots from kExpFrom; a pair is packed and summed with its second
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        if (kExpFrom + (j * (NS - kExpFrom)) / 32 != k) continue;
-        const int cb = j / 16, r = j % 16;
-        float sv = s_cur[cb][r];
-        anchor(sv);  // computed in this slot, not earlier
-        p[cb][r] = __builtin_amdgcn_exp2f(fmaf(sv, c, -msub[cb]));
-        if (r % 2 == 1) {
-          const int m = r / 8, w = (r % 8) / 2;
-          const uint32_t pk = pack_bf16(p[cb][r - 1], p[cb][r]);
-          if (w == 0) p_cur[cb][m].x = pk;
-          if (w == 1) p_cur[cb][m].y = pk;
-          if (w == 2) p_cur[cb][m].z = pk;
-          if (w == 3) p_cur[cb][m].w = pk;
-          l[cb] = dot2_ones(pk, l[cb]);
-          settle(l[cb]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // the softmax results are due here, not sunk past the wait below
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      settle(p_cur[cb][0]);
-      settle(p_cur[cb][1]);
-      settle(l[cb]);
-    }
-    lpart[0] = l[0];
-    lpart[1] = l[1];
+    scores((it + 1) % kBufs, s_nxt);
+    softmax(std::false_type{}, it * kKeys, it % kBufs, s_cur, p_cur, alpha, resc);
+    pv((it + kBufs - 1) % kBufs, p_prev, o);
     finish_tile(it + 2, std::integral_constant<int, kAhead - 2>{});
     __syncthreads();
   };
   // General step: masked softmax, the parts this step has, and the rescale.
-  auto slow_step = [&](int it, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const U4 (&p_prev)[2][2],
-                       U4 (&p_cur)[2][2], f32x16 (&o)[2][DT]) {
+  auto slow_step = [&](int it, f32x16 (&s_cur)[kCB], f32x16 (&s_nxt)[kCB], const U4 (&p_prev)[kCB][2],
+                       U4 (&p_cur)[kCB][2], f32x16 (&o)[kCB][DT]) {
     load_tile(it + kAhead, kAhead - 2);
-    float alpha[2] = {1.f, 1.f};
+    float alpha[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) alpha[cb] = 1.f;
     bool resc = false;
     if (it + 1 < wave_tiles) scores((it + 1) % kBufs, s_nxt);
     if (it < wave_tiles) softmax(std::true_type{}, it * kKeys, it % kBufs, s_cur, p_cur, alpha, resc);
@@ -618,17 +501,19 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   finish_tile(0, std::integral_constant<int, kAhead - 1>{});
   finish_tile(1, std::integral_constant<int, kAhead - 2>{});
   __syncthreads();
-  f32x16 sA[2], sB[2];
-  U4 pA[2][2], pB[2][2];
+  f32x16 sA[kCB], sB[kCB];
+  U4 pA[kCB][2], pB[kCB][2];
   if (wave_tiles > 0) scores(0, sA);
   slow_step(0, sA, sB, pA, pB, o);  // the first real tile never rescales (and has no PV)
   // here sB holds the scores of tile 1 and pB the weights of tile 0
   int it = 1;
   bool resc = false;
-  float alpha[2] = {1.f, 1.f};
+  float alpha[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) alpha[cb] = 1.f;
   auto advance = [&]() {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       sA[cb] = sB[cb];
       pA[cb][0] = pB[cb][0];
       pA[cb][1] = pB[cb][1];
@@ -638,9 +523,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // nothing the compiler tracks may be in flight in the fast loop: its waits
   // would then also wait for the tile transfers
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-    for (int c = 0; c < DK; ++c) settle_acc(qf[cb][c]);
+    for (int c = 0; c < DK; ++c) settle(qf[cb][c]);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   while (it < fast_end) {
     fast_step(it, sA, sB, pA, pB, alpha, resc, o);
@@ -656,7 +541,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
 
   // ---- epilogue: O^T[d][q] / l[q] -> out[q][d]; rows >= q_len are 0 ----
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart[cb]), __float_as_uint(lpart[cb]), false, false);
     const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     if (tq[cb] < n_max) {
