@@ -376,7 +376,11 @@ int kvattn_attn_prefill(const kvattn_cache* cache, int32_t batch, int32_t num_q_
   a.scale = scale;
   a.out = out;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (cache) {
+  // The bf16 MFMA kernel writes a bf16 cache itself: each of its workgroups
+  // stores the rows of the query tile it owns.  Otherwise the append kernel
+  // runs first.
+  a.write_cache = cache && cache->dtype == dtype && kvattn::prefill_mfma_supports(a);
+  if (cache && !a.write_cache) {
     kvattn::AppendLaunch w{};
     w.c = a.c;
     w.cache_dtype = cache->dtype;

@@ -72,8 +72,13 @@ struct PrefillLaunch {
   int32_t causal, attend_prefix;
   float scale;
   float* out;
+  // The MFMA kernel stores the new K/V rows into the cache itself (same
+  // dtype in and out); otherwise the caller launches the append.
+  int32_t write_cache;
 };
 int launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+// Whether launch_prefill runs the bf16 MFMA kernel for these arguments.
+bool prefill_mfma_supports(const PrefillLaunch& a);
 
 struct ValidateLaunch {
   CacheView c;

@@ -23,7 +23,6 @@
 namespace kvattn {
 
 int launch_prefill_mfma(const PrefillLaunch& a, hipStream_t s);  // prefill_mfma.hip
-bool prefill_mfma_supports(const PrefillLaunch& a);
 
 namespace {
 

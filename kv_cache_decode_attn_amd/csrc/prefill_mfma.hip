@@ -561,6 +561,29 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
         }
     }
   }
+
+  // ---- cache write: the K/V rows of this workgroup's query tile ----
+  // One workgroup owns each (sequence, KV head, query tile), so the tiles'
+  // rows (those below q_len) are written exactly once, as kv_append writes
+  // them: token i goes to position positions[b] + i, skipped outside the
+  // cache.  They were just staged from these addresses, so the reads hit L2.
+  if (a.write_cache) {
+    constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
+    const int nrows = min(rows_wg, qlen - q_wg);
+    const int p0 = a.positions ? a.positions[b] : 0;
+    const CacheView cv = a.c;
+    for (int idx = tid; idx < nrows * CPR; idx += kThreads) {
+      const int i = q_wg + idx / CPR, ch = idx % CPR;
+      const int64_t off = position_offset(cv, b, g, (int64_t)p0 + i);
+      if (off < 0) continue;
+      const int64_t src = (int64_t)i * GE::RB + ch * 16;
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 xk = *reinterpret_cast<const u32x4*>(kg + src);
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(vg + src);
+      *reinterpret_cast<u32x4*>(cv.k + off + ch * 16) = xk;
+      *reinterpret_cast<u32x4*>(cv.v + off + ch * 16) = xv;
+    }
+  }
 }
 
 template <int D, bool CAUSAL, bool MASK>

@@ -97,26 +97,46 @@ def test_causal_matrix_through_one_hot_values():
     assert max_abs(got, want) <= 1e-6
 
 
-@pytest.mark.parametrize("layout", [K.PAGED, K.CONTIGUOUS])
-def test_prefill_writes_cache_bit_exact(layout):
-    B, Hq, Hkv, N, d = 2, 8, 2, 40, 128
+@pytest.mark.parametrize("layout,G,d,N,pos,cache_dtype", [
+    (K.PAGED, 4, 128, 40, (0, 0), K.BF16),
+    (K.CONTIGUOUS, 4, 128, 40, (0, 0), K.BF16),
+    (K.PAGED, 1, 64, 300, (5, 37), K.BF16),        # two query tiles per head, shifted positions
+    (K.PAGED, 8, 128, 200, (16, 3), K.BF16),       # seven query tiles
+    (K.CONTIGUOUS, 2, 128, 150, (7, 0), K.BF16),
+    (K.PAGED, 4, 128, 100, (3, 0), K.FP8_E4M3),    # encoded by the separate append pass
+])
+def test_prefill_writes_cache_bit_exact(layout, G, d, N, pos, cache_dtype):
+    """The cache bytes after attn_prefill equal the oracle's append of the
+    new tokens (bf16: written by the MFMA kernel's own workgroups; fp8: by
+    the append kernel), and the attention output matches."""
+    B, Hkv = 2, 2
+    Hq = G * Hkv
     q, k, v = _inputs(B, Hq, Hkv, N, d, torch.bfloat16, 33, std=1 / math.sqrt(d))
-    q_lens = np.array([40, 23], np.int32)
+    q_lens = np.array([N, (2 * N) // 3 + 1], np.int32)
+    positions = np.array(pos, np.int32)
+    ks = vs = None
+    if cache_dtype == K.FP8_E4M3:
+        ks = torch.from_numpy(synth.fp8_scales(Hkv, (33, synth.T_SCALE))).to(DEV)
+        vs = torch.from_numpy(synth.fp8_scales(Hkv, (34, synth.T_SCALE))).to(DEV)
     if layout == K.PAGED:
-        table, nblk = synth.block_table([3, 2], 3, (33, synth.T_PERM), num_blocks=7)
-        cache = K.KVCache.paged(nblk, Hkv, d, K.BF16, DEV, fill=0.5)
+        nb = [synth.blocks_for(p + N) for p in positions]
+        table, nblk = synth.block_table(nb, max(nb), (33, synth.T_PERM), num_blocks=sum(nb) + 3)
+        cache = K.KVCache.paged(nblk, Hkv, d, cache_dtype, DEV, ks, vs, fill=0.5 if ks is None else 7)
         tdev = torch.from_numpy(table).to(DEV)
     else:
         table, tdev = None, None
-        cache = K.KVCache.contiguous(B, Hkv, 48, d, K.BF16, DEV, fill=0.5)
+        cap = 16 * synth.blocks_for(int(positions.max()) + N)
+        cache = K.KVCache.contiguous(B, Hkv, cap, d, cache_dtype, DEV, ks, vs, fill=0.5)
     before_k, before_v = storage(cache.k), storage(cache.v)
     got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), cache=cache, q_lens=torch.from_numpy(q_lens).to(DEV),
-                         positions=torch.zeros(B, dtype=torch.int32, device=DEV), block_table=tdev).cpu().numpy()
-    want_k, want_v = OC.predict_append(before_k, before_v, storage(k), storage(v), [0, 0], N, layout == K.PAGED,
-                                       table, n_valid=q_lens)
+                         positions=torch.from_numpy(positions).to(DEV), block_table=tdev).cpu().numpy()
+    want_k, want_v = OC.predict_append(before_k, before_v, storage(k), storage(v), positions, N, layout == K.PAGED,
+                                       table, in_dtype=K.BF16, cache_dtype=cache_dtype,
+                                       k_scale=None if ks is None else ks.cpu().numpy(),
+                                       v_scale=None if vs is None else vs.cpu().numpy(), n_valid=q_lens)
     np.testing.assert_array_equal(storage(cache.k), want_k)
     np.testing.assert_array_equal(storage(cache.v), want_v)
-    assert max_abs(got, _oracle(q, k, v, [0, 0], q_lens)) <= TOL
+    assert max_abs(got, _oracle(q, k, v, positions, q_lens)) <= TOL
 
 
 @pytest.mark.parametrize("cache_dtype", [K.BF16, K.FP8_E4M3])
