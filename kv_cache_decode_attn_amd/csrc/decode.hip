@@ -136,6 +136,20 @@ struct QFrag<KVATTN_BF16, G> {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
+// Register sets in each wave's block ring (blocks in flight + 1), per
+// partition kernel.
+#ifndef KVATTN_RING_VEC
+#define KVATTN_RING_VEC 2
+#endif
+#ifndef KVATTN_RING_BF16
+#define KVATTN_RING_BF16 2
+#endif
+#ifndef KVATTN_RING_FP8
+#define KVATTN_RING_FP8 2
+#endif
+constexpr int kRingVec = KVATTN_RING_VEC;
+constexpr int kRingBf16 = KVATTN_RING_BF16;
+constexpr int kRingFp8 = KVATTN_RING_FP8;
 
 // LDS layout of the partition kernel, in floats: block offsets (int64, one
 // per 16-token block of the partition), then scores/weights [T][G] (reused
@@ -202,30 +216,39 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Streams the blocks jb, jb + kWaves, ... (< nblk) of one wave through two
-// register sets: while one block is consumed the next one's loads are in
-// flight.  `a` already holds block jb when jb < nblk.  Every load is a real
-// block and every iteration issues the same loads, so the compiler's
+// Streams the blocks jb, jb + kWaves, ... (< nblk) of one wave through a
+// ring of NB register sets: while one block is consumed the next NB - 1
+// blocks' loads are in flight.  ring_fill loads the first NB - 1 blocks
+// (before anything else needs the wave, so the first loads overlap other
+// work); stream_ring then consumes every block, refilling the set it has
+// just freed with the block NB - 1 places ahead.  Every load is a real block
+// and every steady-state iteration issues the same loads, so the compiler's
 // load-count waits release exactly the block about to be consumed; the
 // scheduling barriers keep each prefetch ahead of the wait for the block
-// before it.
-template <typename Buf, typename LoadF, typename BodyF>
-__device__ __forceinline__ void stream_blocks(int jb, int nblk, Buf& a, Buf& b, const LoadF& load,
-                                              const BodyF& body) {
-  for (; jb + 2 * kWaves < nblk; jb += 2 * kWaves) {
-    load(jb + kWaves, b);
-    __builtin_amdgcn_sched_barrier(0);
-    body(jb, a);
-    load(jb + 2 * kWaves, a);
-    __builtin_amdgcn_sched_barrier(0);
-    body(jb + kWaves, b);
+// before it.  The last 2 NB - 2 blocks form an explicit tail.
+template <int NB, typename Buf, typename LoadF>
+__device__ __forceinline__ void ring_fill(int jb, int nblk, Buf (&r)[NB], const LoadF& load) {
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i)
+    if (jb + i * kWaves < nblk) load(jb + i * kWaves, r[i]);
+}
+
+template <int NB, typename Buf, typename LoadF, typename BodyF>
+__device__ __forceinline__ void stream_ring(int jb, int nblk, Buf (&r)[NB], const LoadF& load, const BodyF& body) {
+  static_assert(NB >= 2, "ring");
+  for (; jb + (2 * NB - 2) * kWaves < nblk; jb += NB * kWaves) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      load(jb + (i + NB - 1) * kWaves, r[(i + NB - 1) % NB]);
+      __builtin_amdgcn_sched_barrier(0);
+      body(jb + i * kWaves, r[i]);
+    }
   }
-  if (jb < nblk) {
-    const bool two = jb + kWaves < nblk;
-    if (two) load(jb + kWaves, b);
+#pragma unroll
+  for (int i = 0; i < 2 * NB - 2; ++i) {
+    if (i <= NB - 2 && jb + (i + NB - 1) * kWaves < nblk) load(jb + (i + NB - 1) * kWaves, r[(i + NB - 1) % NB]);
     __builtin_amdgcn_sched_barrier(0);
-    body(jb, a);
-    if (two) body(jb + kWaves, b);
+    if (jb + i * kWaves < nblk) body(jb + i * kWaves, r[i % NB]);
   }
 }
 
@@ -242,6 +265,52 @@ __device__ __forceinline__ Raw stream_load(const Raw* p) {
     return __builtin_bit_cast(Raw, __builtin_nontemporal_load(reinterpret_cast<const v2*>(p)));
   }
 }
+
+// K blocks of the MFMA partition passes are staged through LDS.  The matrix
+// core wants lane l to hold key l % 16, so loading K straight into registers
+// reads 64 bytes of each of 16 rows per instruction: half cache lines, which
+// cap a plain read of such blocks at about 5.8 TB/s on MI355X against
+// 6.8 TB/s for whole rows.  Instead each wave copies its block into an LDS
+// slot of its own with 16-byte-per-lane global-to-LDS transfers in which 16
+// lanes read one row completely, and then reads the slot in the MFMA layout.
+// In the slot, 16-byte chunk c of row r sits at position c ^ swz(r), so the
+// 16 rows of one MFMA-layout read fall on distinct LDS banks.
+template <int ROWB>
+struct KStage {
+  static constexpr int BYTES = kBlockTokens * ROWB;  // one 16-token block of one head
+  static constexpr int XFERS = BYTES / 1024;          // 1 KB transfers per block
+  static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+  static constexpr int RP = 256 / ROWB;               // rows per 256 bytes (one pass over the banks)
+  static_assert(XFERS >= 1 && CPR >= 4 && RP >= 1, "row size");
+  __device__ static int swz(int r) { return (r / RP) % CPR; }
+  // byte of the block that lane `lane` of transfer x copies
+  __device__ static int src(int x, int lane) {
+    const int e = x * 1024 + 16 * lane;  // its slot byte
+    const int r = e / ROWB;
+    return r * ROWB + 16 * (((e % ROWB) / 16) ^ swz(r));
+  }
+  // slot byte of chunk c of row r
+  __device__ static int at(int r, int c) { return r * ROWB + 16 * (c ^ swz(r)); }
+};
+// s_waitcnt immediates (gfx9 encoding): all vector memory operations done;
+// all LDS operations done.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+// Cache policy of the K transfers: non-temporal (each byte is read once).
+constexpr int kPolicyNT = 2;
+
+// 16 bytes per lane from `src` into LDS at dst + 16 * lane (dst uniform over
+// the wave), non-temporally.  The body exists in the device pass only: the
+// host pass compiles each kernel just for its launch stub.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, kPolicyNT);
+#endif
+}
+
+// Byte offset of the K slots in the dynamic LDS of an MFMA partition pass
+// whose other arrays take `floats` floats (rounded up to 16 bytes).
+__host__ __device__ constexpr int kslot_offset(int floats) { return ((floats * 4 + 15) / 16) * 16; }
 
 template <int KVT, int D, int G, bool MASK>
 __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
@@ -309,7 +378,7 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   };
 
   // ---- phase 1: scores of every key of the partition ----
-  // Wave w handles blocks w, w + 4, ... (stream_blocks).
+  // Wave w handles blocks w, w + 4, ... (stream_ring).
   auto scores = [&](int jb, const Raw* cur) {
     const bool in_cache = uniform64(offs[jb]) >= 0;
 #pragma unroll
@@ -338,13 +407,15 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
     }
   };
   {
-    Raw ka[NI], kb[NI];
-    if (wave < nblk) load_block(wave, kbase, ka);
-    stream_blocks(wave, nblk, ka, kb, [&](int jb, Raw* r) { load_block(jb, kbase, r); }, scores);
+    Raw kr[kRingVec][NI];
+    auto load_k = [&](int jb, Raw* r) { load_block(jb, kbase, r); };
+    ring_fill(wave, nblk, kr, load_k);
+    stream_ring(wave, nblk, kr, load_k, scores);
   }
-  // The first V block is fetched while the softmax statistics are formed.
-  Raw va[NI], vb[NI];
-  if (wave < nblk) load_block(wave, vbase, va);
+  // The first V blocks are fetched while the softmax statistics are formed.
+  Raw vr[kRingVec][NI];
+  auto load_v = [&](int jb, Raw* r) { load_block(jb, vbase, r); };
+  ring_fill(wave, nblk, vr, load_v);
   __syncthreads();
 
   // ---- phase 2: per-head max and sum; scores -> weights exp2(z - max) ----
@@ -410,7 +481,7 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
         for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(w[h], vf[e], o[h][e]);
     }
   };
-  stream_blocks(wave, nblk, va, vb, [&](int jb, Raw* r) { load_block(jb, vbase, r); }, accumulate);
+  stream_ring(wave, nblk, vr, load_v, accumulate);
 
   // reduce over the TPI rows of the wave (lanes sharing col)
 #pragma unroll
@@ -544,15 +615,22 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
     return uniform64(o >= 0 ? o : 0);
   };
 
-  // ---- phase 1: scores; blocks jb = wave + 4i (stream_blocks) ----
-  // K chunk c of lane (r16, lg): bytes 64c + 16*lg of key r16's row, so one
-  // load instruction reads 64 contiguous bytes of each of 16 rows (a 128-byte
-  // line is read by two instructions back to back, never in quarters).
-  const uint8_t* kbase = p.c.k + r16 * ROWB + 16 * lg;
-  auto load_k = [&](int jb, U4* kr) {
-    const int64_t off = load_off(jb);
+  // ---- phase 1: scores; wave w takes blocks w, w + 4, ... ----
+  // Chunk c of lane (r16, lg) is bytes 64c + 16*lg of key r16's row (read from
+  // the wave's K slot; the next block's transfer is in flight meanwhile).
+  using KST = KStage<ROWB>;
+  uint8_t* kslot = reinterpret_cast<uint8_t*>(lds) +
+                   kslot_offset(decode_lds_floats(T, G, D) + (MASK ? T / 4 : 0)) + wave * KST::BYTES;
+  int ksrc[KST::XFERS], kat[KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) kr[c] = stream_load(reinterpret_cast<const U4*>(kbase + off + 64 * c));
+  for (int x = 0; x < KST::XFERS; ++x) ksrc[x] = KST::src(x, lane);
+#pragma unroll
+  for (int c = 0; c < KC; ++c) kat[c] = KST::at(r16, 4 * c + lg);
+  auto issue_k = [&](int jb) {
+    const uint8_t* blk = p.c.k + load_off(jb);
+#pragma unroll
+    for (int x = 0; x < KST::XFERS; ++x)
+      copy16_to_lds(blk + ksrc[x], kslot + x * 1024);
   };
   auto scores = [&](int jb, const U4* kr) {
     const bool in_cache = uniform64(offs[jb]) >= 0;
@@ -577,10 +655,15 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
       *reinterpret_cast<float4*>(s_lds + r16 * T + tk) = z;
     }
   };
-  {
-    U4 ka[KC], kb[KC];
-    if (wave < nblk) load_k(wave, ka);
-    stream_blocks(wave, nblk, ka, kb, load_k, scores);
+  if (wave < nblk) issue_k(wave);
+  for (int jb = wave; jb < nblk; jb += kWaves) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // block jb is in the slot (only K transfers are in flight)
+    U4 kr[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const U4*>(kslot + kat[c]);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot is read out before the next transfer refills it
+    if (jb + kWaves < nblk) issue_k(jb + kWaves);
+    scores(jb, kr);
   }
   // V: 8 bytes (d 64*hf + 4*r16 ..+3) of each of keys 4*lg + i
   const uint8_t* vbase = p.c.v + (4 * lg) * ROWB + 8 * r16;
@@ -594,8 +677,8 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
             uint2, __builtin_nontemporal_load(reinterpret_cast<const v2u*>(vbase + off + i * ROWB + 128 * hf)));
   };
   // The first V block is fetched while the softmax statistics are formed.
-  uint2 va[HALVES][4], vb[HALVES][4];
-  if (wave < nblk) load_v(wave, va);
+  uint2 vring[kRingBf16][HALVES][4];
+  ring_fill(wave, nblk, vring, load_v);
   __syncthreads();
 
   // ---- phase 2: per-head max and sum; scores -> weights exp2(z - max) ----
@@ -670,7 +753,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
         o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], plo, o[4 * hf + j], 0, 0, 0);
     }
   };
-  stream_blocks(wave, nblk, va, vb, load_v, accumulate);
+  stream_ring(wave, nblk, vring, load_v, accumulate);
 
   __syncthreads();  // every wave is done reading weights; reuse LDS
   float* red = s_lds;  // [kWaves][G][D]
@@ -932,9 +1015,9 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     }
   };
   {
-    Blk ba, bb;
-    if (wave < nblk) load(wave, ba);
-    stream_blocks(wave, nblk, ba, bb, load, process);
+    Blk ring[kRingFp8];
+    ring_fill(wave, nblk, ring, load);
+    stream_ring(wave, nblk, ring, load, process);
   }
 
   // ---- combine the four waves: per head, M = max of the wave maxima ----
@@ -1078,7 +1161,8 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
                                 (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
     hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
   } else if constexpr (KVT == KVATTN_BF16 && G >= 4) {
-    const size_t lds = (size_t)(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
+    const size_t lds = (size_t)kslot_offset(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) +
+                       (size_t)kWaves * KStage<2 * D>::BYTES;
     hipLaunchKernelGGL((decode_partition_bf16_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
   } else {
     const size_t lds = (size_t)(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
