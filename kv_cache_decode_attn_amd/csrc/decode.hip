@@ -296,6 +296,8 @@ struct KStage {
 // all LDS operations done.
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitLgkm0 = 0xC07F;
+// s_waitcnt immediate: at most n vector memory operations outstanding.
+__host__ __device__ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 // Cache policy of the K transfers: non-temporal (each byte is read once).
 constexpr int kPolicyNT = 2;
 
@@ -305,6 +307,18 @@ constexpr int kPolicyNT = 2;
 __device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, kPolicyNT);
+#endif
+}
+
+// Four OCP E4M3FN codes -> two words of two bf16 each (codes 0, 1 and codes
+// 2, 3), exactly: every E4M3FN value is a bf16 value, and gfx950 converts a
+// pair of codes to a bf16 pair in one instruction (scale 1).
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+#else
+  lo = hi = w;
 #endif
 }
 
@@ -620,17 +634,16 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
   // the wave's K slot; the next block's transfer is in flight meanwhile).
   using KST = KStage<ROWB>;
   uint8_t* kslot = reinterpret_cast<uint8_t*>(lds) +
-                   kslot_offset(decode_lds_floats(T, G, D) + (MASK ? T / 4 : 0)) + wave * KST::BYTES;
+                   kslot_offset(decode_lds_floats(T, G, D) + (MASK ? T / 4 : 0)) + wave * 2 * KST::BYTES;
   int ksrc[KST::XFERS], kat[KC];
 #pragma unroll
   for (int x = 0; x < KST::XFERS; ++x) ksrc[x] = KST::src(x, lane);
 #pragma unroll
   for (int c = 0; c < KC; ++c) kat[c] = KST::at(r16, 4 * c + lg);
-  auto issue_k = [&](int jb) {
+  auto issue_k = [&](int jb, uint8_t* slot) {
     const uint8_t* blk = p.c.k + load_off(jb);
 #pragma unroll
-    for (int x = 0; x < KST::XFERS; ++x)
-      copy16_to_lds(blk + ksrc[x], kslot + x * 1024);
+    for (int x = 0; x < KST::XFERS; ++x) copy16_to_lds(blk + ksrc[x], slot + x * 1024);
   };
   auto scores = [&](int jb, const U4* kr) {
     const bool in_cache = uniform64(offs[jb]) >= 0;
@@ -655,15 +668,32 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
       *reinterpret_cast<float4*>(s_lds + r16 * T + tk) = z;
     }
   };
-  if (wave < nblk) issue_k(wave);
-  for (int jb = wave; jb < nblk; jb += kWaves) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // block jb is in the slot (only K transfers are in flight)
+  // Two slots per wave: block jb + 4's transfer is issued into the other slot
+  // before block jb is read (only K transfers are in flight in this phase,
+  // so waiting until at most that one block's transfers are pending means
+  // block jb has landed).  The slot refilled was read out by the previous
+  // step, whose matrix products consumed those reads.
+  auto kstep = [&](int jb, uint8_t* cur, uint8_t* nxt) {
+    if (jb + kWaves < nblk) {
+      issue_k(jb + kWaves, nxt);
+      __builtin_amdgcn_s_waitcnt(wait_vm(KST::XFERS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
     U4 kr[KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const U4*>(kslot + kat[c]);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot is read out before the next transfer refills it
-    if (jb + kWaves < nblk) issue_k(jb + kWaves);
+    for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const U4*>(cur + kat[c]);
     scores(jb, kr);
+  };
+  {
+    uint8_t* slot1 = kslot + KST::BYTES;
+    int jb = wave;
+    if (jb < nblk) issue_k(jb, kslot);
+    for (; jb + kWaves < nblk; jb += 2 * kWaves) {
+      kstep(jb, kslot, slot1);
+      kstep(jb + kWaves, slot1, kslot);
+    }
+    if (jb < nblk) kstep(jb, kslot, slot1);
   }
   // V: 8 bytes (d 64*hf + 4*r16 ..+3) of each of keys 4*lg + i
   const uint8_t* vbase = p.c.v + (4 * lg) * ROWB + 8 * r16;
@@ -875,18 +905,7 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
   for (int t = 0; t < NT; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lsum = 0.f;
 
-  auto cvt4 = [](uint32_t w, uint32_t& lo, uint32_t& hi) {
-    float f[4];
-    fp8x4_to_f32(w, f);
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    bf2 a, c;
-    a[0] = (__bf16)f[0];
-    a[1] = (__bf16)f[1];
-    c[0] = (__bf16)f[2];
-    c[1] = (__bf16)f[3];
-    lo = __builtin_bit_cast(uint32_t, a);
-    hi = __builtin_bit_cast(uint32_t, c);
-  };
+  auto cvt4 = [](uint32_t w, uint32_t& lo, uint32_t& hi) { fp8x4_to_bf16x4(w, lo, hi); };
   auto key_ok = [&](int t) -> bool {
     if (t >= n) return false;
     if constexpr (MASK) return mflag[t] != 0;
@@ -1162,7 +1181,7 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
   } else if constexpr (KVT == KVATTN_BF16 && G >= 4) {
     const size_t lds = (size_t)kslot_offset(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) +
-                       (size_t)kWaves * KStage<2 * D>::BYTES;
+                       (size_t)kWaves * 2 * KStage<2 * D>::BYTES;
     hipLaunchKernelGGL((decode_partition_bf16_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
   } else {
     const size_t lds = (size_t)(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
