@@ -1092,24 +1092,38 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
 // ... and issues all their loads (the (max, sum) pair and its float4 of the
 // output) before using any, keeping its own running max, sum and output
 // (each partition's weight exp2(m_p - M) relative to the running M); the
-// phases are then combined in order through LDS.  Fixed order throughout,
-// so the result is bitwise reproducible.
+// phases are then combined in order through LDS.  The first U partitions of
+// each phase are loaded together with the sequence length (every slot below
+// num_parts is inside the workspace; slots at or past the sequence's own
+// partition count hold stale bytes and are dropped unread), so the usual
+// merge takes one round trip to memory.  Fixed order throughout, so the
+// result is bitwise reproducible.
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge(const DecodeLaunch p) {
   constexpr int NC = D / 4;       // float4 columns
   constexpr int PH = 256 / NC;    // partition phases
-  constexpr int U = 4;            // partitions per batch of loads
+  constexpr int U = 5;            // partitions per batch of loads
   __shared__ float4 pacc[PH][NC];
   __shared__ float pm[PH], pl[PH];
   const int hq = blockIdx.x, b = blockIdx.y;
-  const int T = p.part_tokens;
-  const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
-  const int np = (ctx + T - 1) / T;
-  if (np <= 1) return;  // written by the partition pass
   const int tid = threadIdx.x, c = tid % NC, ph = tid / NC;
   const int64_t slot0 = ((int64_t)b * p.num_q_heads + hq) * p.num_parts;
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + slot0;
   const float4* wo = reinterpret_cast<const float4*>(p.ws_o + slot0 * D) + c;
+  float2 s0[U];
+  float4 x0[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int i = ph + k * PH;
+    if (i < p.num_parts) {
+      s0[k] = ml[i];
+      x0[k] = wo[(int64_t)i * NC];
+    }
+  }
+  const int T = p.part_tokens;
+  const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
+  const int np = (ctx + T - 1) / T;
+  if (np <= 1) return;  // written by the partition pass
   float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   auto add = [&](float2 s, float4 x) {
@@ -1130,7 +1144,10 @@ __global__ void __launch_bounds__(256) decode_merge(const DecodeLaunch p) {
     acc.w = fmaf(w, x.w, acc.w);
     l = fmaf(w, s.y, l);
   };
-  int i = ph;
+#pragma unroll
+  for (int k = 0; k < U; ++k)
+    if (ph + k * PH < np) add(s0[k], x0[k]);
+  int i = ph + U * PH;
   for (; i + (U - 1) * PH < np; i += U * PH) {
     float2 s[U];
     float4 x[U];
