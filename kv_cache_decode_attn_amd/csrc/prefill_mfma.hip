@@ -467,8 +467,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // waits.
   //
   // Fast step (tiles 1 <= it < fast_end: no mask, a predecessor, all three
-  // parts).  It does not rescale o: when its softmax moves a running maximum
-  // the fast loop ends and the rescale runs before the next PV product.
+  // parts).  It does not rescale o itself: when its softmax moves a running
+  // maximum (resc), the caller rescales o before the next PV product.
   auto fast_step = [&](int it, f32x16 (&s_cur)[kCB], f32x16 (&s_nxt)[kCB], const U4 (&p_prev)[kCB][2],
                        U4 (&p_cur)[kCB][2], float (&alpha)[kCB], bool& resc, f32x16 (&o)[kCB][DT]) {
     load_tile(it + kAhead, kAhead - 2);
@@ -527,13 +527,23 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
 #pragma unroll
     for (int c = 0; c < DK; ++c) settle(qf[cb][c]);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  while (it < fast_end) {
+  // Two steps per iteration with the score and weight buffers trading roles,
+  // so the step-to-step hand-over needs no register copies (advance copies
+  // once when a step is left over).  A step whose softmax moved a running
+  // maximum rescales o before the next step's PV product.
+  while (it + 1 < fast_end) {
     fast_step(it, sA, sB, pA, pB, alpha, resc, o);
+    if (resc) rescale(alpha, o);
+    fast_step(it + 1, sB, sA, pB, pA, alpha, resc, o);
+    if (resc) rescale(alpha, o);
+    it += 2;
+  }
+  if (it < fast_end) {
+    fast_step(it, sA, sB, pA, pB, alpha, resc, o);
+    if (resc) rescale(alpha, o);
     advance();
     ++it;
-    if (resc) break;
   }
-  if (resc) rescale(alpha, o);
   for (; it <= ntiles; ++it) {
     slow_step(it, sA, sB, pA, pB, o);
     advance();
