@@ -634,7 +634,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
   // the wave's K slot; the next block's transfer is in flight meanwhile).
   using KST = KStage<ROWB>;
   uint8_t* kslot = reinterpret_cast<uint8_t*>(lds) +
-                   kslot_offset(decode_lds_floats(T, G, D) + (MASK ? T / 4 : 0)) + wave * 2 * KST::BYTES;
+                   kslot_offset(decode_lds_floats(T, G, D) + (MASK ? T / 4 : 0)) + wave * KST::BYTES;
   int ksrc[KST::XFERS], kat[KC];
 #pragma unroll
   for (int x = 0; x < KST::XFERS; ++x) ksrc[x] = KST::src(x, lane);
@@ -668,32 +668,20 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
       *reinterpret_cast<float4*>(s_lds + r16 * T + tk) = z;
     }
   };
-  // Two slots per wave: block jb + 4's transfer is issued into the other slot
-  // before block jb is read (only K transfers are in flight in this phase,
-  // so waiting until at most that one block's transfers are pending means
-  // block jb has landed).  The slot refilled was read out by the previous
-  // step, whose matrix products consumed those reads.
-  auto kstep = [&](int jb, uint8_t* cur, uint8_t* nxt) {
-    if (jb + kWaves < nblk) {
-      issue_k(jb + kWaves, nxt);
-      __builtin_amdgcn_s_waitcnt(wait_vm(KST::XFERS));
-    } else {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    }
+  // One slot per wave (a second slot, letting the next transfer start before
+  // the current block is read, measured slower: the LDS it takes costs a
+  // workgroup per CU).  Only K transfers are in flight in this phase, so
+  // waiting for all of them means block jb has landed; the slot is read out
+  // before the next transfer refills it.
+  if (wave < nblk) issue_k(wave, kslot);
+  for (int jb = wave; jb < nblk; jb += kWaves) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     U4 kr[KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const U4*>(cur + kat[c]);
+    for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const U4*>(kslot + kat[c]);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (jb + kWaves < nblk) issue_k(jb + kWaves, kslot);
     scores(jb, kr);
-  };
-  {
-    uint8_t* slot1 = kslot + KST::BYTES;
-    int jb = wave;
-    if (jb < nblk) issue_k(jb, kslot);
-    for (; jb + kWaves < nblk; jb += 2 * kWaves) {
-      kstep(jb, kslot, slot1);
-      kstep(jb + kWaves, slot1, kslot);
-    }
-    if (jb < nblk) kstep(jb, kslot, slot1);
   }
   // V: 8 bytes (d 64*hf + 4*r16 ..+3) of each of keys 4*lg + i
   const uint8_t* vbase = p.c.v + (4 * lg) * ROWB + 8 * r16;
@@ -1198,7 +1186,7 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
   } else if constexpr (KVT == KVATTN_BF16 && G >= 4) {
     const size_t lds = (size_t)kslot_offset(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) +
-                       (size_t)kWaves * 2 * KStage<2 * D>::BYTES;
+                       (size_t)kWaves * KStage<2 * D>::BYTES;
     hipLaunchKernelGGL((decode_partition_bf16_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
   } else {
     const size_t lds = (size_t)(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
