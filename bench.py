@@ -491,7 +491,8 @@ def main(argv=None):
         "two_call_step": {"ms_per_step": ms2, "GB/s": step_bytes / (ms2 * 1e-3) / 1e9, "per_launch": launch2,
                           "attn_decode_GB/s": w.decode_bytes() / (launch2["attn_decode"]["mean_ms"] * 1e-3) / 1e9},
         "roofline": {"bound": "hbm",
-                     "kernel": "attn_decode_append (decode_partition with the fused append + decode_merge)",
+                     "kernel": "attn_decode_append (decode_partition_bf16_mfma with the fused append, "
+                               "then decode_merge)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "bytes_per_launch": step_bytes, "traffic": decode_traffic()},
     }
@@ -528,7 +529,8 @@ def main(argv=None):
         tf = pf.flops() / (msp * 1e-3) / 1e12
         extra["prefill8k"] = {"config": pf.config(), "ms_per_step": msp, "TFLOP/s": tf,
                               "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS, "flops": pf.flops(),
-                              "roofline": {"bound": "mfma", "kernel": "attn_prefill (kv_append + prefill_mfma_kernel)",
+                              "roofline": {"bound": "mfma",
+                                           "kernel": "attn_prefill (prefill_mfma_kernel, which also writes the cache)",
                                            "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                            "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
         del pf

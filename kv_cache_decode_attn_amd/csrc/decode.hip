@@ -540,9 +540,10 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
 // ---------------------------------------------------------------------------
 // bf16 cache with G >= 4 query heads per KV head: the partition pass with
 // both contractions on v_mfma_f32_16x16x16_bf16 and the same three phases.
-//   phase 1  S^T[key][h] = K Q^T per 16-token block.  A = K as loaded, no
-//            conversion: lane l holds key l%16, 16-byte chunks c at row
-//            bytes 64c + 16(l/16) (k-step 2c + u takes half u of chunk c);
+//   phase 1  S^T[key][h] = K Q^T per 16-token block.  A = K, staged
+//            through the wave's LDS slot (KStage) and read from it so that
+//            lane l holds key l%16, 16-byte chunks c at row bytes
+//            64c + 16(l/16) (k-step 2c + u takes half u of chunk c);
 //            B = q of head l%16 in the same d order (zero for heads >= G).
 //            Lane l gets keys 4(l/16) + r of head l%16, stored head-major.
 //   phase 2  as in decode_partition: per head max, exp2 weights and sum.
