@@ -15,8 +15,9 @@ Other workloads run in the same invocation and are reported under
 "workloads": the padded 32-layer MHA decode (batch 8, 4096-position
 contiguous cache, key padding mask), the 80-layer fp8 long-context decode
 (batch 1, 64/8 heads, 131,073 keys per layer), the causal 8192-token
-prefill that writes the paged cache, a copy-on-write fan-out of 4096 paged
-blocks and a contiguous beam reorder (32 rows of 4096 positions).
+prefill that writes the paged cache, a 2048-token chunked prefill against
+6144 cached positions, a copy-on-write fan-out of 4096 paged blocks and a
+contiguous beam reorder (32 rows of 4096 positions).
 
 Timing: W untimed warm-up steps, then K steps bracketed by synchronize +
 HIP events on the stream the library launches on (torch's current stream).
@@ -348,6 +349,47 @@ class CausalPrefill:
                 "head_dim": self.D, "dtype": "bf16", "causal": True, "writes_paged_cache": True}
 
 
+class ChunkedPrefill:
+    """Chunked prefill against a paged bf16 cache: a 2,048-token chunk of a
+    Llama-3-8B-shaped layer (32/8 heads, d 128) at positions 6,144..8,191 that
+    attends the 6,144 cached positions and, causally, itself, and stores its
+    rows in the cache (attn_prefill with attend_prefix)."""
+
+    name = "chunked-prefill-6144-cached-2048-new-gqa"
+
+    def __init__(self, wid=8, P=6144, n=2048):
+        self.Hq, self.Hkv, self.D, self.P, self.n = 32, 8, 128, P, n
+        std = 1.0 / math.sqrt(self.D)
+        nb = synth.blocks_for(P + n)
+        table, nblk = synth.block_table([nb], nb, (wid, synth.T_PERM))
+        self.table = torch.from_numpy(table).to(DEV)
+        self.cache = K.KVCache.paged(nblk, self.Hkv, self.D, K.BF16, DEV)
+        kp = synth.normal_device((1, self.Hkv, P, self.D), (wid, synth.T_K), std=std)
+        vp = synth.normal_device((1, self.Hkv, P, self.D), (wid, synth.T_V), std=std)
+        K.kv_append(self.cache, kp, vp, torch.zeros(1, dtype=torch.int32, device=DEV), block_table=self.table)
+        del kp, vp
+        self.q = synth.normal_device((1, self.Hq, n, self.D), (wid, synth.T_Q), std=std)
+        self.k = synth.normal_device((1, self.Hkv, n, self.D), (wid, synth.T_KNEW), std=std)
+        self.v = synth.normal_device((1, self.Hkv, n, self.D), (wid, synth.T_VNEW), std=std)
+        self.positions = torch.tensor([P], dtype=torch.int32, device=DEV)
+        self.out = torch.empty((1, self.Hq, n, self.D), dtype=torch.float32, device=DEV)
+        torch.cuda.synchronize()
+
+    def flops(self):
+        # QK^T and PV over the attended (query, key) pairs: every cached key,
+        # and the causal triangle of the chunk incl. its diagonal
+        pairs = self.n * self.P + self.n * (self.n + 1) // 2
+        return 4 * self.D * self.Hq * pairs
+
+    def step(self, i, ev=None):
+        K.attn_prefill(self.q, self.k, self.v, cache=self.cache, positions=self.positions, block_table=self.table,
+                       attend_prefix=True, out=self.out)
+
+    def config(self):
+        return {"workload": self.name, "batch": 1, "q_heads": self.Hq, "kv_heads": self.Hkv, "cached": self.P,
+                "new": self.n, "head_dim": self.D, "dtype": "bf16", "causal": True, "writes_paged_cache": True}
+
+
 class CowBlockCopy:
     """Copy-on-write fan-out: 4096 whole-block copies in a Llama-3-8B-shaped
     bf16 paged pool (8 KV heads x 16 positions x 128 = 32 KiB per block per
@@ -444,8 +486,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode8b,padded32,longctx70b,prefill8k,cowcopy,beamreorder",
-                    help="comma list: decode8b (headline), padded32, longctx70b, prefill8k, cowcopy, beamreorder")
+    ap.add_argument("--workloads", default="decode8b,padded32,longctx70b,prefill8k,chunkprefill,cowcopy,beamreorder",
+                    help="comma list: decode8b (headline), padded32, longctx70b, prefill8k, chunkprefill, cowcopy, "
+                         "beamreorder")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the headline workload the oracle runs")
     args = ap.parse_args(argv)
@@ -534,6 +577,18 @@ def main(argv=None):
                                            "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                            "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
         del pf
+        torch.cuda.empty_cache()
+    if "chunkprefill" in names:
+        cp = ChunkedPrefill()
+        msc, _ = time_steps(cp, max(20, args.steps), max(50, args.warmup))
+        tf = cp.flops() / (msc * 1e-3) / 1e12
+        extra["chunkprefill"] = {"config": cp.config(), "ms_per_step": msc, "TFLOP/s": tf,
+                                 "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS, "flops": cp.flops(),
+                                 "roofline": {"bound": "mfma", "kernel": "attn_prefill (prefill_mfma_kernel, "
+                                              "cached prefix gathered through the block table)",
+                                              "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                              "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
+        del cp
         torch.cuda.empty_cache()
     for key, cls_ in (("cowcopy", CowBlockCopy), ("beamreorder", BeamReorder)):
         if key not in names:

@@ -59,6 +59,16 @@
 //                            row sum is the sum of the same weights used for O.
 // Masked keys (causal, beyond q_len, key_mask) get P = 0 and their V rows are
 // staged as zeros, so non-finite padding never reaches O.
+//
+// Cached prefix (chunked prefill, verification of drafted tokens: query t at
+// position P + t also attends the cached positions 0 .. P-1; "KV Cache"
+// (heepie.pages.dev), section "Prefill and Decode", and "Transformer
+// Attention Masks and KV-Cache Inference", section "Prefill and decode
+// stages").  Keys are then indexed from position 0; tiles are gathered row
+// by row, a prefix row through the block table (or the contiguous cache) and
+// a new row from the new K/V, with per-lane global-to-LDS transfers.  The
+// workgroup first checks that every prefix block id is valid; if one is not,
+// its positions are masked keys and every tile takes the masked step.
 #include <math.h>
 
 #include <type_traits>
@@ -159,14 +169,33 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
 // it wait for every load in flight before any LDS read of the tile ring;
 // completion is awaited explicitly (finish_tile) before a barrier publishes
 // the tile.
-__device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint8_t* lds, int voffset) {
+__device__ __forceinline__ void load_lds16(const i32x4& rsrc_in, uint8_t* lds, int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  // the descriptor is the same in every lane; say so, so that it is held in
+  // scalar registers as the instruction requires
+  const i32x4 rsrc = {__builtin_amdgcn_readfirstlane(rsrc_in[0]), __builtin_amdgcn_readfirstlane(rsrc_in[1]),
+                      __builtin_amdgcn_readfirstlane(rsrc_in[2]), __builtin_amdgcn_readfirstlane(rsrc_in[3])};
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "buffer_load_dwordx4 %1, %2, 0 offen lds"
       :
       : "s"(m0), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+#endif
+}
+// 16 bytes per lane from the global address src straight into LDS at
+// lds + 16 * lane (lds uniform over the wave): the per-lane-address form,
+// for rows gathered from the cache.  Inline assembly for the same reason as
+// load_lds16: the compiler must not wait on the transfer before LDS reads.
+__device__ __forceinline__ void load_lds16_ptr(const uint8_t* src, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(m0), "v"(src)
       : "memory", "m0");
 #endif
 }
@@ -179,7 +208,7 @@ __device__ __forceinline__ s16x4 read_tr16(const uint8_t* lds) {
 #endif
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool PREFIX>
 __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const PrefillLaunch a, int hw) {
   using GE = Geo<D>;
   constexpr int DK = D / 16;  // 16-wide d chunks of the QK^T contraction
@@ -200,6 +229,13 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   const int n_max = a.n_max;
   const int qlen = a.q_lens ? min(max(a.q_lens[b], 0), n_max) : n_max;
   const int P = a.positions ? max(a.positions[b], 0) : 0;
+  // Keys are indexed from kbase: the cached prefix (positions 0 .. P-1, read
+  // from the cache) when it is attended, else the first new token.  Query t
+  // sits at position P + t, i.e. at key index t + QO; Ltot keys exist.
+  constexpr bool prefix = PREFIX;  // a.has_cache && a.attend_prefix
+  const int kbase = prefix ? 0 : P;
+  const int QO = P - kbase;
+  const int Ltot = QO + qlen;
 
   // this wave's two column blocks: head hb[cb], first row rb[cb]
   int hb[kCB], rb[kCB];
@@ -223,13 +259,39 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     }
     return;
   }
-  const int key_end = CAUSAL ? min(qlen, q_wg + rows_wg) : qlen;  // workgroup bound
-  const int wave_end = CAUSAL ? min(qlen, row_hi) : qlen;          // this wave's bound
+  const int key_end = CAUSAL ? min(Ltot, QO + q_wg + rows_wg) : Ltot;  // workgroup bound
+  const int wave_end = CAUSAL ? min(Ltot, QO + row_hi) : Ltot;          // this wave's bound
   const int ntiles = (key_end + kKeys - 1) / kKeys;
   const int wave_tiles = (wave_end + kKeys - 1) / kKeys;
-  // Tiles below fast_end need no mask: every key is real and causally
-  // visible to every query of the wave.
-  const int fast_end = MASK ? 0 : min(wave_tiles, (CAUSAL ? min(qlen, row_lo + 1) : qlen) / kKeys);
+  // Whether every prefix position lies in the cache (a valid block id for
+  // each of its blocks): one scan of the sequence's table row by the
+  // workgroup.  Prefix positions outside the cache are masked keys.
+  bool prefix_ok = true;
+  if (PREFIX && P > 0) {
+    __shared__ int bad;
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    const CacheView& cv = a.c;
+    if (cv.paged) {
+      const int nb = (P + kBlockTokens - 1) / kBlockTokens;
+      int mine = nb > cv.max_blocks;
+      const int32_t* row = cv.block_table + (int64_t)b * cv.max_blocks;
+      for (int j = tid; j < min(nb, cv.max_blocks); j += kThreads) {
+        const int32_t blk = row[j];
+        mine |= (blk < 0) | ((int64_t)blk >= cv.num_blocks);
+      }
+      if (mine) bad = 1;
+    } else if (tid == 0 && (int64_t)P > cv.capacity) {
+      bad = 1;
+    }
+    __syncthreads();
+    prefix_ok = __builtin_amdgcn_readfirstlane(bad) == 0;  // uniform (the loop bounds depend on it)
+  }
+  // Tiles below fast_end need no mask: every key is real, in the cache and
+  // causally visible to every query of the wave.
+  const int fast_end = (MASK || !prefix_ok)
+                           ? 0
+                           : min(wave_tiles, (CAUSAL ? min(Ltot, QO + row_lo + 1) : Ltot) / kKeys);
 
   const int64_t head_bytes = (int64_t)n_max * D * 2;
   const uint8_t* kg = a.k + ((int64_t)b * a.num_kv_heads + g) * head_bytes;
@@ -260,7 +322,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // it return zeros, so rows of absent keys are staged as zeros.  With a key
   // mask, rows of masked keys are zeroed by the loading wave once its loads
   // have landed, so no non-finite padding reaches the PV product.
-  const int key_lim = min(qlen, ntiles * kKeys);
+  const int key_lim = min(Ltot, ntiles * kKeys);
   int koff[GE::LOADS], voff[GE::LOADS], lrow[GE::LOADS];  // per lane, tile independent
 #pragma unroll
   for (int i = 0; i < GE::LOADS; ++i) {
@@ -270,16 +332,25 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     koff[i] = r * GE::RB + (cs ^ GE::swz_k(r)) * 16;
     voff[i] = r * GE::RB + (cs ^ GE::swz_v(r)) * 16;
   }
+  // With a prefix, every tile is gathered row by row: key index k is cache
+  // position kbase + k (below P) or new token k - QO.  A row that is absent
+  // (k >= Ltot) or outside the cache is read from new token 0 (a valid
+  // address) and zeroed once it has landed, like a masked key's V row.
+  constexpr bool zero_rows = MASK || PREFIX;
   // A key is valid if it is a real token (< q_len) and, with a key mask, its
   // mask byte (at absolute position P + key) is nonzero.  The byte is read at
   // a clamped index and the terms are combined bitwise, so the test has no
   // branch (a branchy form of this test was miscompiled).
   const int mask_last = MASK ? (int)min<int64_t>(a.key_mask_stride, (int64_t)INT32_MAX) - 1 : 0;
   auto key_valid = [&](int key) -> bool {
-    bool ok = key < qlen;
+    bool ok = key < Ltot;
     if (MASK) {
-      const uint8_t mb = mrow[min(P + key, mask_last)];  // always inside the mask row
-      ok = ok & (P + key <= mask_last) & (mb != 0);
+      const uint8_t mb = mrow[min(kbase + key, mask_last)];  // always inside the mask row
+      ok = ok & (kbase + key <= mask_last) & (mb != 0);
+    }
+    if (PREFIX && !prefix_ok) {  // uniform: only with prefix positions outside the cache
+      const int ka = kbase + key;
+      ok = ok & ((ka >= P) || (position_offset(a.c, b, g, ka) >= 0));
     }
     return ok;
   };
@@ -293,14 +364,40 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     uint8_t* kl = smem + (t % kBufs) * GE::BUF;
     uint8_t* vl = kl + GE::KBYTES;
     if (wave >= GE::LWAVES) return;
-    if (MASK) {
+    if constexpr (zero_rows) {
       uint32_t info = 0;
 #pragma unroll
       for (int i = 0; i < GE::LOADS; ++i) {
         const int key = kt0 + lrow[i];
-        if (key < key_lim && !key_valid(key)) info |= 1u << i;
+        // without a prefix, rows at or past key_lim arrive as zeros already
+        if ((prefix || key < key_lim) && !key_valid(key)) info |= 1u << i;
       }
       pending |= (uint64_t)info << (8 * slot);
+    }
+    if constexpr (PREFIX) {
+#pragma unroll
+      for (int i = 0; i < GE::LOADS; ++i) {
+        const int key = kt0 + lrow[i];
+        const int ka = kbase + key;
+        const uint8_t* rk = kg;  // new token 0: the stand-in for absent rows
+        const uint8_t* rv = vg;
+        if (key < Ltot) {
+          if (ka >= P) {
+            rk = kg + (int64_t)(ka - P) * GE::RB;
+            rv = vg + (int64_t)(ka - P) * GE::RB;
+          } else {
+            const int64_t off = position_offset(a.c, b, g, ka);
+            if (off >= 0) {
+              rk = a.c.k + off;
+              rv = a.c.v + off;
+            }
+          }
+        }
+        const int piece = wave * GE::LOADS + i;
+        load_lds16_ptr(rk + (koff[i] - lrow[i] * GE::RB), kl + piece * 1024);
+        load_lds16_ptr(rv + (voff[i] - lrow[i] * GE::RB), vl + piece * 1024);
+      }
+      return;
     }
     const int nbytes = max(key_lim - kt0, 0) * GE::RB;
     const i32x4 kr = make_rsrc(kg + (int64_t)kt0 * GE::RB, nbytes);
@@ -319,7 +416,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     constexpr int vm = decltype(younger)::value * 2 * GE::LOADS;  // loads per tile: K and V
     static_assert(vm < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8));  // vmcnt(vm)
-    if (MASK) {
+    if constexpr (zero_rows) {
       uint8_t* vl = smem + (t % kBufs) * GE::BUF + GE::KBYTES;
       const uint32_t info = (uint32_t)pending & 0xffu;
       pending >>= 8;
@@ -374,7 +471,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
           const bool kok = key_valid(key);
 #pragma unroll
           for (int cb = 0; cb < kCB; ++cb) {
-            const bool ok = kok & (!CAUSAL || key <= tq[cb]);
+            const bool ok = kok & (!CAUSAL || key <= tq[cb] + QO);
             s[cb][r] = ok ? s[cb][r] : -INFINITY;
           }
         }
@@ -596,21 +693,27 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool PREFIX>
 int launch_typed(const PrefillLaunch& a, hipStream_t s) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int hw = G < kBlocks ? G : kBlocks;
   const int rows = 32 * kBlocks / hw;
   const dim3 grid(a.num_q_heads / hw, (a.n_max + rows - 1) / rows, a.batch);
   const size_t lds = kBufs * Geo<D>::BUF;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, CAUSAL, MASK>), grid, dim3(kThreads), lds, s, a, hw);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, CAUSAL, MASK, PREFIX>), grid, dim3(kThreads), lds, s, a, hw);
   return hipGetLastError() == hipSuccess ? KVATTN_OK : KVATTN_ELAUNCH;
 }
 
-template <int D>
+template <int D, bool PREFIX>
 int launch_flags(const PrefillLaunch& a, hipStream_t s) {
-  if (a.causal) return a.key_mask ? launch_typed<D, true, true>(a, s) : launch_typed<D, true, false>(a, s);
-  return a.key_mask ? launch_typed<D, false, true>(a, s) : launch_typed<D, false, false>(a, s);
+  if (a.causal)
+    return a.key_mask ? launch_typed<D, true, true, PREFIX>(a, s) : launch_typed<D, true, false, PREFIX>(a, s);
+  return a.key_mask ? launch_typed<D, false, true, PREFIX>(a, s) : launch_typed<D, false, false, PREFIX>(a, s);
+}
+
+template <int D>
+int launch_prefix(const PrefillLaunch& a, hipStream_t s) {
+  return (a.has_cache && a.attend_prefix) ? launch_flags<D, true>(a, s) : launch_flags<D, false>(a, s);
 }
 
 }  // namespace
@@ -618,14 +721,16 @@ int launch_flags(const PrefillLaunch& a, hipStream_t s) {
 bool prefill_mfma_supports(const PrefillLaunch& a) {
   if (a.dtype != KVATTN_BF16) return false;
   if (a.head_dim != 64 && a.head_dim != 128) return false;
-  if (a.has_cache && a.attend_prefix) return false;  // cached prefix: general kernel
+  // a cached prefix is read by this kernel from a bf16 cache (same rows as
+  // the new K/V); other cache types take the general kernel
+  if (a.has_cache && a.attend_prefix && a.cache_dtype != KVATTN_BF16) return false;
   if ((int64_t)a.n_max * a.head_dim * 2 >= ((int64_t)1 << 31) - 4096) return false;  // 32-bit buffer offsets
   const int G = a.num_q_heads / a.num_kv_heads;
   return G == 1 || G == 2 || G == 4 || G == 8;
 }
 
 int launch_prefill_mfma(const PrefillLaunch& a, hipStream_t s) {
-  return a.head_dim == 64 ? launch_flags<64>(a, s) : launch_flags<128>(a, s);
+  return a.head_dim == 64 ? launch_prefix<64>(a, s) : launch_prefix<128>(a, s);
 }
 
 }  // namespace kvattn

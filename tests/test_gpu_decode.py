@@ -130,14 +130,16 @@ def test_fp32_cache(d):
     assert max_abs(c.run(64).cpu().numpy(), c.oracle()) <= TOL
 
 
-def test_key_mask_with_nan_poisoned_padding():
+@pytest.mark.parametrize("Hq,Hkv,d", [(8, 2, 128), (16, 2, 64), (4, 4, 64)])
+def test_key_mask_with_nan_poisoned_padding(Hq, Hkv, d):
     """Masked keys carry NaN K/V: weights exactly 0, outputs finite
     ("Transformer Attention Masks and KV-Cache Inference", "Padding mask and
-    batch length")."""
+    batch length").  Group 4 and 8 (matrix-core pass, K staged through LDS
+    with 256- and 128-byte rows) and group 1 (vector pass)."""
     lens = [100, 37, 260]
     mask = synth.random_mask((3, 272), 0.6, (5, synth.T_MASK))
     mask[:, 0] = 1
-    c = Case(3, 8, 2, 128, lens, seed=5, mask=mask)
+    c = Case(3, Hq, Hkv, d, lens, seed=5, mask=mask)
     for part in (64, 0):
         got = c.run(part).cpu().numpy()
         assert np.isfinite(got).all()
@@ -202,8 +204,11 @@ def test_one_key_returns_its_value():
         assert max_abs(got[:, h], want) <= 1e-6
 
 
-def test_invalid_block_ids_read_as_masked():
-    c = Case(2, 4, 2, 64, [64, 64], seed=12)
+@pytest.mark.parametrize("Hq,d", [(4, 64), (8, 128), (16, 64)])
+def test_invalid_block_ids_read_as_masked(Hq, d):
+    """Out-of-range and negative block ids: those blocks read as masked
+    (group 2: vector pass; groups 4 and 8: matrix-core pass)."""
+    c = Case(2, Hq, 2, d, [64, 64], seed=12)
     bad = c.table.clone()
     bad[0, 1] = 10 ** 6   # positions 16..31 of sequence 0 unreadable
     bad[1, 3] = -1        # positions 48..63 of sequence 1

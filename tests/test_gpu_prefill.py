@@ -261,3 +261,130 @@ def test_mfma_prefill_each_masked_key_gets_zero_weight(causal):
             assert np.all(got[:, c] == 0.0), masked
         rows = [t for t in range(N) if mask[0, :t + 1 if causal else N].any()]
         assert np.abs(got[rows].sum(axis=1) - 1.0).max() <= 1e-6, masked
+
+
+def _prefix_case(B, Hq, Hkv, d, P, n2, layout, seed, poison=None):
+    """A bf16 cache holding positions 0 .. P[b]-1 of each sequence (appended
+    from seeded rows; `poison` marks prefix positions whose K/V are set to NaN
+    first), and a padded chunk of n2[b] new tokens."""
+    P = np.asarray(P, np.int32)
+    n2 = np.asarray(n2, np.int32)
+    n_max = int(n2.max())
+    total = int((P + n2).max())
+    kp = synth.normal((B, Hkv, total, d), (seed, synth.T_K), torch.bfloat16, std=1 / math.sqrt(d))
+    vp = synth.normal((B, Hkv, total, d), (seed, synth.T_V), torch.bfloat16, std=1 / math.sqrt(d))
+    if poison is not None:
+        for b, s in zip(*np.nonzero(poison[:, :total])):
+            kp[b, :, s] = float("nan")
+            vp[b, :, s] = float("nan")
+    q2, k2, v2 = _inputs(B, Hq, Hkv, n_max, d, torch.bfloat16, seed + 1, std=1 / math.sqrt(d))
+    for b in range(B):
+        q2[b, :, n2[b]:] = 0
+        k2[b, :, n2[b]:] = 0
+        v2[b, :, n2[b]:] = 0
+    table = tdev = None
+    if layout == K.PAGED:
+        nbs = [synth.blocks_for(int(P[b] + n2[b])) for b in range(B)]
+        table, nblk = synth.block_table(nbs, max(nbs), (seed, synth.T_PERM))
+        cache = K.KVCache.paged(nblk, Hkv, d, K.BF16, DEV)
+        tdev = torch.from_numpy(table).to(DEV)
+    else:
+        cap = -(-total // 16) * 16
+        cache = K.KVCache.contiguous(B, Hkv, cap, d, K.BF16, DEV)
+    cache.k.zero_()
+    cache.v.zero_()
+    zeros = torch.zeros(B, dtype=torch.int32, device=DEV)
+    K.kv_append(cache, kp.to(DEV), vp.to(DEV), zeros, block_table=tdev, n_valid=torch.from_numpy(P).to(DEV))
+    prefix = ([f64(kp[b, :, :P[b]]) for b in range(B)], [f64(vp[b, :, :P[b]]) for b in range(B)])
+    return cache, table, tdev, q2, k2, v2, P, n2, prefix
+
+
+@pytest.mark.parametrize("G,d", [(4, 128), (8, 64), (1, 128), (2, 64)])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("layout", [K.PAGED, K.CONTIGUOUS])
+def test_mfma_chunked_prefill_attends_cached_prefix(G, d, causal, layout):
+    """bf16 chunk against a bf16 cached prefix on the matrix-core kernel:
+    prefixes that are not whole tiles (77 and 130 positions), ragged chunks,
+    causal and not; the chunk's rows are also stored in the cache."""
+    B, Hkv = 2, 2
+    Hq = G * Hkv
+    cache, table, tdev, q2, k2, v2, P, n2, prefix = _prefix_case(B, Hq, Hkv, d, [77, 130], [100, 37], layout,
+                                                                   60 + G + d)
+    got = K.attn_prefill(q2.to(DEV), k2.to(DEV), v2.to(DEV), cache=cache, positions=torch.from_numpy(P).to(DEV),
+                         q_lens=torch.from_numpy(n2).to(DEV), block_table=tdev, causal=causal,
+                         attend_prefix=True).cpu().numpy()
+    want = _oracle(q2, k2, v2, P, n2, causal=causal, prefix=prefix)
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= TOL
+    for b in range(B):
+        assert np.all(got[b, :, n2[b]:] == 0.0)
+    # the chunk's K rows were stored at positions P[b] + i
+    kc = storage(cache.k)
+    k2s = storage(k2)
+    for b in range(B):
+        for i in (0, int(n2[b]) - 1):
+            p = int(P[b]) + i
+            if layout == K.PAGED:
+                row = kc[table[b][p // 16], :, p % 16]
+            else:
+                row = kc[b, :, p]
+            np.testing.assert_array_equal(row, k2s[b, :, i])
+
+
+def test_mfma_chunked_prefill_long_prefix_many_tiles():
+    """A 1,000-position prefix and a 300-token chunk (GQA 4, d 128): most
+    tiles take the unmasked step; equals the matching rows of a one-shot
+    prefill of all 1,300 tokens."""
+    B, Hq, Hkv, d = 1, 8, 2, 128
+    N, P0 = 1300, 1000
+    q, k, v = _inputs(B, Hq, Hkv, N, d, torch.bfloat16, 70, std=1 / math.sqrt(d))
+    nb = synth.blocks_for(N)
+    table, nblk = synth.block_table([nb], nb, (70, synth.T_PERM))
+    tdev = torch.from_numpy(table).to(DEV)
+    cache = K.KVCache.paged(nblk, Hkv, d, K.BF16, DEV)
+    P = torch.tensor([P0], dtype=torch.int32, device=DEV)
+    K.kv_append(cache, k.to(DEV), v.to(DEV), torch.zeros(1, dtype=torch.int32, device=DEV), block_table=tdev,
+                n_valid=P)
+    got = K.attn_prefill(q[:, :, P0:].contiguous().to(DEV), k[:, :, P0:].contiguous().to(DEV),
+                         v[:, :, P0:].contiguous().to(DEV), cache=cache, positions=P, block_table=tdev,
+                         attend_prefix=True).cpu().numpy()
+    full = _oracle(q, k, v, [0], [N])
+    assert max_abs(got[0], full[0, :, P0:]) <= TOL
+
+
+def test_mfma_prefix_key_mask_nan_poisoned_and_verify_shape():
+    """Key mask over absolute positions with NaN in the masked cached rows
+    (weights exactly 0, outputs finite), and a 4-token chunk (the shape of
+    checking drafted tokens) after 500 cached positions."""
+    B, Hq, Hkv, d = 2, 16, 2, 128
+    P, n2 = [200, 500], [64, 4]
+    mask = synth.random_mask((B, 520), 0.7, (71, synth.T_MASK))
+    mask[:, 0] = 1
+    poison = (mask == 0)
+    poison[:, 200:] = False   # only cached rows are poisoned
+    cache, table, tdev, q2, k2, v2, P, n2, prefix = _prefix_case(B, Hq, Hkv, d, P, n2, K.PAGED, 72, poison=poison)
+    got = K.attn_prefill(q2.to(DEV), k2.to(DEV), v2.to(DEV), cache=cache, positions=torch.from_numpy(P).to(DEV),
+                         q_lens=torch.from_numpy(n2).to(DEV), block_table=tdev,
+                         key_mask=torch.from_numpy(mask).to(DEV), attend_prefix=True).cpu().numpy()
+    assert np.isfinite(got).all()
+    # the oracle sees the masked positions as masked, whatever they hold
+    clean = ([np.nan_to_num(x, nan=0.0) for x in prefix[0]], [np.nan_to_num(x, nan=0.0) for x in prefix[1]])
+    want = _oracle(q2, k2, v2, P, n2, key_mask=mask, prefix=clean)
+    assert max_abs(got, want) <= TOL
+
+
+def test_mfma_prefix_invalid_block_ids_are_masked():
+    """Prefix positions whose block id is out of range or negative are masked
+    keys (as for decode); every tile then takes the masked step."""
+    B, Hq, Hkv, d = 1, 8, 2, 64
+    cache, table, tdev, q2, k2, v2, P, n2, prefix = _prefix_case(B, Hq, Hkv, d, [96], [70], K.PAGED, 73)
+    bad = tdev.clone()
+    bad[0, 1] = 10 ** 6   # positions 16..31
+    bad[0, 4] = -1        # positions 64..79
+    got = K.attn_prefill(q2.to(DEV), k2.to(DEV), v2.to(DEV), cache=cache, positions=torch.from_numpy(P).to(DEV),
+                         block_table=bad, attend_prefix=True).cpu().numpy()
+    mask = np.ones((1, 96 + 70), np.uint8)
+    mask[0, 16:32] = 0
+    mask[0, 64:80] = 0
+    want = _oracle(q2, k2, v2, P, n2, key_mask=mask, prefix=prefix)
+    assert max_abs(got, want) <= TOL
