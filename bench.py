@@ -14,8 +14,10 @@ HBM bytes per step / step time, in GB/s.  The same step as two calls
 Other workloads run in the same invocation and are reported under
 "workloads": the padded 32-layer MHA decode (batch 8, 4096-position
 contiguous cache, key padding mask), the 80-layer fp8 long-context decode
-(batch 1, 64/8 heads, 131,073 keys per layer), the causal 8192-token
-prefill that writes the paged cache, a 2048-token chunked prefill against
+(batch 1, 64/8 heads, 131,073 keys per layer), the check of 4 drafted
+tokens per sequence on the Llama-3-8B decode workload (append, then all 4
+attended together), the causal 8192-token prefill that writes the paged
+cache, a 2048-token chunked prefill against
 6144 cached positions, a copy-on-write fan-out of 4096 paged blocks and a
 contiguous beam reorder (32 rows of 4096 positions).
 
@@ -390,6 +392,67 @@ class ChunkedPrefill:
                 "new": self.n, "head_dim": self.D, "dtype": "bf16", "causal": True, "writes_paged_cache": True}
 
 
+class PagedVerify:
+    """Checking drafted tokens: the Llama-3-8B-shaped paged decode workload
+    (batch 32, 32/8 heads, d 128, bf16, cached lengths U[1, 8192]) with 4 new
+    tokens per sequence appended (kv_append) and attended together, causal
+    among themselves (attn_decode_multi: 16 query columns per KV head)."""
+
+    name = "llama3-8b-paged-gqa-verify-4-tokens"
+
+    def __init__(self, replicas=4, wid=9, n_q=4):
+        self.B, self.Hq, self.Hkv, self.D, self.nq = 32, 32, 8, 128, n_q
+        self.cached = synth.uniform_lengths(self.B, 1, 8192, (wid, synth.T_LENS))
+        self.ctx = (self.cached + n_q).astype(np.int32)
+        self.max_seq_len = 8192 + n_q
+        nbs = [synth.blocks_for(c) for c in self.ctx]
+        self.max_blocks = synth.blocks_for(self.max_seq_len)
+        table, self.nblk = synth.block_table(nbs, self.max_blocks, (wid, synth.T_PERM))
+        self.table = torch.from_numpy(table).to(DEV)
+        width = int(self.ctx.max())
+        src_k = synth.normal_device((self.B, self.Hkv, width, self.D), (wid, synth.T_K))
+        src_v = synth.normal_device((self.B, self.Hkv, width, self.D), (wid, synth.T_V))
+        self.q = synth.normal_device((self.B, self.Hq, n_q, self.D), (wid, synth.T_Q))
+        idx = torch.from_numpy(self.cached.astype(np.int64)).to(DEV).view(self.B, 1, 1, 1) + \
+            torch.arange(n_q, device=DEV).view(1, 1, n_q, 1)
+        idx = idx.expand(self.B, self.Hkv, n_q, self.D)
+        self.k_new = torch.gather(src_k, 2, idx).contiguous()
+        self.v_new = torch.gather(src_v, 2, idx).contiguous()
+        self.positions = torch.from_numpy(self.cached).to(DEV)
+        self.seq_lens = torch.from_numpy(self.ctx).to(DEV)
+        zeros = torch.zeros(self.B, dtype=torch.int32, device=DEV)
+        self.caches = []
+        for _ in range(replicas):
+            c = K.KVCache.paged(self.nblk, self.Hkv, self.D, K.BF16, DEV)
+            K.kv_append(c, src_k, src_v, zeros, block_table=self.table, n_valid=self.positions)
+            self.caches.append(c)
+        del src_k, src_v
+        self.out = torch.empty((self.B, self.Hq, n_q, self.D), dtype=torch.float32, device=DEV)
+        self.part = K.decode_default_part_tokens(K.BF16, self.B, self.Hq * n_q, self.Hkv, self.max_seq_len)
+        self.ws = K.decode_workspace(self.caches[0], self.B, self.Hq * n_q, self.max_seq_len, self.part)
+        torch.cuda.synchronize()
+
+    def step_bytes(self):
+        """K/V of every attended key (4096 B per key over the 8 KV heads), q,
+        the fp32 output, the block table and lengths, and the appended rows
+        (read and written)."""
+        blocks = sum(synth.blocks_for(c) for c in self.ctx)
+        kv = 2 * self.Hkv * self.D * 2 * int(self.ctx.sum())
+        new = 2 * 2 * self.B * self.Hkv * self.nq * self.D * 2
+        return kv + self.B * self.Hq * self.nq * self.D * (2 + 4) + 4 * blocks + 8 * self.B + new
+
+    def step(self, i, ev=None):
+        c = self.caches[i % len(self.caches)]
+        K.kv_append(c, self.k_new, self.v_new, self.positions, block_table=self.table)
+        K.attn_decode_multi(c, self.q, self.seq_lens, self.max_seq_len, block_table=self.table, out=self.out,
+                            workspace=self.ws, part_tokens=self.part)
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "q_heads": self.Hq, "kv_heads": self.Hkv, "new_tokens": self.nq,
+                "head_dim": self.D, "kv_dtype": "bf16", "block_tokens": 16, "keys_total": int(self.ctx.sum()),
+                "cached_len": "U[1,8192] + 4 appended", "part_tokens": self.part}
+
+
 class CowBlockCopy:
     """Copy-on-write fan-out: 4096 whole-block copies in a Llama-3-8B-shaped
     bf16 paged pool (8 KV heads x 16 positions x 128 = 32 KiB per block per
@@ -486,9 +549,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode8b,padded32,longctx70b,prefill8k,chunkprefill,cowcopy,beamreorder",
-                    help="comma list: decode8b (headline), padded32, longctx70b, prefill8k, chunkprefill, cowcopy, "
-                         "beamreorder")
+    ap.add_argument("--workloads",
+                    default="decode8b,padded32,longctx70b,verify8b,prefill8k,chunkprefill,cowcopy,beamreorder",
+                    help="comma list: decode8b (headline), padded32, longctx70b, verify8b, prefill8k, chunkprefill, "
+                         "cowcopy, beamreorder")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the headline workload the oracle runs")
     args = ap.parse_args(argv)
@@ -563,6 +627,15 @@ def main(argv=None):
                                "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "seqs_per_s": 1 / (ms5 * 1e-3),
                                "step_bytes": lw.step_bytes()}
         del lw
+        torch.cuda.empty_cache()
+    if "verify8b" in names:
+        vw = PagedVerify()
+        msv, _ = time_steps(vw, max(10, args.steps), args.warmup)
+        gbs = vw.step_bytes() / (msv * 1e-3) / 1e9
+        extra["verify8b"] = {"config": vw.config(), "ms_per_step": msv, "GB/s": gbs,
+                             "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "seqs_per_s": vw.B / (msv * 1e-3),
+                             "step_bytes": vw.step_bytes()}
+        del vw
         torch.cuda.empty_cache()
     if "prefill8k" in names:
         pf = CausalPrefill()

@@ -246,6 +246,45 @@ int kvattn_attn_decode_append(const kvattn_cache* cache, int32_t batch, int32_t 
                               void* workspace, size_t workspace_bytes, int32_t part_tokens,
                               void* stream);
 
+/* kvattn_attn_decode_multi - n_q new query tokens per sequence against the
+ * cache that already holds them: decoding several tokens at once, such as
+ * checking drafted tokens (speculative decoding) - the cache-read-bound
+ * counterpart of a chunked prefill ("KV Cache" (heepie.pages.dev), section
+ * "Prefill and Decode": decode steps are bound by the key/value scan;
+ * "Transformer Attention Masks and KV-Cache Inference", sections "Prefill
+ * and decode stages" and "Causal mask and future positions").
+ *
+ * For sequence b, head h and query i < n_q (at position seq_lens[b] - n_q + i):
+ *   keys s in [0, seq_lens[b] - (n_q - 1 - i)) with key_mask[b, s] != 0,
+ *   out[b, h, i, :] = sum_s softmax(scale * q[b, h, i, :] . K[s, :])_s V[s, :]
+ * (0 if no key is allowed), i.e. causal among the n_q new tokens, whose K/V
+ * must have been appended at positions seq_lens[b] - n_q .. seq_lens[b] - 1
+ * (kvattn_kv_append with n_new = n_q).  Same as kvattn_attn_prefill with
+ * attend_prefix over those tokens, computed as a split-K decode: query i of
+ * head h is treated as head h * n_q + i, so the group becomes G * n_q query
+ * columns per KV head.
+ *
+ *  num_q_heads  query heads Hq; G * n_q must be 1, 2, 4, 8 or 16, 16 only
+ *               with a bf16 or fp8 cache
+ *  n_q          queries per sequence, 1 .. 16
+ *  q            device [batch, num_q_heads, n_q, head_dim] (bf16; f32 for an
+ *               f32 cache), 16-byte aligned
+ *  out          device fp32 [batch, num_q_heads, n_q, head_dim]
+ *  workspace    >= kvattn_decode_workspace_bytes(dtype, batch,
+ *               num_q_heads * n_q, num_kv_heads, head_dim, max_seq_len,
+ *               part_tokens) bytes (the query columns count as heads)
+ *  every other argument as in kvattn_attn_decode (part_tokens * G * n_q
+ *  <= 8192 with a bf16 cache).
+ */
+int kvattn_attn_decode_multi(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t n_q,
+                             const void* q, int32_t q_dtype,
+                             const int32_t* seq_lens, int32_t max_seq_len,
+                             const int32_t* block_table, int32_t max_blocks,
+                             const uint8_t* key_mask, int64_t key_mask_stride,
+                             float scale, float* out,
+                             void* workspace, size_t workspace_bytes, int32_t part_tokens,
+                             void* stream);
+
 /* kvattn_attn_prefill - attention of n_max new tokens per sequence, causal
  * and/or padding masked, tiled so that no n x n score matrix is ever
  * stored ("KV Cache, Flash Attention and Inference Optimization", section

@@ -17,7 +17,8 @@ VALIDATE_LEN_RANGE, VALIDATE_BLOCK_RANGE, VALIDATE_POSITION = 1, 2, 4
 EXPORTS = (
     "kvattn_version", "kvattn_status_string", "kvattn_last_error", "kvattn_cache_bytes",
     "kvattn_kv_append", "kvattn_decode_workspace_bytes", "kvattn_decode_default_part_tokens",
-    "kvattn_attn_decode", "kvattn_attn_decode_append", "kvattn_attn_prefill", "kvattn_validate",
+    "kvattn_attn_decode", "kvattn_attn_decode_append", "kvattn_attn_decode_multi", "kvattn_attn_prefill",
+    "kvattn_validate",
     "kvattn_reorder_rows", "kvattn_reorder_cache", "kvattn_copy_blocks",
     "kvattn_pool_create", "kvattn_pool_destroy", "kvattn_pool_num_blocks", "kvattn_pool_num_free",
     "kvattn_pool_refcount", "kvattn_pool_alloc", "kvattn_pool_retain", "kvattn_pool_release", "kvattn_pool_fork",
@@ -69,6 +70,8 @@ _SIGS = {
                                           _F, _P, _P, _SZ, _I32, _P]),
     "kvattn_attn_decode_append": (ctypes.c_int, [_CP, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _I32, _P,
                                                  _I64, _F, _P, _P, _SZ, _I32, _P]),
+    "kvattn_attn_decode_multi": (ctypes.c_int, [_CP, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _I64,
+                                                _F, _P, _P, _SZ, _I32, _P]),
     "kvattn_attn_prefill": (ctypes.c_int, [_CP, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P,
                                            _P, _I32, _P, _I64, _I32, _I32, _F, _P, _P]),
     "kvattn_validate": (ctypes.c_int, [_CP, _I32, _P, _I32, _P, _P, _I32, _P, _P]),

@@ -326,7 +326,7 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32
 // whose other arrays take `floats` floats (rounded up to 16 bytes).
 __host__ __device__ constexpr int kslot_offset(int floats) { return ((floats * 4 + 15) / 16) * 16; }
 
-template <int KVT, int D, int G, bool MASK>
+template <int KVT, int D, int G, bool MASK, bool TAIL>
 __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   using TR = Traits<KVT>;
   using Raw = typename TR::Raw;
@@ -360,6 +360,10 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   const int n = t1 - t0;
   const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
   const int j0 = t0 / kBlockTokens;
+  // Several queries per sequence (TAIL): column h of the group is query
+  // h % n_tail of its head, which sees the keys below
+  // ctx - (n_tail - 1 - h % n_tail); ncol is that bound relative to t0.
+  auto ncol = [&](int h) { return ctx - (p.n_tail - 1 - h % p.n_tail) - t0; };
 
   int64_t* offs = reinterpret_cast<int64_t*>(lds);        // [T/16] block byte offsets (-1: outside)
   float* s_lds = lds + decode_off_floats(T);              // [T][G] scores -> weights
@@ -415,7 +419,10 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
         if constexpr (MASK) valid = valid && mflag[t] != 0;
         if (col == 0) {
 #pragma unroll
-          for (int h = 0; h < G; ++h) s_lds[t * G + h] = valid ? acc[h] * zscale : -INFINITY;
+          for (int h = 0; h < G; ++h) {
+            const bool ok = valid && (!TAIL || t < ncol(h));
+            s_lds[t * G + h] = ok ? acc[h] * zscale : -INFINITY;
+          }
         }
       }
     }
@@ -557,7 +564,7 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
 // Per 16-token block a wave issues 8 (D = 128) MFMAs for the scores and 16
 // for the output instead of the vector pass's per-element dot products,
 // lane reductions and multiply-adds.
-template <int D, int G, bool MASK>
+template <int D, int G, bool MASK, bool TAIL>
 __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLaunch p) {
   typedef short v4s __attribute__((ext_vector_type(4)));
   typedef float v4f __attribute__((ext_vector_type(4)));
@@ -661,11 +668,14 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
     sacc += sacc2;
     if (r16 < G) {
       const int tk = kBlockTokens * jb + 4 * lg;  // partition-relative key of r = 0
+      // several queries per sequence (TAIL): column r16 is query r16 % n_tail,
+      // which sees keys below ctx - (n_tail - 1 - r16 % n_tail)
+      const int ncol = TAIL ? ctx - (p.n_tail - 1 - r16 % p.n_tail) - t0 : n;
       float4 z;
-      z.x = (in_cache && key_ok(tk + 0)) ? sacc[0] * zscale : -INFINITY;
-      z.y = (in_cache && key_ok(tk + 1)) ? sacc[1] * zscale : -INFINITY;
-      z.z = (in_cache && key_ok(tk + 2)) ? sacc[2] * zscale : -INFINITY;
-      z.w = (in_cache && key_ok(tk + 3)) ? sacc[3] * zscale : -INFINITY;
+      z.x = (in_cache && key_ok(tk + 0) && tk + 0 < ncol) ? sacc[0] * zscale : -INFINITY;
+      z.y = (in_cache && key_ok(tk + 1) && tk + 1 < ncol) ? sacc[1] * zscale : -INFINITY;
+      z.z = (in_cache && key_ok(tk + 2) && tk + 2 < ncol) ? sacc[2] * zscale : -INFINITY;
+      z.w = (in_cache && key_ok(tk + 3) && tk + 3 < ncol) ? sacc[3] * zscale : -INFINITY;
       *reinterpret_cast<float4*>(s_lds + r16 * T + tk) = z;
     }
   };
@@ -828,7 +838,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
 // The weights are split into bf16 hi + lo parts (two MFMAs), so P keeps about
 // 16 bits.  Each wave keeps its own running (max, sum, O) over its blocks with
 // a lazily raised maximum; the four waves are combined through LDS.
-template <int D, int G, bool MASK>
+template <int D, int G, bool MASK, bool TAIL>
 __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLaunch p) {
   typedef short v4s __attribute__((ext_vector_type(4)));
   typedef float v4f __attribute__((ext_vector_type(4)));
@@ -948,12 +958,15 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     sacc += sacc2;
     // ---- mask, block max, lazily raised running max ----
     const int tk = kBlockTokens * jb + 4 * lg;
+    // several queries per sequence (TAIL): column r16 is query r16 % n_tail,
+    // which sees keys below ctx - (n_tail - 1 - r16 % n_tail)
+    const int ncol = TAIL ? ctx - (p.n_tail - 1 - r16 % p.n_tail) - t0 : n;
     float z[4];
     bool live[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       live[r] = key_ok(tk + r);
-      z[r] = live[r] ? sacc[r] * zscale : -INFINITY;
+      z[r] = (live[r] && tk + r < ncol) ? sacc[r] * zscale : -INFINITY;
     }
     float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     {
@@ -1178,20 +1191,20 @@ __global__ void __launch_bounds__(256) decode_merge(const DecodeLaunch p) {
   }
 }
 
-template <int KVT, int D, int G, bool MASK>
+template <int KVT, int D, int G, bool MASK, bool TAIL>
 int launch_typed(const DecodeLaunch& a, hipStream_t s) {
   const dim3 grid(a.num_kv_heads, a.num_parts, a.batch);
   if constexpr (KVT == KVATTN_FP8_E4M3 && G >= 4) {
     const size_t lds = (size_t)(decode_off_floats(a.part_tokens) + kWaves * G * D + kWaves * G * 2 +
                                 (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
-    hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
   } else if constexpr (KVT == KVATTN_BF16 && G >= 4) {
     const size_t lds = (size_t)kslot_offset(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) +
                        (size_t)kWaves * KStage<2 * D>::BYTES;
-    hipLaunchKernelGGL((decode_partition_bf16_mfma<D, G, MASK>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((decode_partition_bf16_mfma<D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
   } else {
     const size_t lds = (size_t)(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
-    hipLaunchKernelGGL((decode_partition<KVT, D, G, MASK>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((decode_partition<KVT, D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
   }
   if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
   if (a.num_parts > 1) {
@@ -1201,18 +1214,26 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
   return KVATTN_OK;
 }
 
-template <int KVT, int D, int G>
+template <int KVT, int D, int G, bool TAIL>
 int launch_mask(const DecodeLaunch& a, hipStream_t s) {
-  return a.key_mask ? launch_typed<KVT, D, G, true>(a, s) : launch_typed<KVT, D, G, false>(a, s);
+  return a.key_mask ? launch_typed<KVT, D, G, true, TAIL>(a, s) : launch_typed<KVT, D, G, false, TAIL>(a, s);
+}
+
+template <int KVT, int D, int G>
+int launch_tail(const DecodeLaunch& a, hipStream_t s) {
+  return a.n_tail > 1 ? launch_mask<KVT, D, G, true>(a, s) : launch_mask<KVT, D, G, false>(a, s);
 }
 
 template <int KVT, int D>
 int launch_group(const DecodeLaunch& a, hipStream_t s) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_mask<KVT, D, 1>(a, s);
-    case 2: return launch_mask<KVT, D, 2>(a, s);
-    case 4: return launch_mask<KVT, D, 4>(a, s);
-    case 8: return launch_mask<KVT, D, 8>(a, s);
+    case 1: return launch_tail<KVT, D, 1>(a, s);
+    case 2: return launch_tail<KVT, D, 2>(a, s);
+    case 4: return launch_tail<KVT, D, 4>(a, s);
+    case 8: return launch_tail<KVT, D, 8>(a, s);
+    case 16:  // matrix-core passes only (16 columns per KV head)
+      if constexpr (KVT == KVATTN_F32) return KVATTN_EUNSUPPORTED;
+      else return launch_tail<KVT, D, 16>(a, s);
     default: return KVATTN_EUNSUPPORTED;
   }
 }

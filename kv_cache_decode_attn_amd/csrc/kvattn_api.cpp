@@ -47,6 +47,13 @@ int group_ok(int32_t hq, int32_t hkv) {
   return g == 1 || g == 2 || g == 4 || g == 8;
 }
 
+// Decode groups: also 16 query columns per KV head on the matrix-core
+// passes (bf16 and fp8 caches).
+int decode_group_ok(int32_t dtype, int32_t hq, int32_t hkv) {
+  if (group_ok(hq, hkv)) return 1;
+  return hkv >= 1 && hq == 16 * hkv && dtype != KVATTN_F32;
+}
+
 // Fills the kernels' view of a cache descriptor; also returns the number of
 // positions a sequence can hold.
 int make_view(const char* who, const kvattn_cache* c, int32_t batch, const int32_t* block_table,
@@ -128,14 +135,15 @@ int attn_decode_impl(const char* who, const kvattn_cache* cache, int32_t batch, 
                      int32_t q_dtype, const void* k_new, const void* v_new, int32_t in_dtype,
                      const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table, int32_t max_blocks,
                      const uint8_t* key_mask, int64_t key_mask_stride, float scale, float* out, void* workspace,
-                     size_t workspace_bytes, int32_t part_tokens, void* stream) {
+                     size_t workspace_bytes, int32_t part_tokens, void* stream, int32_t n_tail = 1) {
   if (batch < 0 || batch > 65535) return fail(KVATTN_EINVAL, "%s: batch %d out of range", who, batch);
   kvattn::CacheView view;
   int64_t cap = 0;
   int rc = make_view(who, cache, batch, block_table, max_blocks, &view, &cap);
   if (rc) return rc;
-  if (!group_ok(num_q_heads, cache->num_kv_heads))
-    return fail(KVATTN_EUNSUPPORTED, "%s: %d query heads over %d KV heads: group must be 1, 2, 4 or 8", who,
+  if (!decode_group_ok(cache->dtype, num_q_heads, cache->num_kv_heads))
+    return fail(KVATTN_EUNSUPPORTED,
+                "%s: %d query columns over %d KV heads: group must be 1, 2, 4, 8 (or 16 with a bf16/fp8 cache)", who,
                 num_q_heads, cache->num_kv_heads);
   const int32_t want_q = (cache->dtype == KVATTN_F32) ? KVATTN_F32 : KVATTN_BF16;
   if (q_dtype != want_q)
@@ -203,6 +211,7 @@ int attn_decode_impl(const char* who, const kvattn_cache* cache, int32_t batch, 
   a.ws_ml = ws_ml;
   a.part_tokens = t;
   a.num_parts = (int32_t)(parts < 1 ? 1 : parts);
+  a.n_tail = n_tail;
   if (append) {
     a.k_new = static_cast<const uint8_t*>(k_new);
     a.v_new = static_cast<const uint8_t*>(v_new);
@@ -281,14 +290,16 @@ int kvattn_kv_append(const kvattn_cache* cache, int32_t batch, int32_t n_new, co
 
 int32_t kvattn_decode_default_part_tokens(int32_t cache_dtype, int32_t batch, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t max_seq_len) {
-  if (batch < 0 || max_seq_len < 0 || !elem_bytes(cache_dtype) || !group_ok(num_q_heads, num_kv_heads)) return 0;
+  if (batch < 0 || max_seq_len < 0 || !elem_bytes(cache_dtype) ||
+      !decode_group_ok(cache_dtype, num_q_heads, num_kv_heads))
+    return 0;
   return default_part_tokens(cache_dtype, batch, num_q_heads, num_kv_heads, max_seq_len);
 }
 
 size_t kvattn_decode_workspace_bytes(int32_t cache_dtype, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t max_seq_len, int32_t part_tokens) {
   if (batch < 0 || max_seq_len < 0 || head_dim <= 0 || !elem_bytes(cache_dtype) ||
-      !group_ok(num_q_heads, num_kv_heads))
+      !decode_group_ok(cache_dtype, num_q_heads, num_kv_heads))
     return 0;
   const int32_t t =
       part_tokens ? part_tokens : default_part_tokens(cache_dtype, batch, num_q_heads, num_kv_heads, max_seq_len);
@@ -318,6 +329,22 @@ int kvattn_attn_decode_append(const kvattn_cache* cache, int32_t batch, int32_t 
   return attn_decode_impl("kvattn_attn_decode_append", cache, batch, num_q_heads, q, q_dtype, k_new, v_new,
                           in_dtype, seq_lens, max_seq_len, block_table, max_blocks, key_mask, key_mask_stride, scale,
                           out, workspace, workspace_bytes, part_tokens, stream);
+}
+
+int kvattn_attn_decode_multi(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t n_q,
+                             const void* q, int32_t q_dtype, const int32_t* seq_lens, int32_t max_seq_len,
+                             const int32_t* block_table, int32_t max_blocks, const uint8_t* key_mask,
+                             int64_t key_mask_stride, float scale, float* out, void* workspace,
+                             size_t workspace_bytes, int32_t part_tokens, void* stream) {
+  const char* who = "kvattn_attn_decode_multi";
+  if (n_q < 1 || n_q > 16) return fail(KVATTN_EINVAL, "%s: n_q %d out of range [1, 16]", who, n_q);
+  if (num_q_heads < 1 || (int64_t)num_q_heads * n_q > 65535)
+    return fail(KVATTN_EINVAL, "%s: %d query heads x %d queries out of range", who, num_q_heads, n_q);
+  // query i of head h is virtual head h * n_q + i: q and out [batch, heads, n_q, d]
+  // are [batch, heads * n_q, d], and the group becomes G * n_q
+  return attn_decode_impl(who, cache, batch, num_q_heads * n_q, q, q_dtype, nullptr, nullptr, -1, seq_lens,
+                          max_seq_len, block_table, max_blocks, key_mask, key_mask_stride, scale, out, workspace,
+                          workspace_bytes, part_tokens, stream, n_q);
 }
 
 int kvattn_attn_prefill(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -48,6 +48,10 @@ struct DecodeLaunch {
   const uint8_t* k_new;
   const uint8_t* v_new;
   int32_t in_dtype;
+  // Queries per sequence (1 for a plain decode): num_q_heads counts
+  // (head, query) pairs, query i of head h being virtual head h * n_tail + i;
+  // it sees the keys below seq_lens[b] - (n_tail - 1 - i).
+  int32_t n_tail;
 };
 int launch_decode(const DecodeLaunch& a, hipStream_t stream);
 // Dynamic LDS bytes of the decode partition kernel.
