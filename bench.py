@@ -395,8 +395,9 @@ class ChunkedPrefill:
 class PagedVerify:
     """Checking drafted tokens: the Llama-3-8B-shaped paged decode workload
     (batch 32, 32/8 heads, d 128, bf16, cached lengths U[1, 8192]) with 4 new
-    tokens per sequence appended (kv_append) and attended together, causal
-    among themselves (attn_decode_multi: 16 query columns per KV head)."""
+    tokens per sequence stored in the cache and attended together, causal
+    among themselves, in one attn_decode_multi call (16 query columns per KV
+    head; each partition's workgroup stores the new rows in its key range)."""
 
     name = "llama3-8b-paged-gqa-verify-4-tokens"
 
@@ -443,9 +444,8 @@ class PagedVerify:
 
     def step(self, i, ev=None):
         c = self.caches[i % len(self.caches)]
-        K.kv_append(c, self.k_new, self.v_new, self.positions, block_table=self.table)
-        K.attn_decode_multi(c, self.q, self.seq_lens, self.max_seq_len, block_table=self.table, out=self.out,
-                            workspace=self.ws, part_tokens=self.part)
+        K.attn_decode_multi(c, self.q, self.seq_lens, self.max_seq_len, k_new=self.k_new, v_new=self.v_new,
+                            block_table=self.table, out=self.out, workspace=self.ws, part_tokens=self.part)
 
     def config(self):
         return {"workload": self.name, "batch": self.B, "q_heads": self.Hq, "kv_heads": self.Hkv, "new_tokens": self.nq,

@@ -224,8 +224,9 @@ int kvattn_attn_decode(const kvattn_cache* cache, int32_t batch, int32_t num_q_h
  * cache bytes and the output), for every sequence with
  * 1 <= seq_lens[b] <= min(max_seq_len, capacity); a sequence outside that
  * range has nothing written.  The workgroup that attends key seq_lens[b] - 1
- * encodes the new rows, uses them in place of that cache slot and stores
- * them after its last cache read, so no separate write pass is launched.
+ * encodes the new rows and stores them in that cache slot before it reads
+ * the cache (no other workgroup reads the slot), so no separate write pass
+ * is launched.
  *
  *  k_new, v_new device [batch, num_kv_heads, head_dim] of in_dtype, 16-byte
  *               aligned: the new token of each sequence
@@ -258,17 +259,23 @@ int kvattn_attn_decode_append(const kvattn_cache* cache, int32_t batch, int32_t 
  *   keys s in [0, seq_lens[b] - (n_q - 1 - i)) with key_mask[b, s] != 0,
  *   out[b, h, i, :] = sum_s softmax(scale * q[b, h, i, :] . K[s, :])_s V[s, :]
  * (0 if no key is allowed), i.e. causal among the n_q new tokens, whose K/V
- * must have been appended at positions seq_lens[b] - n_q .. seq_lens[b] - 1
- * (kvattn_kv_append with n_new = n_q).  Same as kvattn_attn_prefill with
- * attend_prefix over those tokens, computed as a split-K decode: query i of
- * head h is treated as head h * n_q + i, so the group becomes G * n_q query
- * columns per KV head.
+ * sit at positions seq_lens[b] - n_q .. seq_lens[b] - 1: given as k_new and
+ * v_new, they are stored there by this call first (the workgroup that
+ * attends a position stores it, encoded as kvattn_kv_append would); with
+ * k_new = v_new = NULL they must have been appended already.  Same as
+ * kvattn_attn_prefill with attend_prefix over those tokens, computed as a
+ * split-K decode: query i of head h is treated as head h * n_q + i, so the
+ * group becomes G * n_q query columns per KV head.
  *
  *  num_q_heads  query heads Hq; G * n_q must be 1, 2, 4, 8 or 16, 16 only
  *               with a bf16 or fp8 cache
  *  n_q          queries per sequence, 1 .. 16
  *  q            device [batch, num_q_heads, n_q, head_dim] (bf16; f32 for an
  *               f32 cache), 16-byte aligned
+ *  k_new, v_new device [batch, num_kv_heads, n_q, head_dim] of in_dtype (f32
+ *               or bf16, equal to the cache dtype unless the cache is fp8),
+ *               16-byte aligned, or both NULL; the position of a sequence
+ *               outside [1, min(max_seq_len, capacity)] has nothing written
  *  out          device fp32 [batch, num_q_heads, n_q, head_dim]
  *  workspace    >= kvattn_decode_workspace_bytes(dtype, batch,
  *               num_q_heads * n_q, num_kv_heads, head_dim, max_seq_len,
@@ -278,6 +285,7 @@ int kvattn_attn_decode_append(const kvattn_cache* cache, int32_t batch, int32_t 
  */
 int kvattn_attn_decode_multi(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t n_q,
                              const void* q, int32_t q_dtype,
+                             const void* k_new, const void* v_new, int32_t in_dtype,
                              const int32_t* seq_lens, int32_t max_seq_len,
                              const int32_t* block_table, int32_t max_blocks,
                              const uint8_t* key_mask, int64_t key_mask_stride,

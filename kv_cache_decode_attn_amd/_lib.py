@@ -70,8 +70,8 @@ _SIGS = {
                                           _F, _P, _P, _SZ, _I32, _P]),
     "kvattn_attn_decode_append": (ctypes.c_int, [_CP, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _I32, _P,
                                                  _I64, _F, _P, _P, _SZ, _I32, _P]),
-    "kvattn_attn_decode_multi": (ctypes.c_int, [_CP, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _I64,
-                                                _F, _P, _P, _SZ, _I32, _P]),
+    "kvattn_attn_decode_multi": (ctypes.c_int, [_CP, _I32, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _I32,
+                                                _P, _I64, _F, _P, _P, _SZ, _I32, _P]),
     "kvattn_attn_prefill": (ctypes.c_int, [_CP, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P,
                                            _P, _I32, _P, _I64, _I32, _I32, _F, _P, _P]),
     "kvattn_validate": (ctypes.c_int, [_CP, _I32, _P, _I32, _P, _P, _I32, _P, _P]),

@@ -221,26 +221,37 @@ def attn_decode_append(cache, q, k_new, v_new, seq_lens, max_seq_len, block_tabl
 
 
 
-def attn_decode_multi(cache, q, seq_lens, max_seq_len, block_table=None, key_mask=None, scale=None, out=None,
-                      workspace=None, part_tokens=0):
-    """n_q query tokens per sequence against the cache that already holds
-    them (kvattn_attn_decode_multi): q [B, Hq, n_q, d]; query i sees the keys
-    below seq_lens[b] - (n_q - 1 - i).  Returns fp32 [B, Hq, n_q, d]."""
+def attn_decode_multi(cache, q, seq_lens, max_seq_len, k_new=None, v_new=None, block_table=None, key_mask=None,
+                      scale=None, out=None, workspace=None, part_tokens=0):
+    """n_q query tokens per sequence against the cache (kvattn_attn_decode_multi):
+    q [B, Hq, n_q, d]; their K/V are the last n_q positions below seq_lens[b],
+    stored by this call when k_new/v_new [B, Hkv, n_q, d] (f32 or bf16) are
+    given.  Query i sees the keys below seq_lens[b] - (n_q - 1 - i).  Returns
+    fp32 [B, Hq, n_q, d]."""
     _dev(q, "q")
     if q.dim() != 4:
         raise ValueError("q must be [B, Hq, n_q, d]")
     B, Hq, nq, d = q.shape
+    in_code = -1
+    if k_new is not None or v_new is not None:
+        _dev(k_new, "k_new")
+        _dev(v_new, "v_new")
+        if k_new.dtype not in _CODE or v_new.dtype != k_new.dtype or k_new.shape != v_new.shape:
+            raise TypeError("k_new/v_new must be matching f32 or bf16 tensors")
+        if tuple(k_new.shape) != (B, cache.num_kv_heads, nq, cache.head_dim):
+            raise ValueError("k_new shape %s does not match [B, Hkv, n_q, d]" % (tuple(k_new.shape),))
+        in_code = _CODE[k_new.dtype]
     if out is None:
         out = torch.empty((B, Hq, nq, d), dtype=torch.float32, device=q.device)
     # query i of head h is column h * n_q + i: q and out viewed as [B, Hq * n_q, d]
-    _, _, scale, out3, workspace, mb, stride = _decode_args(cache, q.view(B, Hq * nq, d), seq_lens, max_seq_len,
-                                                            block_table, key_mask, scale,
-                                                            out.view(B, Hq * nq, d), workspace, part_tokens)
+    _, _, scale, _, workspace, mb, stride = _decode_args(cache, q.view(B, Hq * nq, d), seq_lens, max_seq_len,
+                                                         block_table, key_mask, scale, out.view(B, Hq * nq, d),
+                                                         workspace, part_tokens)
     check(lib().kvattn_attn_decode_multi(ctypes.byref(cache.desc()), B, Hq, nq, _ptr(q), _CODE.get(q.dtype, -1),
-                                         _ptr(seq_lens), int(max_seq_len), _ptr(block_table), mb, _ptr(key_mask),
-                                         stride, scale, _ptr(out), _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), int(part_tokens),
-                                         _stream(q.device)))
+                                         _ptr(k_new), _ptr(v_new), in_code, _ptr(seq_lens), int(max_seq_len),
+                                         _ptr(block_table), mb, _ptr(key_mask), stride, scale, _ptr(out),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         int(part_tokens), _stream(q.device)))
     return out
 
 def attn_prefill(q, k, v, cache=None, positions=None, q_lens=None, block_table=None, key_mask=None, causal=True,

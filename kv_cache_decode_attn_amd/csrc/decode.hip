@@ -159,16 +159,17 @@ __host__ __device__ constexpr int decode_off_floats(int T) { return 2 * (T / kBl
 __host__ __device__ constexpr int decode_lds_floats(int T, int G, int D) {
   return decode_off_floats(T) + ((T * G > kWaves * G * D) ? T * G : kWaves * G * D) + 2 * G;
 }
-// Fused append: the workgroup that attends key tn = seq_lens[b] - 1 (the
-// last key of the sequence, in its last partition) first stores the new
-// token's K and V rows of KV head g into that slot, encoded as kv_append
-// encodes them (a copy for an fp32 or bf16 cache, E4M3(x / scale) for an fp8
-// cache), then reads the cache as usual: the barrier that follows makes the
-// stores visible to every wave of the workgroup (a workgroup-scope release
-// and acquire on global memory).  No other workgroup of the launch reads
-// the slot, so the step needs no separate write pass.
+// Fused append: the new tokens' K and V rows (k_new/v_new [batch,
+// num_kv_heads, n_tail, head_dim]) go to positions seq_lens[b] - n_tail ..
+// seq_lens[b] - 1.  Each partition's workgroup stores the rows whose
+// positions fall in its own key range, encoded as kv_append encodes them (a
+// copy for an fp32 or bf16 cache, E4M3(x / scale) for an fp8 cache), then
+// reads the cache as usual: the barrier that follows makes the stores
+// visible to every wave of the workgroup (a workgroup-scope release and
+// acquire on global memory).  A position is read only by the workgroup of
+// its partition, so the step needs no separate write pass.
 template <int KVT, int D>
-__device__ void store_new_rows(const DecodeLaunch& p, int b, int g, int tn) {
+__device__ void store_new_row(const DecodeLaunch& p, int b, int g, int tn, int row) {
   constexpr int ES = (KVT == KVATTN_F32) ? 4 : (KVT == KVATTN_BF16) ? 2 : 1;
   constexpr int EPW = 4 / ES;     // elements per 32-bit word
   constexpr int W = D * ES / 4;   // words per row
@@ -176,7 +177,7 @@ __device__ void store_new_rows(const DecodeLaunch& p, int b, int g, int tn) {
   if (off < 0) return;  // outside the cache: nothing is stored (and the key is masked)
   for (int i = threadIdx.x; i < 2 * W; i += blockDim.x) {
     const int kv = i / W, w = i - kv * W;
-    const int64_t src = ((int64_t)b * p.num_kv_heads + g) * D + (int64_t)w * EPW;
+    const int64_t src = (((int64_t)b * p.num_kv_heads + g) * p.n_tail + row) * D + (int64_t)w * EPW;
     const uint8_t* in = kv ? p.v_new : p.k_new;
     uint32_t word;
     if constexpr (KVT == KVATTN_F32) {
@@ -374,9 +375,13 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
     const uint8_t* mask_row = p.key_mask + (int64_t)b * p.key_mask_stride + t0;
     for (int t = tid; t < n; t += 256) mflag[t] = mask_row[t];
   }
-  // fused append: the partition that ends the sequence stores the new key
-  const bool app = p.k_new != nullptr && t1 == ctx && p.seq_lens[b] == ctx;
-  if (app) store_new_rows<KVT, D>(p, b, g, ctx - 1);
+  // fused append: each partition stores the new rows in its key range
+  if (p.k_new != nullptr && p.seq_lens[b] == ctx) {
+    for (int i = 0; i < p.n_tail; ++i) {
+      const int tn = ctx - p.n_tail + i;
+      if (tn >= t0 && tn < t1) store_new_row<KVT, D>(p, b, g, tn, i);
+    }
+  }
 
   QFrag<KVT, G> q;
   q.load(p.q, (int64_t)b * p.num_q_heads + hq0, D, col);
@@ -605,8 +610,12 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
     for (int t = tid; t < n; t += 256) mflag[t] = mask_row[t];
   }
   // fused append (as in decode_partition)
-  const bool app = p.k_new != nullptr && t1 == ctx && p.seq_lens[b] == ctx;
-  if (app) store_new_rows<KVATTN_BF16, D>(p, b, g, ctx - 1);
+  if (p.k_new != nullptr && p.seq_lens[b] == ctx) {
+    for (int i = 0; i < p.n_tail; ++i) {
+      const int tn = ctx - p.n_tail + i;
+      if (tn >= t0 && tn < t1) store_new_row<KVATTN_BF16, D>(p, b, g, tn, i);
+    }
+  }
 
   // q of head r16 in the k order of the K chunks: k-step s = 2c + u uses
   // d 32c + 8*lg + 4u + 0..3 (zero for heads >= G)
@@ -881,8 +890,12 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     for (int t = tid; t < n; t += 256) mflag[t] = mask_row[t];
   }
   // fused append (as in decode_partition)
-  const bool app = p.k_new != nullptr && t1 == ctx && p.seq_lens[b] == ctx;
-  if (app) store_new_rows<KVATTN_FP8_E4M3, D>(p, b, g, ctx - 1);
+  if (p.k_new != nullptr && p.seq_lens[b] == ctx) {
+    for (int i = 0; i < p.n_tail; ++i) {
+      const int tn = ctx - p.n_tail + i;
+      if (tn >= t0 && tn < t1) store_new_row<KVATTN_FP8_E4M3, D>(p, b, g, tn, i);
+    }
+  }
 
   // q of head r16 as bf16 pairs: k-step s uses d 64(s/4) + 16*lg + 4(s%4) + 0..3
   uint32_t qb[KS][2];

@@ -332,19 +332,22 @@ int kvattn_attn_decode_append(const kvattn_cache* cache, int32_t batch, int32_t 
 }
 
 int kvattn_attn_decode_multi(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t n_q,
-                             const void* q, int32_t q_dtype, const int32_t* seq_lens, int32_t max_seq_len,
-                             const int32_t* block_table, int32_t max_blocks, const uint8_t* key_mask,
-                             int64_t key_mask_stride, float scale, float* out, void* workspace,
-                             size_t workspace_bytes, int32_t part_tokens, void* stream) {
+                             const void* q, int32_t q_dtype, const void* k_new, const void* v_new, int32_t in_dtype,
+                             const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                             int32_t max_blocks, const uint8_t* key_mask, int64_t key_mask_stride, float scale,
+                             float* out, void* workspace, size_t workspace_bytes, int32_t part_tokens, void* stream) {
   const char* who = "kvattn_attn_decode_multi";
   if (n_q < 1 || n_q > 16) return fail(KVATTN_EINVAL, "%s: n_q %d out of range [1, 16]", who, n_q);
   if (num_q_heads < 1 || (int64_t)num_q_heads * n_q > 65535)
     return fail(KVATTN_EINVAL, "%s: %d query heads x %d queries out of range", who, num_q_heads, n_q);
+  const bool append = k_new || v_new;
+  if (append && in_dtype != KVATTN_F32 && in_dtype != KVATTN_BF16)
+    return fail(KVATTN_EINVAL, "%s: input dtype must be f32 or bf16", who);
   // query i of head h is virtual head h * n_q + i: q and out [batch, heads, n_q, d]
   // are [batch, heads * n_q, d], and the group becomes G * n_q
-  return attn_decode_impl(who, cache, batch, num_q_heads * n_q, q, q_dtype, nullptr, nullptr, -1, seq_lens,
-                          max_seq_len, block_table, max_blocks, key_mask, key_mask_stride, scale, out, workspace,
-                          workspace_bytes, part_tokens, stream, n_q);
+  return attn_decode_impl(who, cache, batch, num_q_heads * n_q, q, q_dtype, k_new, v_new, append ? in_dtype : -1,
+                          seq_lens, max_seq_len, block_table, max_blocks, key_mask, key_mask_stride, scale, out,
+                          workspace, workspace_bytes, part_tokens, stream, n_q);
 }
 
 int kvattn_attn_prefill(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -42,9 +42,10 @@ struct DecodeLaunch {
   float* ws_ml;  // [batch, num_q_heads, num_parts, 2]
   int32_t part_tokens;
   int32_t num_parts;
-  // Fused append: the new token's K and V rows [batch, num_kv_heads,
-  // head_dim] of in_dtype, stored at position seq_lens[b] - 1 by the
-  // workgroup that attends that key.  Null for a plain decode.
+  // Fused append: the new tokens' K and V rows [batch, num_kv_heads,
+  // n_tail, head_dim] of in_dtype, stored at positions seq_lens[b] - n_tail
+  // .. seq_lens[b] - 1 by the workgroups that attend those keys.  Null for a
+  // plain decode.
   const uint8_t* k_new;
   const uint8_t* v_new;
   int32_t in_dtype;

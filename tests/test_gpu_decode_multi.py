@@ -136,3 +136,61 @@ def test_decode_multi_rejects_unsupported_groups():
     table = torch.zeros((1, 4), dtype=torch.int32, device=DEV)
     with pytest.raises(K.KvattnError):
         K.attn_decode_multi(cache, q, seq, 10, block_table=table)
+
+
+@pytest.mark.parametrize("dtype,G,n_q,layout", [
+    (K.BF16, 4, 4, K.PAGED),
+    (K.BF16, 2, 2, K.CONTIGUOUS),
+    (K.FP8_E4M3, 8, 2, K.PAGED),
+    (K.FP8_E4M3, 1, 4, K.CONTIGUOUS),
+    (K.F32, 2, 2, K.PAGED),
+])
+def test_decode_multi_fused_append_equals_append_then_attend(dtype, G, n_q, layout):
+    """Given k_new/v_new, the call stores the n_q rows itself: the cache bytes
+    and the output equal kv_append(n_q) followed by the call without them, bit
+    for bit - also when the new positions straddle two partitions (64 keys
+    each: lengths 66 and 130)."""
+    Hkv, d = 2, 128
+    Hq = G * Hkv
+    lens = np.array([66, 130, 5, 700], np.int32)
+    B = len(lens)
+    total = int(lens.max())
+    tdt = _TORCH[dtype]
+    kx = synth.normal((B, Hkv, total, d), (90, synth.T_K), tdt)
+    vx = synth.normal((B, Hkv, total, d), (90, synth.T_V), tdt)
+    q = synth.normal((B, Hq, n_q, d), (90, synth.T_Q), tdt).to(DEV)
+    ks = vs = None
+    if dtype == K.FP8_E4M3:
+        ks = torch.full((Hkv,), 0.7, dtype=torch.float32, device=DEV)
+        vs = torch.full((Hkv,), 1.3, dtype=torch.float32, device=DEV)
+    tdev = None
+
+    def make():
+        nonlocal tdev
+        if layout == K.PAGED:
+            nbs = [synth.blocks_for(int(x)) for x in lens]
+            table, nblk = synth.block_table(nbs, max(nbs), (90, synth.T_PERM))
+            tdev = torch.from_numpy(table).to(DEV)
+            c = K.KVCache.paged(nblk, Hkv, d, dtype, DEV, ks, vs)
+        else:
+            c = K.KVCache.contiguous(B, Hkv, -(-total // 16) * 16, d, dtype, DEV, ks, vs)
+        c.k.zero_()
+        c.v.zero_()
+        # everything but the last n_q positions of each sequence
+        K.kv_append(c, kx.to(DEV), vx.to(DEV), torch.zeros(B, dtype=torch.int32, device=DEV), block_table=tdev,
+                    n_valid=torch.from_numpy(lens - n_q).to(DEV))
+        return c
+
+    idx = torch.from_numpy((lens - n_q).astype(np.int64)).view(B, 1, 1, 1) + torch.arange(n_q).view(1, 1, n_q, 1)
+    idx = idx.expand(B, Hkv, n_q, d)
+    k1 = torch.gather(kx, 2, idx).contiguous().to(DEV)
+    v1 = torch.gather(vx, 2, idx).contiguous().to(DEV)
+    seq = torch.from_numpy(lens).to(DEV)
+    a = make()
+    got = K.attn_decode_multi(a, q, seq, total, k_new=k1, v_new=v1, block_table=tdev, part_tokens=64).cpu()
+    b = make()
+    K.kv_append(b, k1, v1, torch.from_numpy(lens - n_q).to(DEV), block_table=tdev)
+    ref = K.attn_decode_multi(b, q, seq, total, block_table=tdev, part_tokens=64).cpu()
+    assert torch.equal(got, ref)
+    np.testing.assert_array_equal(storage(a.k), storage(b.k))
+    np.testing.assert_array_equal(storage(a.v), storage(b.v))
