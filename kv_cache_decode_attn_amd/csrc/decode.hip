@@ -150,6 +150,8 @@ constexpr int kWaves = 4;
 constexpr int kRingVec = KVATTN_RING_VEC;
 constexpr int kRingBf16 = KVATTN_RING_BF16;
 constexpr int kRingFp8 = KVATTN_RING_FP8;
+// DPP control: rotate each row of 16 lanes right by 8 (lane i reads lane i ^ 8)
+constexpr int kDppRowRor8 = 0x128;
 
 // LDS layout of the partition kernel, in floats: block offsets (int64, one
 // per 16-token block of the partition), then scores/weights [T][G] (reused
@@ -897,14 +899,15 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     }
   }
 
-  // q of head r16 as bf16 pairs: k-step s uses d 64(s/4) + 16*lg + 4(s%4) + 0..3
+  // q of head r16 as bf16 pairs: k-step s uses d 4*KS*lg + 4s + 0..3, the
+  // bytes of the K row that lane group lg holds (see the K load below)
   uint32_t qb[KS][2];
   {
     const int hr = r16 < G ? r16 : 0;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)b * p.num_q_heads + hq0 + hr) * D;
 #pragma unroll
     for (int sd = 0; sd < KS; ++sd) {
-      const uint2 w = *reinterpret_cast<const uint2*>(qrow + 64 * (sd / 4) + 16 * lg + 4 * (sd % 4));
+      const uint2 w = *reinterpret_cast<const uint2*>(qrow + 4 * KS * lg + 4 * sd);
       qb[sd][0] = r16 < G ? w.x : 0u;
       qb[sd][1] = r16 < G ? w.y : 0u;
     }
@@ -925,7 +928,13 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
   };
   // Block jb's K chunks and V words (jb < nblk); a block outside the cache
   // is read at offset 0, a valid address whose bytes are never used.
-  const uint8_t* kbase = p.c.k + r16 * D + 16 * lg;
+  // K: every load instruction reads whole 64-byte (D = 64) or 128-byte
+  // (D = 128) rows.  D = 64: lane (r16, lg) reads bytes 16lg.. of row r16.
+  // D = 128: load c reads rows 8c..8c+7, lane (r16, lg) bytes 16((r16 >> 3)
+  // + 2lg).. of row 8c + (r16 & 7); one swap with the lane 8 apart (DPP row
+  // rotate) then leaves lane (r16, lg) with bytes 32lg..32lg+31 of row r16.
+  const uint8_t* kbase = (KC == 1) ? p.c.k + r16 * D + 16 * lg : p.c.k + (r16 & 7) * D + 16 * ((r16 >> 3) + 2 * lg);
+  static_assert(KC <= 2, "K row split");
   const uint8_t* vbase = p.c.v + (4 * lg) * D + VB * r16;
   struct Blk {
     U4 k[KC];
@@ -937,7 +946,7 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     const int64_t o0 = offs[jb];
     const int64_t off = uniform64(o0 >= 0 ? o0 : 0);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) kr[c] = stream_load(reinterpret_cast<const U4*>(kbase + off + 64 * c));
+    for (int c = 0; c < KC; ++c) kr[c] = stream_load(reinterpret_cast<const U4*>(kbase + off + 8 * D * c));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (VW == 2) {
@@ -956,7 +965,27 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     if (uniform64(offs[jb]) < 0) return;  // block outside the cache: fully masked
     // ---- scores S^T (keys 4*lg + r, head r16), two accumulation chains ----
     v4f sacc = v4f{0.f, 0.f, 0.f, 0.f}, sacc2 = v4f{0.f, 0.f, 0.f, 0.f};
-    const uint32_t* kw = reinterpret_cast<const uint32_t*>(kr);
+    U4 kx[KC];
+    if constexpr (KC == 1) {
+      kx[0] = kr[0];
+    } else {
+      // lane r16 < 8 holds row r16's chunk 2lg (load 0) and row r16 + 8's
+      // chunk 2lg (load 1); lane r16 >= 8 holds row r16 - 8's chunk 2lg + 1
+      // and row r16's chunk 2lg + 1: each gives the other its foreign chunk
+      const bool lo = r16 < 8;
+      const uint32_t* k0 = reinterpret_cast<const uint32_t*>(&kr[0]);
+      const uint32_t* k1 = reinterpret_cast<const uint32_t*>(&kr[1]);
+      uint32_t* x0 = reinterpret_cast<uint32_t*>(&kx[0]);
+      uint32_t* x1 = reinterpret_cast<uint32_t*>(&kx[1]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t give = lo ? k1[w] : k0[w];
+        const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, kDppRowRor8, 0xF, 0xF, false);
+        x0[w] = lo ? k0[w] : got;
+        x1[w] = lo ? got : k1[w];
+      }
+    }
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(kx);
 #pragma unroll
     for (int sd = 0; sd < KS; ++sd) {
       uint32_t a0, a1;
@@ -1054,7 +1083,7 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     stream_ring(wave, nblk, ring, load, process);
   }
 
-  // ---- combine the four waves: per head, M = max of the wave maxima ----
+  // ---- combine the waves: per head, M = max of the wave maxima ----
   // the wave's row sum of head r16 is spread over its four lane groups
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
