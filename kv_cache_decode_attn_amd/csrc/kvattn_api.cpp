@@ -105,12 +105,16 @@ int make_view(const char* who, const kvattn_cache* c, int32_t batch, const int32
 }
 
 constexpr int32_t kMaxPartTokens = 8192;
+constexpr int64_t kComputeUnits = 256;  // MI355X (gfx950)
 constexpr int32_t kMaxPartScores = 8192;  // part_tokens * group, bounds the LDS
 
 // Default keys per partition, per partition kernel (measured on MI355X):
 //  - fp8 cache with G >= 4 (matrix-core pass): long partitions amortise the
-//    per-workgroup combine and shrink the merge; take the largest size that
-//    still gives >= 256 workgroups (4096 keys at 131K keys x 8 KV heads).
+//    per-workgroup combine and shrink the merge, and the pass runs best at
+//    one workgroup per compute unit (a unit given two workgroups finishes
+//    last).  Take as many partitions per (sequence, KV head) as the 256
+//    units hold, with the keys split as evenly as 64-key steps allow
+//    (4160 keys at 131,073 keys x 8 KV heads: exactly 256 workgroups).
 //  - vector-ALU pass: 512 keys for G >= 4, 256 for G <= 2, shrunk until the
 //    grid offers >= 2048 workgroups.
 bool fp8_mfma_pass(int32_t dtype, int32_t group) { return dtype == KVATTN_FP8_E4M3 && group >= 4; }
@@ -119,9 +123,10 @@ int32_t default_part_tokens(int32_t dtype, int32_t batch, int32_t hq, int32_t hk
   const int32_t group = hq / hkv;
   auto wgs = [&](int32_t t) { return (int64_t)batch * hkv * (((int64_t)max_seq_len + t - 1) / t); };
   if (fp8_mfma_pass(dtype, group)) {
-    int32_t t = kMaxPartTokens;
-    while (t > 256 && wgs(t) < 256) t /= 2;
-    return t;
+    const int64_t heads = (int64_t)batch * hkv;
+    const int64_t per = heads >= kComputeUnits ? 1 : kComputeUnits / heads;
+    const int64_t t = ((max_seq_len + per - 1) / per + 63) / 64 * 64;
+    return (int32_t)(t < 256 ? 256 : t > kMaxPartTokens ? kMaxPartTokens : t);
   }
   int32_t t = group >= 4 ? 512 : 256;
   while (t * group > kMaxPartScores) t /= 2;

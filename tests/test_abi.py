@@ -56,8 +56,15 @@ def test_workspace_and_partition_sizing():
     assert L.kvattn_decode_workspace_bytes(_lib.BF16, 32, 32, 8, 128, 100, 512) == 0  # single partition
     assert L.kvattn_decode_default_part_tokens(_lib.BF16, 1, 3, 2, 100) == 0          # bad group
     assert L.kvattn_decode_default_part_tokens(9, 1, 8, 8, 100) == 0                  # bad dtype
-    # the fp8 matrix-core pass takes long partitions for one long sequence
-    assert L.kvattn_decode_default_part_tokens(_lib.FP8_E4M3, 1, 64, 8, 131073) == 4096
+    # the fp8 matrix-core pass: one workgroup per compute unit (256), keys
+    # split as evenly as 64-key steps allow
+    assert L.kvattn_decode_default_part_tokens(_lib.FP8_E4M3, 1, 64, 8, 131073) == 4160   # 8 x 32 partitions
+    assert L.kvattn_decode_default_part_tokens(_lib.FP8_E4M3, 4, 32, 8, 32768) == 4096    # 32 x 8
+    assert L.kvattn_decode_default_part_tokens(_lib.FP8_E4M3, 1, 64, 8, 1000) == 256      # floor
+    assert L.kvattn_decode_default_part_tokens(_lib.FP8_E4M3, 64, 512, 64, 9000) == 8192  # ceiling
+    for B, Hkv, n in [(1, 8, 131073), (2, 8, 100000), (3, 4, 77777), (1, 1, 50000)]:
+        t = L.kvattn_decode_default_part_tokens(_lib.FP8_E4M3, B, 8 * Hkv, Hkv, n)
+        assert t % 64 == 0 and B * Hkv * -(-n // t) <= 256 or t == 8192, (B, Hkv, n, t)
 
 
 FAKE = 0x10000  # an aligned non-null address; host validation never dereferences it
