@@ -110,10 +110,10 @@ class PagedDecode:
 
     name = "llama3-8b-paged-gqa-decode"
 
-    def __init__(self, replicas=4, wid=2, fused=True):
+    def __init__(self, replicas=4, wid=2, fused=True, batch=32, min_cached=1):
         self.fused = fused
-        self.B, self.Hq, self.Hkv, self.D = 32, 32, 8, 128
-        self.cached = synth.uniform_lengths(self.B, 1, 8192, (wid, synth.T_LENS))
+        self.B, self.Hq, self.Hkv, self.D = batch, 32, 8, 128
+        self.cached = synth.uniform_lengths(self.B, min_cached, 8192, (wid, synth.T_LENS))
         self.ctx = (self.cached + 1).astype(np.int32)          # keys incl. the appended token
         self.maxlen = int(self.ctx.max()) if self.B else 0
         self.max_seq_len = 8193
