@@ -207,3 +207,25 @@ def test_reorder_and_copy_host_errors():
     assert L.kvattn_copy_blocks(ctypes.byref(_cache()), -1, P, P, None) == _lib.EINVAL
     assert L.kvattn_copy_blocks(None, 4, P, P, None) == _lib.EINVAL
     assert L.kvattn_copy_blocks(ctypes.byref(_cache()), 0, None, None, None) == _lib.OK
+
+
+def _decode_multi(c, n_q=4, hq=32, k_new=None, v_new=None, in_dtype=-1, part=0):
+    L = _lib.lib()
+    return L.kvattn_attn_decode_multi(ctypes.byref(c), 4, hq, n_q, FAKE, _lib.BF16, k_new, v_new, in_dtype, FAKE, 1000,
+                                      FAKE, 64, None, 0, 0.1, FAKE, None, 0, part, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({"n_q": 0}, _lib.EINVAL),
+    ({"n_q": 17}, _lib.EINVAL),
+    ({"hq": 8, "n_q": 3}, _lib.EUNSUPPORTED),                          # G 1 x 3 queries = 3 columns
+    ({"hq": 64, "n_q": 4}, _lib.EUNSUPPORTED),                         # G 8 x 4 = 32 columns > 16
+    ({"k_new": FAKE}, _lib.EINVAL),                                    # k_new without v_new / dtype
+    ({"k_new": FAKE, "v_new": FAKE, "in_dtype": 7}, _lib.EINVAL),
+    ({"k_new": FAKE, "in_dtype": _lib.BF16}, _lib.EINVAL),            # v_new missing
+    ({"k_new": FAKE, "v_new": FAKE, "in_dtype": _lib.F32}, _lib.EUNSUPPORTED),  # f32 rows into a bf16 cache
+    ({}, _lib.EWORKSPACE),                                             # valid up to the workspace
+])
+def test_decode_multi_host_errors(kw, want):
+    assert _decode_multi(_cache(), **kw) == want
+    assert _lib.lib().kvattn_last_error().decode() != ""
