@@ -173,3 +173,35 @@ def test_causal_prefill_8192_full_size():
     all_pos = list(range(w.N))
     assert torch.equal(_paged_rows(w.cache.k, w.table, 0, all_pos).transpose(0, 1), w.k[0])
     assert torch.equal(_paged_rows(w.cache.v, w.table, 0, all_pos).transpose(0, 1), w.v[0])
+
+
+def test_chunked_prefill_6144_cached_2048_new_full_size():
+    """A 2,048-token chunk of a 32/8-head layer at positions 6,144..8,191
+    attending the 6,144 cached positions and, causally, itself (the timed
+    attn_prefill with attend_prefix): sampled rows of every head against the
+    oracle, and the chunk's cache write bit for bit."""
+    bench = _bench()
+    from kv_cache_decode_attn_amd import synth
+    w = bench.ChunkedPrefill()
+    w.step(0)
+    torch.cuda.synchronize()
+    std = 1.0 / math.sqrt(w.D)
+    kp = synth.normal_device((1, w.Hkv, w.P, w.D), (8, synth.T_K), std=std)   # the appended prefix
+    vp = synth.normal_device((1, w.Hkv, w.P, w.D), (8, synth.T_V), std=std)
+    kf = np.concatenate([f64(kp[0]), f64(w.k[0])], axis=1)
+    vf = np.concatenate([f64(vp[0]), f64(w.v[0])], axis=1)
+    rows = sorted({0, 1, 31, 32, 1023, 2046, 2047} |
+                  set(int(x) for x in np.random.default_rng(105).choice(w.n, size=5, replace=False)))
+    got = w.out[0][:, rows].cpu().numpy()
+    qf = f64(w.q[0][:, rows])
+    G = w.Hq // w.Hkv
+    scale = 1.0 / math.sqrt(w.D)
+    allow = np.arange(w.P + w.n)[None, :] <= (w.P + np.asarray(rows))[:, None]
+    for h in range(w.Hq):
+        want = OA.sdpa(qf[h], kf[h // G], vf[h // G], allow, scale)
+        assert max_abs(got[h], want) <= TOL, h
+    new_pos = list(range(w.P, w.P + w.n))
+    assert torch.equal(_paged_rows(w.cache.k, w.table, 0, new_pos).transpose(0, 1), w.k[0])
+    assert torch.equal(_paged_rows(w.cache.v, w.table, 0, new_pos).transpose(0, 1), w.v[0])
+    prefix_pos = list(range(w.P))
+    assert torch.equal(_paged_rows(w.cache.k, w.table, 0, prefix_pos).transpose(0, 1), kp[0])
