@@ -343,7 +343,9 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
   extern __shared__ float lds[];
   // KV head fastest in the grid: neighbouring workgroups read the heads of
   // the same 16-token blocks, which sit side by side in the paged pool.
-  const int g = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
+  // grid (KV head, sequence, partition): partition-major, so every
+  // sequence's first partitions are dispatched before any later one
+  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int col = lane % LPT, row = lane / LPT;
@@ -1246,7 +1248,8 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_partition_bf16_mfma<D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
   } else {
     const size_t lds = (size_t)(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
-    hipLaunchKernelGGL((decode_partition<KVT, D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
+    const dim3 pgrid(a.num_kv_heads, a.batch, a.num_parts);
+    hipLaunchKernelGGL((decode_partition<KVT, D, G, MASK, TAIL>), pgrid, dim3(256), lds, s, a);
   }
   if (hipGetLastError() != hipSuccess) return KVATTN_ELAUNCH;
   if (a.num_parts > 1) {
