@@ -74,49 +74,63 @@ def attention_weights(q, K, allow, scale):
     return w
 
 
-def tiled_softmax_dot(q, K, V, scale, tile, allow=None):
-    """One query against K/V, visiting the keys tile by tile with a running
-    (max, sum) pair - the second route to the same result.
+def softmax_state(z, V):
+    """Unnormalised softmax state (m, l, o) of a set of scaled scores z and
+    their value rows V: m = max z, l = sum exp(z - m), o = sum exp(z - m) v.
+    An empty set has the state (-inf, 0, 0)."""
+    z = np.asarray(z, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if z.size == 0:
+        return (-np.inf, 0.0, np.zeros(V.shape[1], dtype=np.float64))
+    m = float(z.max())
+    e = np.exp(z - m)
+    return (m, float(e.sum()), e @ V)
 
-    [P1] section "Build it", Step 2 (tiled softmax) and section "Flash
-    Attention", numerical trick: keep a running maximum m, a running sum s
-    and an unnormalised output; for each tile take the new maximum over the
-    old one and the tile's scores, rescale s and the output by
-    exp(m_old - m_new) (that factor is 0 while m_old is still -inf), add the
-    tile's exponentials, and divide by s at the end.  Added to the page's
-    version: the 1/sqrt(d) score scale, and keys with allow == 0 are left out
-    of their tile.  A query that sees no key returns zeros.
+
+def combine_states(a, b):
+    """State of the union of two disjoint key sets from their two states:
+    both are brought to the common maximum M = max(m_a, m_b) by the factors
+    exp(m_a - M) and exp(m_b - M), then l and o add.  [P1] section "Flash
+    Attention - tiling trick", numerical trick: keeping the running maximum
+    and sum is what makes a tiled softmax exact."""
+    ma, la, oa = a
+    mb, lb, ob = b
+    if mb == -np.inf:
+        return a
+    if ma == -np.inf:
+        return b
+    M = max(ma, mb)
+    fa, fb = np.exp(ma - M), np.exp(mb - M)
+    return (M, la * fa + lb * fb, oa * fa + ob * fb)
+
+
+def tiled_fold(q, K, V, scale, tile, allow=None):
+    """One query against K/V, the keys consumed `tile` at a time: each tile's
+    own state (softmax_state of its allowed keys) is folded into the running
+    state with combine_states, and the output is o / l at the end - the
+    second route to the result of sdpa, which never holds more than one tile
+    of scores ([P1] section "Flash Attention - tiling trick"; the pages'
+    version of this algorithm has no score scale and no mask, both added
+    here).  A query that sees no key returns zeros.
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     n = K.shape[0]
     allow = np.ones(n, dtype=bool) if allow is None else np.asarray(allow).astype(bool)
-    m = -np.inf
-    s = 0.0
-    out = np.zeros(V.shape[1], dtype=np.float64)
-    for start in range(0, n, tile):
-        keep = np.nonzero(allow[start:start + tile])[0] + start
-        if keep.size == 0:
-            continue
-        scores = (K[keep] @ q) * scale
-        new_m = max(m, float(scores.max()))
-        exp_old = np.exp(m - new_m) if m != -np.inf else 0.0
-        exp_new = np.exp(scores - new_m)
-        s = s * exp_old + exp_new.sum()
-        out = out * exp_old + exp_new @ V[keep]
-        m = new_m
-    if s == 0.0:
-        return out
-    return out / s
+    state = softmax_state(np.zeros(0), V[:0])
+    for lo in range(0, n, tile):
+        idx = lo + np.flatnonzero(allow[lo:lo + tile])
+        state = combine_states(state, softmax_state((K[idx] @ q) * scale, V[idx]))
+    _, l, o = state
+    return o / l if l > 0 else o
 
 
 def split_partials(q, K, V, scale, part, allow=None):
     """Split the keys into consecutive partitions of `part` keys and return,
-    per partition, the unnormalised softmax state (m, l, o): m the largest
-    allowed score (-inf if none), l = sum exp(z - m), o = sum exp(z - m) v.
-    The exact-renormalisation identity of [P1] "Flash Attention", numerical
-    trick, applied across partitions instead of tiles.
+    per partition, the softmax_state (m, l, o) of its allowed keys: the
+    exact-renormalisation identity of [P1] "Flash Attention - tiling trick",
+    numerical trick, applied across partitions instead of tiles.
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -124,15 +138,9 @@ def split_partials(q, K, V, scale, part, allow=None):
     n = K.shape[0]
     allow = np.ones(n, dtype=bool) if allow is None else np.asarray(allow).astype(bool)
     parts = []
-    for start in range(0, n, part):
-        keep = np.nonzero(allow[start:start + part])[0] + start
-        if keep.size == 0:
-            parts.append((-np.inf, 0.0, np.zeros(V.shape[1])))
-            continue
-        z = (K[keep] @ q) * scale
-        m = float(z.max())
-        e = np.exp(z - m)
-        parts.append((m, float(e.sum()), e @ V[keep]))
+    for lo in range(0, n, part):
+        idx = lo + np.flatnonzero(allow[lo:lo + part])
+        parts.append(softmax_state((K[idx] @ q) * scale, V[idx]))
     return parts
 
 

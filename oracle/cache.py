@@ -74,34 +74,38 @@ def encode_rows(x_storage, in_dtype, cache_dtype, scale=None):
     raise ValueError("unsupported conversion %r -> %r" % (in_dtype, cache_dtype))
 
 
-class LogicalCache:
-    """Per-sequence, per-KV-head position-indexed K/V rows with the append
-    contract.
+class SequenceStore:
+    """Logical contents of one layer's cache: per sequence, an fp64 array
+    [Hkv, stored length, d] for K and one for V, in position order, with the
+    append contract.
 
-    [P1] section "Build it", Step 1 (a KV cache keeps per-layer, per-head
-    lists and appends one token's K, V at a time); [P4] section "Position IDs
-    and the append contract" (an append must happen at cache_position equal to
-    the current stored length, positions 0-based).  One instance is one layer.
+    [P3] section "Tensor" (the cache of one layer is [batch, kv_heads, seq,
+    head_dim]; here each sequence keeps its own seq extent); [P4] section
+    "Position IDs and the append contract" (new rows go in at cache_position
+    equal to the current stored length, positions 0-based; anything else is
+    an error).
     """
 
     def __init__(self, batch, kv_heads, head_dim):
-        self.k = [[[] for _ in range(kv_heads)] for _ in range(batch)]
-        self.v = [[[] for _ in range(kv_heads)] for _ in range(batch)]
-        self.length = [0] * batch
+        empty = np.zeros((kv_heads, 0, head_dim), dtype=np.float64)
+        self.k = [empty.copy() for _ in range(batch)]
+        self.v = [empty.copy() for _ in range(batch)]
 
-    def append(self, b, position, k_rows, v_rows):
-        """k_rows, v_rows: [Hkv, n, d] fp64 values of n new tokens."""
-        assert position == self.length[b], "append at %d, stored length %d" % (position, self.length[b])
-        n = np.asarray(k_rows).shape[1]
-        for g in range(len(self.k[b])):
-            for i in range(n):
-                self.k[b][g].append(np.asarray(k_rows[g][i], dtype=np.float64))
-                self.v[b][g].append(np.asarray(v_rows[g][i], dtype=np.float64))
-        self.length[b] += n
+    def stored(self, b):
+        """Positions stored for sequence b."""
+        return self.k[b].shape[1]
 
-    def read(self, b, g):
-        """([len, d], [len, d]) fp64 arrays of sequence b, KV head g."""
-        return np.array(self.k[b][g]), np.array(self.v[b][g])
+    def store(self, b, position, k_rows, v_rows):
+        """k_rows, v_rows: [Hkv, n, d] values of n new tokens at positions
+        position .. position + n - 1 of sequence b."""
+        if position != self.stored(b):
+            raise ValueError("store at position %d, stored length %d" % (position, self.stored(b)))
+        self.k[b] = np.concatenate([self.k[b], np.asarray(k_rows, dtype=np.float64)], axis=1)
+        self.v[b] = np.concatenate([self.v[b], np.asarray(v_rows, dtype=np.float64)], axis=1)
+
+    def head(self, b, g):
+        """([len, d], [len, d]) arrays of sequence b, KV head g."""
+        return self.k[b][g], self.v[b][g]
 
 
 def predict_append(cache_k, cache_v, k_new, v_new, positions, n_new, paged,

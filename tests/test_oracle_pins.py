@@ -180,7 +180,7 @@ def test_tiled_running_max_equals_one_shot(tile):
     q, k, v = rng.standard_normal(d), rng.standard_normal((n, d)) * 3, rng.standard_normal((n, d))
     allow = rng.random(n) < 0.8
     allow[0] = False  # a masked key inside the first tile
-    got = A.tiled_softmax_dot(q, k, v, 0.25, tile, allow)
+    got = A.tiled_fold(q, k, v, 0.25, tile, allow)
     want = A.sdpa(q[None], k, v, allow[None], 0.25)[0]
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
 
@@ -191,7 +191,7 @@ def test_tiled_with_masked_first_tiles():
     q, k, v = rng.standard_normal(8), rng.standard_normal((20, 8)), rng.standard_normal((20, 8))
     allow = np.zeros(20, bool)
     allow[13:] = True
-    np.testing.assert_allclose(A.tiled_softmax_dot(q, k, v, 0.5, 4, allow),
+    np.testing.assert_allclose(A.tiled_fold(q, k, v, 0.5, 4, allow),
                                A.sdpa(q[None], k, v, allow[None], 0.5)[0], rtol=1e-12, atol=1e-13)
 
 
@@ -256,6 +256,200 @@ def test_chunked_prefill_equals_matching_rows_of_full_prefill():
     second = A.prefill(q[:, :, c:], k[:, :, c:], v[:, :, c:], [c], [N - c], 0.4,
                        prefix_k=[k[0]], prefix_v=[v[0]], attend_prefix=True)
     np.testing.assert_allclose(second[:, :, :N - c], full[:, :, c:], rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------ prefill masking branches ------
+#
+# Each case below runs oracle.attention.prefill and compares every output row
+# with a brute force written from the definition alone: pure-Python loops
+# over absolute key positions with math.exp, no numpy linear algebra and no
+# call into the oracle.
+
+
+def _brute_prefill(q, k_new, v_new, positions, q_lens, scale, causal, key_mask=None,
+                   prefix_k=None, prefix_v=None, attend_prefix=False):
+    """out[b, h, t] for the rows t < q_lens[b]; rows past q_lens[b] are 0.
+    Query t of sequence b sits at absolute position P + t (P = positions[b]);
+    it may read key position s iff lo <= s < P + q_lens[b] (lo = 0 with a
+    cached prefix, else P), s <= P + t when causal, and key_mask[b][s] != 0
+    when a mask is given (the mask is indexed by ABSOLUTE position).  Key s
+    comes from the prefix when s < P, else from new row s - P."""
+    B, Hq, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv = len(k_new[0])
+    G = Hq // Hkv
+    dv = len(v_new[0][0][0])
+    out = np.zeros((B, Hq, N, dv))
+    for b in range(B):
+        P, n = int(positions[b]), int(q_lens[b])
+        for h in range(Hq):
+            g = h // G
+            for t in range(n):
+                keys = []
+                for s in range(0 if attend_prefix else P, P + n):
+                    if causal and s > P + t:
+                        continue
+                    if key_mask is not None and not key_mask[b][s]:
+                        continue
+                    keys.append(s)
+                if not keys:
+                    continue
+                krow = lambda s: prefix_k[b][g][s] if s < P else k_new[b][g][s - P]
+                vrow = lambda s: prefix_v[b][g][s] if s < P else v_new[b][g][s - P]
+                z = [scale * sum(float(q[b][h][t][i]) * float(krow(s)[i]) for i in range(d)) for s in keys]
+                zmax = max(z)
+                e = [math.exp(x - zmax) for x in z]
+                tot = sum(e)
+                for j in range(dv):
+                    out[b, h, t, j] = sum(e[i] / tot * float(vrow(s)[j]) for i, s in enumerate(keys))
+    return out
+
+
+def _padded_batch(rng, d=6):
+    """The padding example of [P4] "Padding mask and batch length": real
+    length 3 ([A, B, C]) padded to a batch length of 5 ([A, B, C, PAD,
+    PAD]), two such sequences; PAD K/V are NaN so that any leak shows."""
+    B, Hq, Hkv, N = 2, 2, 1, 5
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    k[:, :, 3:] = np.nan
+    v[:, :, 3:] = np.nan
+    mask = np.array([[1, 1, 1, 0, 0], [1, 1, 1, 0, 0]], np.uint8)
+    return q, k, v, mask
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_padding_example_padded_rows_zero(causal):
+    """[P4] "Padding mask and batch length" and "Implementation and
+    verification procedure" (two length-3 inputs padded into one batch, PAD
+    influence checked): with q_lens = [3, 3] the PAD query rows are 0 and the
+    real rows equal the brute force over keys 0..2 - causal or not."""
+    rng = np.random.default_rng(70)
+    q, k, v, mask = _padded_batch(rng)
+    scale = 1 / math.sqrt(6)
+    got = A.prefill(q, k, v, [0, 0], [3, 3], scale, causal=causal, key_mask=mask)
+    want = _brute_prefill(q, k, v, [0, 0], [3, 3], scale, causal, key_mask=mask)
+    assert np.all(np.isfinite(got))
+    assert np.all(got[:, :, 3:] == 0.0)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    # without the key mask the result is the same: keys past q_lens are not keys
+    np.testing.assert_array_equal(A.prefill(q, k, v, [0, 0], [3, 3], scale, causal=causal), got)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_padding_example_key_mask_blocks_pad(causal):
+    """Same batch with every row a query (q_lens = [5, 5]) and the padding
+    mask on the keys: PAD keys get weight 0, so every row - the PAD query
+    rows included - is finite and equals the brute force over keys 0..2.
+    Non-causal, rows 0..2 all see A, B, C (an encoder reads the future but
+    never PAD)."""
+    rng = np.random.default_rng(71)
+    q, k, v, mask = _padded_batch(rng)
+    scale = 0.37
+    got = A.prefill(q, k, v, [0, 0], [5, 5], scale, causal=causal, key_mask=mask)
+    want = _brute_prefill(q, k, v, [0, 0], [5, 5], scale, causal, key_mask=mask)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    if not causal:
+        # every query of a sequence reads the same three keys
+        w = A.attention_weights(q[0, 0], k[0, 0, :3], np.ones((5, 3)), scale)
+        np.testing.assert_allclose(got[0, 0], w @ v[0, 0, :3], rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_non_causal_equals_library_softmax():
+    """causal=False: every query row reads every real key; each row equals
+    scipy's softmax of the scaled scores applied to V."""
+    rng = np.random.default_rng(72)
+    B, Hq, Hkv, N, d = 2, 4, 2, 7, 5
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    lens = [7, 4]
+    got = A.prefill(q, k, v, [0, 0], lens, 0.45, causal=False)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // 2
+            for t in range(N):
+                if t >= lens[b]:
+                    assert np.all(got[b, h, t] == 0.0)
+                    continue
+                w = scipy.special.softmax(0.45 * k[b, g, :lens[b]] @ q[b, h, t])
+                np.testing.assert_allclose(got[b, h, t], w @ v[b, g, :lens[b]], rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_at_offset_without_prefix():
+    """positions > 0 with attend_prefix=False: only the new keys are read,
+    causal by absolute position - the same as the same tokens at position 0,
+    and as the brute force; a key mask indexed by absolute position."""
+    rng = np.random.default_rng(73)
+    B, Hq, Hkv, N, d = 2, 2, 1, 6, 4
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    pos, lens = [9, 4], [6, 5]
+    got = A.prefill(q, k, v, pos, lens, 0.6)
+    np.testing.assert_allclose(got, A.prefill(q, k, v, [0, 0], lens, 0.6), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(got, _brute_prefill(q, k, v, pos, lens, 0.6, True), rtol=1e-12, atol=1e-13)
+    mask = (rng.random((B, 16)) < 0.6).astype(np.uint8)
+    got_m = A.prefill(q, k, v, pos, lens, 0.6, key_mask=mask)
+    np.testing.assert_allclose(got_m, _brute_prefill(q, k, v, pos, lens, 0.6, True, key_mask=mask),
+                               rtol=1e-12, atol=1e-13)
+
+
+def _prefix_case(rng):
+    B, Hq, Hkv, N, d = 2, 4, 2, 5, 4
+    pos = [7, 11]
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    pk = [rng.standard_normal((Hkv, 16, d)) for _ in range(B)]
+    pv = [rng.standard_normal((Hkv, 16, d)) for _ in range(B)]
+    lens = [5, 3]
+    # a mask whose absolute and relative (s - P) readings differ
+    mask = (rng.random((B, 20)) < 0.55).astype(np.uint8)
+    for b in range(B):
+        mask[b, pos[b]] = 1
+        assert any(mask[b, s] != mask[b, s - pos[b]] for s in range(pos[b], pos[b] + lens[b]))
+    return q, k, v, pk, pv, pos, lens, mask
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_prefix_key_mask_is_absolute(causal):
+    """attend_prefix with a key mask: the mask is read at the absolute key
+    position ([P4] "Causal mask and future positions": position IDs are
+    absolute token positions), for prefix and new keys alike."""
+    rng = np.random.default_rng(74)
+    q, k, v, pk, pv, pos, lens, mask = _prefix_case(rng)
+    got = A.prefill(q, k, v, pos, lens, 0.5, causal=causal, key_mask=mask,
+                    prefix_k=pk, prefix_v=pv, attend_prefix=True)
+    want = _brute_prefill(q, k, v, pos, lens, 0.5, causal, key_mask=mask,
+                          prefix_k=pk, prefix_v=pv, attend_prefix=True)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_pins_catch_planted_slips():
+    """The brute-force comparison above is strong enough to catch the slips it
+    guards against, planted here in copies of the oracle's inputs/outputs:
+    a key mask read at the relative index s - P, a padded row that is not
+    zeroed, and a causal test with the wrong sign."""
+    rng = np.random.default_rng(74)
+    q, k, v, pk, pv, pos, lens, mask = _prefix_case(rng)
+    want = _brute_prefill(q, k, v, pos, lens, 0.5, True, key_mask=mask,
+                          prefix_k=pk, prefix_v=pv, attend_prefix=True)
+    # relative indexing of the mask = an absolute mask shifted by P
+    rel = np.zeros_like(mask)
+    for b in range(2):
+        rel[b, pos[b]:] = mask[b, :mask.shape[1] - pos[b]]
+    slip = A.prefill(q, k, v, pos, lens, 0.5, key_mask=rel, prefix_k=pk, prefix_v=pv, attend_prefix=True)
+    assert np.abs(slip - want).max() > 1e-3
+    # a padded row left unzeroed (the row computed as if it were real)
+    q2, k2, v2, m2 = _padded_batch(np.random.default_rng(70))
+    ref = _brute_prefill(q2, k2, v2, [0, 0], [3, 3], 0.4, True, key_mask=m2)
+    unzeroed = A.prefill(q2, k2, v2, [0, 0], [5, 5], 0.4, key_mask=m2)
+    assert np.abs(unzeroed - ref).max() > 1e-3
+    # the causal direction flipped (future allowed, past blocked)
+    flipped = A.sdpa(q2[0, 0, :3], k2[0, 0, :3], v2[0, 0, :3], A.causal_allow(3).T, 0.4)
+    assert np.abs(flipped - ref[0, 0, :3]).max() > 1e-3
 
 
 def test_gqa_equals_mha_with_repeated_kv_heads():
@@ -370,17 +564,19 @@ def test_op_counts_printed_example():
     assert C.op_counts(100) == (5050, 100)
 
 
-def test_logical_cache_append_contract():
+def test_sequence_store_append_contract():
     """[P4] "Position IDs and the append contract": appending at a position
     other than the stored length is an error."""
-    lc = C.LogicalCache(1, 2, 4)
-    lc.append(0, 0, np.ones((2, 3, 4)), np.zeros((2, 3, 4)))
-    assert lc.length[0] == 3
-    with pytest.raises(AssertionError):
-        lc.append(0, 5, np.ones((2, 1, 4)), np.ones((2, 1, 4)))
-    lc.append(0, 3, 2 * np.ones((2, 1, 4)), np.ones((2, 1, 4)))
-    k, v = lc.read(0, 1)
-    assert k.shape == (4, 4) and k[3, 0] == 2.0 and v[3, 0] == 1.0
+    st = C.SequenceStore(2, 2, 4)
+    st.store(0, 0, np.ones((2, 3, 4)), np.zeros((2, 3, 4)))
+    assert st.stored(0) == 3 and st.stored(1) == 0
+    with pytest.raises(ValueError):
+        st.store(0, 5, np.ones((2, 1, 4)), np.ones((2, 1, 4)))
+    with pytest.raises(ValueError):
+        st.store(1, 1, np.ones((2, 1, 4)), np.ones((2, 1, 4)))
+    st.store(0, 3, 2 * np.ones((2, 1, 4)), np.ones((2, 1, 4)))
+    k, v = st.head(0, 1)
+    assert k.shape == (4, 4) and k[3, 0] == 2.0 and v[3, 0] == 1.0 and v[0, 0] == 0.0
 
 
 def test_predict_append_paged_roundtrip_and_canaries():
