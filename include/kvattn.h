@@ -169,7 +169,9 @@ size_t kvattn_decode_workspace_bytes(int32_t cache_dtype, int32_t batch, int32_t
 
 /* Keys per split-K partition that part_tokens == 0 selects for these sizes
  * and this cache element type (measured per partition kernel: enough
- * workgroups for the 256 compute units, few enough partials for the merge).
+ * workgroups for the current device's compute units - 256 on a whole
+ * MI355X, and 256 is assumed when no device is visible - few enough
+ * partials for the merge).
  * Returns 0 for invalid sizes. */
 int32_t kvattn_decode_default_part_tokens(int32_t cache_dtype, int32_t batch, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t max_seq_len);

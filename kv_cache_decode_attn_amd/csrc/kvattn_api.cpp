@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "kvattn.h"
@@ -105,15 +106,39 @@ int make_view(const char* who, const kvattn_cache* c, int32_t batch, const int32
 }
 
 constexpr int32_t kMaxPartTokens = 8192;
-constexpr int64_t kComputeUnits = 256;  // MI355X (gfx950)
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device, read once per device.  A host with
+// no visible device (sizing queries made on a CPU-only machine) gets 256, the
+// count of a whole MI355X; a partitioned MI355X (CPX mode) reports its
+// partition's share and the default partitioning follows it.
+int64_t compute_units() {
+  static std::mutex mu;
+  static int cus[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();  // leave no sticky error for the caller's next HIP call
+    return 256;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 constexpr int32_t kMaxPartScores = 8192;  // part_tokens * group, bounds the LDS
 
 // Default keys per partition, per partition kernel (measured on MI355X):
 //  - fp8 cache with G >= 4 (matrix-core pass): long partitions amortise the
 //    per-workgroup combine and shrink the merge, and the pass runs best at
 //    one workgroup per compute unit (a unit given two workgroups finishes
-//    last).  Take as many partitions per (sequence, KV head) as the 256
-//    units hold, with the keys split as evenly as 64-key steps allow
+//    last).  Take as many partitions per (sequence, KV head) as the device's
+//    compute units hold, with the keys split as evenly as 64-key steps allow
 //    (4160 keys at 131,073 keys x 8 KV heads: exactly 256 workgroups).
 //  - vector-ALU pass: 512 keys for G >= 4, 256 for G <= 2, shrunk until the
 //    grid offers >= 2048 workgroups.
@@ -124,7 +149,8 @@ int32_t default_part_tokens(int32_t dtype, int32_t batch, int32_t hq, int32_t hk
   auto wgs = [&](int32_t t) { return (int64_t)batch * hkv * (((int64_t)max_seq_len + t - 1) / t); };
   if (fp8_mfma_pass(dtype, group)) {
     const int64_t heads = (int64_t)batch * hkv;
-    const int64_t per = heads >= kComputeUnits ? 1 : kComputeUnits / heads;
+    const int64_t units = compute_units();
+    const int64_t per = heads >= units ? 1 : units / heads;
     const int64_t t = ((max_seq_len + per - 1) / per + 63) / 64 * 64;
     return (int32_t)(t < 256 ? 256 : t > kMaxPartTokens ? kMaxPartTokens : t);
   }
