@@ -249,6 +249,36 @@ int kvattn_attn_decode_append(const kvattn_cache* cache, int32_t batch, int32_t 
                               void* workspace, size_t workspace_bytes, int32_t part_tokens,
                               void* stream);
 
+/* kvattn_attn_decode_append_noalloc - kvattn_attn_decode_append for callers
+ * that cannot allocate device memory: code under HIP graph capture, serving
+ * loops that forbid allocation, harnesses without an allocator.  It takes no
+ * workspace; the split-K partials go to a static device array of the library
+ * (KVATTN_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the first call on
+ * that GPU until the process ends).  The call allocates and frees nothing.
+ *
+ * Same arguments, same kernels and the same result as
+ * kvattn_attn_decode_append without its workspace arguments, bit for bit.
+ * Sizes whose partials (kvattn_decode_workspace_bytes for the same
+ * arguments) exceed KVATTN_NOALLOC_SCRATCH_BYTES are refused with
+ * KVATTN_EWORKSPACE before anything is enqueued.  The stream must belong to
+ * the current device.
+ *
+ * Every call on one GPU uses that GPU's one array, and the array keeps the
+ * last call's contents (nothing in it needs to start at zero: every partial
+ * the merge reads was written by the same call).  Two calls that overlap in
+ * time on one GPU - on different streams, or from different threads - race
+ * on the array: serialise them.
+ */
+#define KVATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int kvattn_attn_decode_append_noalloc(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads,
+                                      const void* q, int32_t q_dtype,
+                                      const void* k_new, const void* v_new, int32_t in_dtype,
+                                      const int32_t* seq_lens, int32_t max_seq_len,
+                                      const int32_t* block_table, int32_t max_blocks,
+                                      const uint8_t* key_mask, int64_t key_mask_stride,
+                                      float scale, float* out, int32_t part_tokens,
+                                      void* stream);
+
 /* kvattn_attn_decode_multi - n_q new query tokens per sequence against the
  * cache that already holds them: decoding several tokens at once, such as
  * checking drafted tokens (speculative decoding) - the cache-read-bound

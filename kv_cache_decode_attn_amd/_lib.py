@@ -12,12 +12,14 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 CONTIGUOUS, PAGED = 0, 1
 BLOCK_TOKENS = 16
 VALIDATE_LEN_RANGE, VALIDATE_BLOCK_RANGE, VALIDATE_POSITION = 1, 2, 4
+NOALLOC_SCRATCH_BYTES = 16 << 20  # KVATTN_NOALLOC_SCRATCH_BYTES
 
 # Every symbol include/kvattn.h declares.
 EXPORTS = (
     "kvattn_version", "kvattn_status_string", "kvattn_last_error", "kvattn_cache_bytes",
     "kvattn_kv_append", "kvattn_decode_workspace_bytes", "kvattn_decode_default_part_tokens",
-    "kvattn_attn_decode", "kvattn_attn_decode_append", "kvattn_attn_decode_multi", "kvattn_attn_prefill",
+    "kvattn_attn_decode", "kvattn_attn_decode_append", "kvattn_attn_decode_append_noalloc",
+    "kvattn_attn_decode_multi", "kvattn_attn_prefill",
     "kvattn_validate",
     "kvattn_reorder_rows", "kvattn_reorder_cache", "kvattn_copy_blocks",
     "kvattn_pool_create", "kvattn_pool_destroy", "kvattn_pool_num_blocks", "kvattn_pool_num_free",
@@ -70,6 +72,8 @@ _SIGS = {
                                           _F, _P, _P, _SZ, _I32, _P]),
     "kvattn_attn_decode_append": (ctypes.c_int, [_CP, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _I32, _P,
                                                  _I64, _F, _P, _P, _SZ, _I32, _P]),
+    "kvattn_attn_decode_append_noalloc": (ctypes.c_int, [_CP, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P,
+                                                         _I32, _P, _I64, _F, _P, _I32, _P]),
     "kvattn_attn_decode_multi": (ctypes.c_int, [_CP, _I32, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P, _I32,
                                                 _P, _I64, _F, _P, _P, _SZ, _I32, _P]),
     "kvattn_attn_prefill": (ctypes.c_int, [_CP, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P,

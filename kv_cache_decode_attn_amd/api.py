@@ -221,6 +221,39 @@ def attn_decode_append(cache, q, k_new, v_new, seq_lens, max_seq_len, block_tabl
 
 
 
+def attn_decode_append_noalloc(cache, q, k_new, v_new, seq_lens, max_seq_len, block_table=None, key_mask=None,
+                               scale=None, out=None, part_tokens=0):
+    """attn_decode_append without a workspace (kvattn_attn_decode_append_noalloc):
+    the split-K partials go to the library's static per-GPU scratch array
+    (NOALLOC_SCRATCH_BYTES).  `out` must be given for a call that allocates
+    nothing at all (else it is allocated here).  Calls on one GPU share the
+    array: do not overlap them."""
+    _dev(q, "q")
+    _dev(k_new, "k_new")
+    _dev(v_new, "v_new")
+    _i32(seq_lens, "seq_lens")
+    _i32(block_table, "block_table")
+    _dev(key_mask, "key_mask")
+    if key_mask is not None and key_mask.dtype != torch.uint8:
+        raise TypeError("key_mask must be uint8")
+    if k_new.dtype not in _CODE or v_new.dtype != k_new.dtype or k_new.shape != v_new.shape:
+        raise TypeError("k_new/v_new must be matching f32 or bf16 tensors")
+    B, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _dev(out, "out")
+    mb = block_table.shape[1] if block_table is not None else 0
+    stride = key_mask.shape[1] if key_mask is not None else 0
+    check(lib().kvattn_attn_decode_append_noalloc(ctypes.byref(cache.desc()), B, Hq, _ptr(q), _CODE.get(q.dtype, -1),
+                                                  _ptr(k_new), _ptr(v_new), _CODE[k_new.dtype], _ptr(seq_lens),
+                                                  int(max_seq_len), _ptr(block_table), mb, _ptr(key_mask), stride,
+                                                  float(scale), _ptr(out), int(part_tokens), _stream(q.device)))
+    return out
+
+
+
 def attn_decode_multi(cache, q, seq_lens, max_seq_len, k_new=None, v_new=None, block_table=None, key_mask=None,
                       scale=None, out=None, workspace=None, part_tokens=0):
     """n_q query tokens per sequence against the cache (kvattn_attn_decode_multi):

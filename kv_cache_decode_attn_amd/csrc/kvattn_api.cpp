@@ -362,6 +362,74 @@ int kvattn_attn_decode_append(const kvattn_cache* cache, int32_t batch, int32_t 
                           out, workspace, workspace_bytes, part_tokens, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Device memory of kvattn_attn_decode_append_noalloc: the split-K partials
+// live in this array instead of a caller workspace.  Every device the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` is only a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[KVATTN_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (NULL with the error recorded).
+void* scratch_address(const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    fail(KVATTN_ELAUNCH, "%s: no current HIP device (%s)", who, hipGetErrorString(e));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      fail(KVATTN_ELAUNCH, "%s: hipGetSymbolAddress of the scratch array failed on device %d (%s)", who, dev,
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvattn_attn_decode_append_noalloc(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, const void* q,
+                                      int32_t q_dtype, const void* k_new, const void* v_new, int32_t in_dtype,
+                                      const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                                      int32_t max_blocks, const uint8_t* key_mask, int64_t key_mask_stride,
+                                      float scale, float* out, int32_t part_tokens, void* stream) {
+  const char* who = "kvattn_attn_decode_append_noalloc";
+  if (!cache) return fail(KVATTN_EINVAL, "%s: cache descriptor is NULL", who);
+  if (in_dtype < 0) return fail(KVATTN_EINVAL, "%s: input dtype must be f32 or bf16", who);
+  // the partials this call needs must fit the static array
+  const size_t need = kvattn_decode_workspace_bytes(cache->dtype, batch, num_q_heads, cache->num_kv_heads,
+                                                    cache->head_dim, max_seq_len, part_tokens);
+  if (need > (size_t)KVATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(KVATTN_EWORKSPACE,
+                "%s: these sizes need %zu bytes of split-K partials, more than the %zu-byte static scratch; "
+                "use kvattn_attn_decode_append with a workspace",
+                who, need, (size_t)KVATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address(who);
+    if (!ws) return KVATTN_ELAUNCH;
+  }
+  return attn_decode_impl(who, cache, batch, num_q_heads, q, q_dtype, k_new, v_new, in_dtype, seq_lens, max_seq_len,
+                          block_table, max_blocks, key_mask, key_mask_stride, scale, out, ws,
+                          need > 0 ? (size_t)KVATTN_NOALLOC_SCRATCH_BYTES : 0, part_tokens, stream);
+}
+
 int kvattn_attn_decode_multi(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t n_q,
                              const void* q, int32_t q_dtype, const void* k_new, const void* v_new, int32_t in_dtype,
                              const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
