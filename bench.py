@@ -12,23 +12,25 @@ HBM bytes per step / step time, in GB/s.  The same step as two calls
 (kv_append, then attn_decode) is timed too and reported beside it.
 
 Other workloads run in the same invocation and are reported under
-"workloads": the padded 32-layer MHA decode (batch 8, 4096-position
-contiguous cache, key padding mask), the 80-layer fp8 long-context decode
-(batch 1, 64/8 heads, 131,073 keys per layer), the check of 4 drafted
-tokens per sequence on the Llama-3-8B decode workload (append, then all 4
-attended together), the causal 8192-token prefill that writes the paged
-cache, a 2048-token chunked prefill against
-6144 cached positions, a copy-on-write fan-out of 4096 paged blocks and a
-contiguous beam reorder (32 rows of 4096 positions).
+"workloads": the tiny fp32 sequence (16-token prefill into the cache, then a
+decode step over 129 keys; latency), the padded 32-layer MHA decode (batch
+8, 4096-position contiguous cache, key padding mask), the 80-layer fp8
+long-context decode (batch 1, 64/8 heads, 131,073 keys per layer), the check
+of 4 drafted tokens per sequence on the Llama-3-8B decode workload, the
+causal 8192-token prefill that writes the paged cache, a 2048-token chunked
+prefill against 6144 cached positions, a copy-on-write fan-out of 4096 paged
+blocks and a contiguous beam reorder (32 rows of 4096 positions).  A plain
+streaming read and copy (torch kernels) are timed as HBM context.
 
 Timing: W untimed warm-up steps, then K steps bracketed by synchronize +
 HIP events on the stream the library launches on (torch's current stream).
 Each decode step reads a different replica of the cache (round-robin) so the
 256 MB Infinity Cache cannot serve the previous step's bytes.  A second pass
-of K steps with HIP events around every call gives the call's own duration
-for the roofline (kept out of the first pass: event records between kernels
-cost a few microseconds each).  The CPU baseline is the fp64 oracle on the host, timed on the
-same inputs (single thread).
+of K steps with HIP events around every call is reported for information.
+The CPU baseline is the fp64 oracle timed on the host's cores (a pool of
+processes, one BLAS thread each) on the same input bytes, for the headline
+step and a stated sample of the padded, fp8 and prefill workloads; each also
+gives the max abs error of the GPU output against the oracle.
 """
 import argparse
 import hashlib
@@ -55,42 +57,49 @@ METRIC = "decode-attn HBM GB/s (% of peak) & seqs/s; prefill TFLOP/s (% MFMA pea
 DEV = "cuda"
 
 
-DECODE_SOURCES = ("kv_cache_decode_attn_amd/csrc/decode.hip", "kv_cache_decode_attn_amd/csrc/common.h")
-LAUNCH_HEADER = "kv_cache_decode_attn_amd/csrc/launch.h"
+# Sources each workload's timed kernels are built from: files, and the
+# launch-argument structs of launch.h they compile against.
+CSRC = "kv_cache_decode_attn_amd/csrc/"
+KERNEL_SOURCES = {
+    "decode": (CSRC + "decode.hip", CSRC + "common.h", "DecodeLaunch"),
+    "prefill": (CSRC + "prefill_mfma.hip", CSRC + "common.h", "PrefillLaunch"),
+}
+WORKLOAD_KERNELS = {"decode8b": "decode", "padded32": "decode", "longctx70b": "decode", "prefill8k": "prefill"}
 
 
-def _decode_struct(text):
-    """The DecodeLaunch declaration of launch.h: the only part of that
-    header the decode kernels compile against."""
-    i = text.index("struct DecodeLaunch {")
+def _launch_struct(text, name):
+    i = text.index("struct %s {" % name)
     return text[i:text.index("};", i) + 2]
 
 
-def decode_source_sha(read=None):
-    """Hash of the sources the decode kernels are built from."""
+def source_sha(kind, read=None):
+    """Hash of the sources the `kind` kernels ("decode", "prefill") are built from."""
     if read is None:
         def read(rel):
             with open(os.path.join(ROOT, rel), "rb") as f:
                 return f.read()
     h = hashlib.sha256()
-    for rel in DECODE_SOURCES:
-        h.update(read(rel))
-    h.update(_decode_struct(read(LAUNCH_HEADER).decode()).encode())
+    for item in KERNEL_SOURCES[kind]:
+        if item.endswith((".hip", ".h")):
+            h.update(read(item))
+        else:
+            h.update(_launch_struct(read(CSRC + "launch.h").decode(), item).encode())
     return h.hexdigest()
 
 
-def decode_traffic():
-    """HBM bytes per attn_decode call measured with rocprofv3 counters
-    (profiles/decode_traffic.json), or None when that measurement was taken
-    on different decode kernel sources."""
+def traffic(workload):
+    """HBM bytes per launch of the workload's dominant call measured with
+    rocprofv3 FETCH_SIZE / WRITE_SIZE counters and scaled by the copy-kernel
+    calibration (profiles/traffic.json), or None when that measurement was
+    taken on different kernel sources."""
     try:
-        with open(os.path.join(ROOT, "profiles", "decode_traffic.json")) as f:
-            d = json.load(f)
-    except (OSError, ValueError):
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            d = json.load(f)["workloads"][workload]
+    except (OSError, ValueError, KeyError):
         return None
-    if d.get("source_sha256") != decode_source_sha():
+    if d.get("source_sha256") != source_sha(WORKLOAD_KERNELS[workload]):
         return None
-    return d.get("bytes_per_call")
+    return d.get("bytes_per_launch")
 
 
 def _events(n):
@@ -101,6 +110,63 @@ def _stats(ms):
     a = np.asarray(ms, dtype=np.float64)
     return {"median_ms": float(np.median(a)), "min_ms": float(a.min()), "p90_ms": float(np.percentile(a, 90)),
             "mean_ms": float(a.mean())}
+
+
+def _bits(t):
+    """Raw storage words of a device tensor on the host (uint16 for bf16)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def cpu_workers():
+    """Host processes the oracle runs on: the cores this process may use,
+    at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def run_oracle(arrays, fn, units, min_seconds=3.0, prep=None):
+    """Times the oracle work units `units` (oracle.pool function `fn`) on a
+    pool of cpu_workers() host processes that map `arrays` from shared
+    memory; the whole set is repeated until min_seconds of wall time have
+    run.  `prep` = (fn, units) runs once first, untimed (input preparation).
+    Returns (workers, repetitions, seconds, results of the last pass)."""
+    from oracle.pool import OraclePool, SharedInputs
+
+    workers = cpu_workers()
+    with SharedInputs(arrays) as shm, OraclePool(workers, shm.specs) as pool:
+        if prep is not None:
+            pool.run(*prep)
+        reps, total = 0, 0.0
+        while True:
+            dt, res = pool.run(fn, units)
+            reps += 1
+            total += dt
+            if total >= min_seconds:
+                break
+    return workers, reps, total, res
+
+
+def cpu_record(value, unit, workers, what, reps, seconds):
+    return {"value": value, "unit": unit, "cores": workers, "kind": "oracle",
+            "sample": "%s; x%d repetitions in %.1f s; fp64 numpy oracle over a pool of %d host processes "
+                      "(one BLAS thread each) on %s" % (what, reps, seconds, workers, cpu_model())}
 
 
 # ------------------------------------------------------------------ decode ---
@@ -187,41 +253,25 @@ class PagedDecode:
                 "head_dim": self.D, "kv_dtype": "bf16", "block_tokens": 16, "keys_total": int(self.ctx.sum()),
                 "cached_len": "U[1,8192] + 1 appended", "part_tokens": self.part, "cache_replicas": len(self.caches)}
 
-    def cpu_baseline(self, max_seqs=None, min_seconds=10.0):
-        """The oracle on the same bytes, single thread: bf16 -> fp64 decode of
-        the cache plus the attention, timed; returns (result dict, max abs err)."""
-        from threadpoolctl import threadpool_limits
-
-        from oracle import attention as OA
-        from oracle import cache as OC
-
-        seqs = list(range(self.B if max_seqs is None else min(max_seqs, self.B)))
-        kh = [self.src_k[b, :, :self.ctx[b]].cpu().view(torch.int16).numpy().view(np.uint16) for b in seqs]
-        vh = [self.src_v[b, :, :self.ctx[b]].cpu().view(torch.int16).numpy().view(np.uint16) for b in seqs]
-        qh = self.q[seqs].cpu().view(torch.int16).numpy().view(np.uint16)
-        # the whole decode (bf16 decode of the cache + attention) repeated
-        # until about min_seconds of single-thread CPU time has run
-        reps = 0
-        with threadpool_limits(limits=1):
-            t0 = time.perf_counter()
-            while True:
-                keys = [OC.to_f64(x, OC.BF16) for x in kh]
-                vals = [OC.to_f64(x, OC.BF16) for x in vh]
-                want = OA.decode(OC.to_f64(qh, OC.BF16), keys, vals, self.ctx[seqs], 1.0 / math.sqrt(self.D))
-                reps += 1
-                dt = time.perf_counter() - t0
-                if dt >= min_seconds:
-                    break
-        # the GPU output of the last timed step covers the same sequences
-        got = self.out[seqs].cpu().numpy()
-        err = float(np.abs(got - want).max())
-        nbytes = 2 * self.Hkv * self.D * 2 * int(self.ctx[seqs].sum())
-        res = {"value": reps * nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "%d of %d sequences (%d keys, %.0f MB of K/V) x %d repetitions, fp64 numpy, 1 thread, "
-                         "%.1f s; %s" % (len(seqs), self.B, int(self.ctx[seqs].sum()), nbytes / 1e6, reps, dt,
-                                         platform.processor() or platform.machine()),
-               "seqs_per_s": reps * len(seqs) / dt}
-        return res, err
+    def cpu_baseline(self, min_seconds=5.0):
+        """The oracle on the same bytes: per (sequence, KV head), the bf16 ->
+        fp64 decode of the cache and the attention of the group's G query
+        heads; all 32 sequences.  Returns (record, max abs err of the GPU
+        output of the last timed step vs the oracle)."""
+        G = self.Hq // self.Hkv
+        arrays = {"k": _bits(self.src_k), "v": _bits(self.src_v), "q": _bits(self.q)}
+        units = [("", b, g, G, int(self.ctx[b]), 1.0 / math.sqrt(self.D), K.BF16, None)
+                 for b in range(self.B) for g in range(self.Hkv)]
+        workers, reps, dt, res = run_oracle(arrays, "decode_unit", units, min_seconds)
+        want = np.zeros((self.B, self.Hq, self.D))
+        for (_, b, g, G_, _, _, _, _), o in res:
+            want[b, g * G:(g + 1) * G] = o
+        err = float(np.abs(self.out.cpu().numpy() - want).max())
+        gbs = reps * self.kv_bytes() / dt / 1e9
+        rec = cpu_record(gbs, "GB/s", workers, "the whole step: 32 sequences x 8 KV heads, %d keys, %.0f MB of K/V"
+                         % (int(self.ctx.sum()), self.kv_bytes() / 1e6), reps, dt)
+        rec["seqs_per_s"] = reps * self.B / dt
+        return rec, err
 
 
 class PaddedDecode:
@@ -262,6 +312,34 @@ class PaddedDecode:
             K.attn_decode_append(self.caches[layer], self.q[layer], self.k_new[layer], self.v_new[layer],
                                  self.seq_lens, self.cap, key_mask=self.mask, out=self.out[layer], workspace=self.ws,
                                  part_tokens=self.part)
+
+    def layer_bytes(self):
+        return self.step_bytes() // self.L
+
+    def cpu_baseline(self, layers=(0, 8, 16, 24), min_seconds=3.0, wid=3):
+        """The oracle on a stated subset of layers (every sequence and head of
+        each): the layer's K/V regenerated from their seeds (the bytes the
+        cache was filled with), then per (sequence, KV head) the bf16 -> fp64
+        decode and the masked attention over the 4096 cache positions.
+        Returns (record, max abs err of the GPU outputs of those layers)."""
+        arrays = {"mask": self.mask.cpu().numpy()}
+        for l in layers:
+            arrays["L%d_k" % l] = _bits(synth.normal_device(self.caches[l].k.shape, (wid, synth.T_K, l)))
+            arrays["L%d_v" % l] = _bits(synth.normal_device(self.caches[l].v.shape, (wid, synth.T_V, l)))
+            arrays["L%d_q" % l] = _bits(self.q[l])
+        units = [("L%d_" % l, b, g, 1, self.cap, 1.0 / math.sqrt(self.D), K.BF16, "mask")
+                 for l in layers for b in range(self.B) for g in range(self.H)]
+        workers, reps, dt, res = run_oracle(arrays, "decode_unit", units, min_seconds)
+        got = self.out.cpu().numpy()
+        err = 0.0
+        for (prefix, b, g, _, _, _, _, _), o in res:
+            l = int(prefix[1:-1])
+            err = max(err, float(np.abs(got[l, b, g] - o[0]).max()))
+        gbs = reps * len(layers) * self.layer_bytes() / dt / 1e9
+        rec = cpu_record(gbs, "GB/s", workers, "layers %s of 32 (every sequence and head; key mask over 4096 "
+                         "positions)" % (list(layers),), reps, dt)
+        rec["ms_per_step_extrapolated_to_32_layers"] = self.step_bytes() / (gbs * 1e9) * 1e3
+        return rec, err
 
     def config(self):
         return {"workload": self.name, "layers": self.L, "batch": self.B, "q_heads": self.H, "kv_heads": self.H,
@@ -315,6 +393,41 @@ class LongContextFp8Decode:
                                  self.seq_lens, self.ctx, block_table=self.tables[layer], out=self.out[layer],
                                  workspace=self.ws, part_tokens=self.part)
 
+    def cpu_baseline(self, layers=(0, 40), min_seconds=1.0, wid=5):
+        """The oracle on a stated subset of layers: the layer's bf16 K/V
+        regenerated from their seeds, quantised by the oracle's own E4M3FN
+        encoder with the layer's scales (input preparation, untimed), then per
+        KV head the fp8 -> fp64 decode of 131,073 keys and the attention of
+        its 8 query heads.  Returns (record, max abs err of the GPU outputs of
+        those layers vs that quantised oracle)."""
+        Hkv, ctx, D = self.Hkv, self.ctx, self.D
+        arrays, prep = {}, []
+        scales = self.scales.cpu().numpy()
+        for l in layers:
+            arrays["L%d_srck" % l] = _bits(synth.normal_device((1, Hkv, ctx, D), (wid, synth.T_K, l)))[0]
+            arrays["L%d_srcv" % l] = _bits(synth.normal_device((1, Hkv, ctx, D), (wid, synth.T_V, l)))[0]
+            arrays["L%d_k" % l] = np.zeros((Hkv, ctx, D), np.uint8)
+            arrays["L%d_v" % l] = np.zeros((Hkv, ctx, D), np.uint8)
+            arrays["L%d_ks" % l] = scales[l, 0].copy()
+            arrays["L%d_vs" % l] = scales[l, 1].copy()
+            arrays["L%d_q" % l] = _bits(self.q[l])
+            for g in range(Hkv):
+                prep.append(("L%d_srck" % l, "L%d_k" % l, g, float(scales[l, 0, g])))
+                prep.append(("L%d_srcv" % l, "L%d_v" % l, g, float(scales[l, 1, g])))
+        G = self.Hq // Hkv
+        units = [("L%d_" % l, 0, g, G, ctx, 1.0 / math.sqrt(D), K.FP8_E4M3, None) for l in layers for g in range(Hkv)]
+        workers, reps, dt, res = run_oracle(arrays, "decode_unit", units, min_seconds, prep=("quantize_unit", prep))
+        got = self.out.cpu().numpy()
+        err = 0.0
+        for (prefix, _, g, _, _, _, _, _), o in res:
+            l = int(prefix[1:-1])
+            err = max(err, float(np.abs(got[l, 0, g * G:(g + 1) * G] - o).max()))
+        gbs = reps * len(layers) * (self.step_bytes() // self.L) / dt / 1e9
+        rec = cpu_record(gbs, "GB/s", workers, "layers %s of 80 (8 KV heads x 131,073 fp8 keys each)"
+                         % (list(layers),), reps, dt)
+        rec["ms_per_step_extrapolated_to_80_layers"] = self.step_bytes() / (gbs * 1e9) * 1e3
+        return rec, err
+
     def config(self):
         return {"workload": self.name, "layers": self.L, "batch": 1, "q_heads": self.Hq, "kv_heads": self.Hkv,
                 "head_dim": self.D, "kv_dtype": "fp8_e4m3", "keys": self.ctx, "part_tokens": self.part}
@@ -345,6 +458,28 @@ class CausalPrefill:
     def step(self, i, ev=None):
         K.attn_prefill(self.q, self.k, self.v, cache=self.cache, positions=self.positions, block_table=self.table,
                        out=self.out)
+
+    def cpu_baseline(self, rows=16, starts=(0, 1024, 2048, 3072, 4096, 5120, 6144, 7168, 8176), min_seconds=2.0):
+        """The oracle on a stated sample of query rows: for every query head,
+        `rows` consecutive rows at each start position, computed as
+        oracle.attention.prefill of those rows with the keys before them as
+        the attended prefix (the rows of the one-shot causal prefill); FLOPs
+        4 d (t + 1) per row t.  Returns (record, max abs err of the GPU
+        output rows vs the oracle)."""
+        arrays = {"q": _bits(self.q)[0], "k": _bits(self.k)[0], "v": _bits(self.v)[0]}
+        G = self.Hq // self.Hkv
+        units = [(h, h // G, t0, rows, 1.0 / math.sqrt(self.D)) for h in range(self.Hq) for t0 in starts]
+        workers, reps, dt, res = run_oracle(arrays, "prefill_rows_unit", units, min_seconds)
+        got = self.out.cpu().numpy()
+        err = 0.0
+        for (h, _, t0, n, _), o in res:
+            err = max(err, float(np.abs(got[0, h, t0:t0 + n] - o).max()))
+        flops = sum(4 * self.D * (t + 1) for t0 in starts for t in range(t0, t0 + rows)) * self.Hq
+        tf = reps * flops / dt / 1e12
+        rec = cpu_record(tf, "TFLOP/s", workers, "%d rows at each of positions %s for all %d query heads (%.2f GFLOP)"
+                         % (rows, list(starts), self.Hq, flops / 1e9), reps, dt)
+        rec["ms_per_step_extrapolated"] = self.flops() / (tf * 1e12) * 1e3
+        return rec, err
 
     def config(self):
         return {"workload": self.name, "batch": 1, "q_heads": self.Hq, "kv_heads": self.Hkv, "seq": self.N,
@@ -525,6 +660,91 @@ class BeamReorder:
                 "head_dim": self.D, "kv_dtype": "bf16", "lengths": "U[1024,4096]", "beams_per_prompt": 4}
 
 
+class TinySequence:
+    """The tiny workload: 1 layer, batch 1, 4 query / 4 KV heads, head_dim
+    64, fp32, contiguous cache of 256 positions.  A causal prefill of 16
+    tokens fills the cache (attn_prefill with the cache write), positions
+    16..127 are appended, and the decode step stores token 128 and attends
+    the 129 keys (attn_decode_append).  Launch-bound: reported as latency
+    per call."""
+
+    name = "tiny-fp32-prefill16-decode129"
+
+    def __init__(self, wid=1):
+        self.H, self.D, self.cap, self.n_pre, self.cached = 4, 64, 256, 16, 128
+        n = self.cached + 1
+        self.q = synth.normal((1, self.H, n, self.D), (wid, synth.T_Q), torch.float32).to(DEV)
+        self.k = synth.normal((1, self.H, n, self.D), (wid, synth.T_K), torch.float32).to(DEV)
+        self.v = synth.normal((1, self.H, n, self.D), (wid, synth.T_V), torch.float32).to(DEV)
+        self.cache = K.KVCache.contiguous(1, self.H, self.cap, self.D, K.F32, DEV)
+        self.zero = torch.zeros(1, dtype=torch.int32, device=DEV)
+        self.qp = self.q[:, :, :self.n_pre].contiguous()
+        self.kp = self.k[:, :, :self.n_pre].contiguous()
+        self.vp = self.v[:, :, :self.n_pre].contiguous()
+        self.out_pre = torch.empty((1, self.H, self.n_pre, self.D), dtype=torch.float32, device=DEV)
+        # the prefill once, then positions 16..127
+        K.attn_prefill(self.qp, self.kp, self.vp, cache=self.cache, positions=self.zero, out=self.out_pre)
+        K.kv_append(self.cache, self.k[:, :, self.n_pre:self.cached].contiguous(),
+                    self.v[:, :, self.n_pre:self.cached].contiguous(),
+                    torch.full((1,), self.n_pre, dtype=torch.int32, device=DEV))
+        self.qd = self.q[:, :, self.cached].contiguous()
+        self.kd = self.k[:, :, self.cached].contiguous()
+        self.vd = self.v[:, :, self.cached].contiguous()
+        self.seq_lens = torch.full((1,), self.cached + 1, dtype=torch.int32, device=DEV)
+        self.out = torch.empty((1, self.H, self.D), dtype=torch.float32, device=DEV)
+        self.ws = K.decode_workspace(self.cache, 1, self.H, self.cap)
+        self.phase = "decode"
+        torch.cuda.synchronize()
+
+    def step(self, i, ev=None):
+        if self.phase == "prefill":  # re-writes positions 0..15 with the same rows
+            K.attn_prefill(self.qp, self.kp, self.vp, cache=self.cache, positions=self.zero, out=self.out_pre)
+        else:  # re-writes position 128 with the same row
+            K.attn_decode_append(self.cache, self.qd, self.kd, self.vd, self.seq_lens, self.cap, out=self.out,
+                                 workspace=self.ws)
+
+    def parity(self):
+        """Max abs error of the decode output and of the prefill output vs the
+        oracle (fp64 on the same fp32 inputs)."""
+        from oracle import attention as OA
+
+        q, k, v = (t.cpu().numpy().astype(np.float64) for t in (self.q, self.k, self.v))
+        scale = 1.0 / math.sqrt(self.D)
+        dec = OA.decode(q[:, :, self.cached], [k[0]], [v[0]], [self.cached + 1], scale)
+        pre = OA.prefill(q[:, :, :self.n_pre], k[:, :, :self.n_pre], v[:, :, :self.n_pre], [0], [self.n_pre], scale)
+        return (float(np.abs(self.out.cpu().numpy() - dec).max()),
+                float(np.abs(self.out_pre.cpu().numpy() - pre).max()))
+
+    def config(self):
+        return {"workload": self.name, "layers": 1, "batch": 1, "q_heads": self.H, "kv_heads": self.H,
+                "head_dim": self.D, "dtype": "f32", "capacity": self.cap, "prefill_tokens": self.n_pre,
+                "decode_keys": self.cached + 1}
+
+
+class StreamRead:
+    """Context for the HBM rooflines: a plain streaming read (torch.sum over
+    4 GiB of fp32) and a plain copy (2 GiB to 2 GiB, torch copy_) on this
+    GPU.  Not a workload of the library; the bars stay relative to 8 TB/s."""
+
+    name = "plain-stream-read-and-copy"
+
+    def __init__(self):
+        self.x = torch.ones(1 << 30, dtype=torch.float32, device=DEV)
+        self.a = torch.ones(1 << 29, dtype=torch.float32, device=DEV)
+        self.b = torch.empty_like(self.a)
+        self.phase = "read"
+        torch.cuda.synchronize()
+
+    def step(self, i, ev=None):
+        if self.phase == "read":
+            torch.sum(self.x)
+        else:
+            self.b.copy_(self.a)
+
+    def bytes(self):
+        return self.x.numel() * 4 if self.phase == "read" else 2 * self.a.numel() * 4
+
+
 def time_steps(w, steps, warmup, per_launch=False):
     for i in range(warmup):
         w.step(i)
@@ -550,11 +770,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads",
-                    default="decode8b,padded32,longctx70b,verify8b,prefill8k,chunkprefill,cowcopy,beamreorder",
-                    help="comma list: decode8b (headline), padded32, longctx70b, verify8b, prefill8k, chunkprefill, "
-                         "cowcopy, beamreorder")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the headline workload the oracle runs")
+                    default="tiny,padded32,longctx70b,verify8b,prefill8k,chunkprefill,cowcopy,beamreorder,stream",
+                    help="comma list of workloads timed besides the headline (decode8b, always run): tiny, padded32, "
+                         "longctx70b, verify8b, prefill8k, chunkprefill, cowcopy, beamreorder, stream")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip every oracle timing and parity sample")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: the library is a single-GPU kernel library and this build runs on a "
@@ -562,6 +781,7 @@ def main(argv=None):
         return 2
     torch.cuda.set_device(0)
     names = [x for x in args.workloads.split(",") if x]
+    cpu = not args.no_cpu_baseline
 
     w = PagedDecode()
     # the same step as two calls (kv_append, attn_decode), for reference
@@ -569,17 +789,17 @@ def main(argv=None):
     ms2, _ = time_steps(w, args.steps, args.warmup)
     _, launch2 = time_steps(w, args.steps, args.warmup, per_launch=True)
     w.fused = True
-    # `value`: K steps with nothing else in the timed region; then a second
-    # pass with HIP events around every call for the call's own duration
-    # (the event records themselves add a few microseconds per step)
+    # `value`: K steps with nothing else in the timed region (HIP events on
+    # the launch stream around the whole region); then a second pass with HIP
+    # events around every call, reported for information (the event records
+    # themselves add a few microseconds per call)
     ms, _ = time_steps(w, args.steps, args.warmup)
     _, launch = time_steps(w, args.steps, args.warmup, per_launch=True)
     step_bytes = w.step_bytes()
-    call_ms = launch["attn_decode_append"]["mean_ms"]
-    achieved = step_bytes / (call_ms * 1e-3) / 1e9
+    achieved = step_bytes / (ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
-        "value": step_bytes / (ms * 1e-3) / 1e9,
+        "value": achieved,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -591,32 +811,56 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 K/V/Q, seeded lengths and block permutation)",
         "config": w.config(),
-        "frac_of_hbm_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "frac_of_hbm_peak": achieved / HBM_PEAK_GBS,
         "seqs_per_s": w.B / (ms * 1e-3),
         "step_bytes": step_bytes,
         "per_launch": launch,
         "two_call_step": {"ms_per_step": ms2, "GB/s": step_bytes / (ms2 * 1e-3) / 1e9, "per_launch": launch2,
                           "attn_decode_GB/s": w.decode_bytes() / (launch2["attn_decode"]["mean_ms"] * 1e-3) / 1e9},
+        # the dominant launch pair is the whole timed step (one attn_decode_append call:
+        # the partition pass, then the merge); achieved = algorithmic bytes / mean step time
         "roofline": {"bound": "hbm",
                      "kernel": "attn_decode_append (decode_partition_bf16_mfma with the fused append, "
                                "then decode_merge)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "bytes_per_launch": step_bytes, "traffic": decode_traffic()},
+                     "bytes_per_launch": step_bytes, "traffic": traffic("decode8b")},
     }
-    if not args.no_cpu_baseline:
-        base, err = w.cpu_baseline(args.cpu_seqs)
+    if cpu:
+        base, err = w.cpu_baseline()
         line["cpu_baseline"] = base
         line["parity_max_abs_err_vs_oracle"] = err
     del w
     torch.cuda.empty_cache()
 
     extra = {}
+    if "tiny" in names:
+        t = TinySequence()
+        rec = {"config": t.config()}
+        for phase, reps in (("prefill", 200), ("decode", 200)):
+            t.phase = phase
+            msx, _ = time_steps(t, reps, 20)
+            rec["%s_us_per_call" % phase] = msx * 1e3
+        rec["sequence_us"] = rec["prefill_us_per_call"] + rec["decode_us_per_call"]
+        rec["note"] = "launch-bound: latency only (the 112 positions appended in between are set-up, not timed)"
+        if cpu:
+            rec["parity_max_abs_err_vs_oracle"], rec["prefill_parity_max_abs_err_vs_oracle"] = t.parity()
+        extra["tiny"] = rec
+        del t
+        torch.cuda.empty_cache()
     if "padded32" in names:
         p = PaddedDecode()
         ms3, _ = time_steps(p, max(5, args.steps // 2), args.warmup)
         gbs = p.step_bytes() / (ms3 * 1e-3) / 1e9
-        extra["padded32"] = {"config": p.config(), "ms_per_step": ms3, "GB/s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
-                             "seqs_per_s": p.B / (ms3 * 1e-3), "step_bytes": p.step_bytes()}
+        extra["padded32"] = {"config": p.config(), "ms_per_step": ms3, "GB/s": gbs,
+                             "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "seqs_per_s": p.B / (ms3 * 1e-3),
+                             "step_bytes": p.step_bytes(),
+                             "roofline": {"bound": "hbm", "kernel": "attn_decode_append per layer (decode_partition "
+                                          "vector pass with the key mask and fused append, then decode_merge)",
+                                          "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": p.layer_bytes(),
+                                          "traffic": traffic("padded32")}}
+        if cpu:
+            extra["padded32"]["cpu_baseline"], extra["padded32"]["parity_max_abs_err_vs_oracle"] = p.cpu_baseline()
         del p
         torch.cuda.empty_cache()
     if "longctx70b" in names:
@@ -625,7 +869,16 @@ def main(argv=None):
         gbs = lw.step_bytes() / (ms5 * 1e-3) / 1e9
         extra["longctx70b"] = {"config": lw.config(), "ms_per_step": ms5, "GB/s": gbs,
                                "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "seqs_per_s": 1 / (ms5 * 1e-3),
-                               "step_bytes": lw.step_bytes()}
+                               "step_bytes": lw.step_bytes(),
+                               "roofline": {"bound": "hbm", "kernel": "attn_decode_append per layer "
+                                            "(decode_partition_fp8_mfma with the fused append, then decode_merge)",
+                                            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                            "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": lw.step_bytes() // lw.L,
+                                            "traffic": traffic("longctx70b")}}
+        if cpu:
+            rec, err = lw.cpu_baseline()
+            extra["longctx70b"]["cpu_baseline"] = rec
+            extra["longctx70b"]["parity_max_abs_err_vs_quantised_oracle"] = err
         del lw
         torch.cuda.empty_cache()
     if "verify8b" in names:
@@ -648,7 +901,9 @@ def main(argv=None):
                               "roofline": {"bound": "mfma",
                                            "kernel": "attn_prefill (prefill_mfma_kernel, which also writes the cache)",
                                            "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                           "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
+                                           "frac": tf / BF16_PEAK_TFLOPS, "traffic": traffic("prefill8k")}}
+        if cpu:
+            extra["prefill8k"]["cpu_baseline"], extra["prefill8k"]["parity_max_abs_err_vs_oracle"] = pf.cpu_baseline()
         del pf
         torch.cuda.empty_cache()
     if "chunkprefill" in names:
@@ -673,6 +928,17 @@ def main(argv=None):
                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
         del cw
+        torch.cuda.empty_cache()
+    if "stream" in names:
+        sr = StreamRead()
+        rec = {}
+        for phase in ("read", "copy"):
+            sr.phase = phase
+            msx, _ = time_steps(sr, 10, 3)
+            rec["%s_GB/s" % phase] = sr.bytes() / (msx * 1e-3) / 1e9
+        rec["kernels"] = "read: torch.sum over 4 GiB fp32; copy: torch copy_ of 2 GiB fp32 (4 GiB moved)"
+        line["hbm_context"] = rec
+        del sr
         torch.cuda.empty_cache()
     if extra:
         line["workloads"] = extra

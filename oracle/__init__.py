@@ -26,10 +26,12 @@ Modules:
   paging     - block-table batch/beam reorder, block copies, a reference
                block pool (free list, reference counts, copy-on-write) and
                the contiguous vs paged reserved-memory closed forms
+  pool       - runs the functions above over host processes (shared-memory
+               inputs) to time the oracle on many cores; no arithmetic
 
 Every function is pinned by tests/test_oracle_pins.py and
 tests/test_oracle_paging.py against values the
 pages print, closed forms, library routines or brute force.  Parity pinned
 everywhere; no function here is "parity unpinned".
 """
-from . import codec, attention, cache, paging  # noqa: F401
+from . import codec, attention, cache, paging  # noqa: F401  (pool is imported on demand)
