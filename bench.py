@@ -745,6 +745,21 @@ class StreamRead:
         return self.x.numel() * 4 if self.phase == "read" else 2 * self.a.numel() * 4
 
 
+def warm_clocks(w, seconds=0.5):
+    """Runs the workload's step untimed for about `seconds` of wall time: the
+    GPU's clocks ramp for a while after idle host work (the oracle timing,
+    input set-up), and a few warm-up steps of a 1-5 ms step do not cover it."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        w.step(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_steps(w, steps, warmup, per_launch=False):
     for i in range(warmup):
         w.step(i)
@@ -764,26 +779,146 @@ def time_steps(w, steps, warmup, per_launch=False):
     return total_ms / steps, launch
 
 
+LEGS = ("tiny", "padded32", "longctx70b", "verify8b", "prefill8k", "chunkprefill", "cowcopy", "beamreorder", "stream")
+
+
+def run_leg(name, args, cpu):
+    """Times one workload besides the headline; returns its record."""
+    if name == "tiny":
+        t = TinySequence()
+        rec = {"config": t.config()}
+        for phase, reps in (("prefill", 200), ("decode", 200)):
+            t.phase = phase
+            warm_clocks(t, 0.1)
+            msx, _ = time_steps(t, reps, 20)
+            rec["%s_us_per_call" % phase] = msx * 1e3
+        rec["sequence_us"] = rec["prefill_us_per_call"] + rec["decode_us_per_call"]
+        rec["note"] = "launch-bound: latency only (the 112 positions appended in between are set-up, not timed)"
+        if cpu:
+            rec["parity_max_abs_err_vs_oracle"], rec["prefill_parity_max_abs_err_vs_oracle"] = t.parity()
+        return rec
+    if name == "padded32":
+        p = PaddedDecode()
+        warm_clocks(p)
+        ms3, _ = time_steps(p, max(5, args.steps // 2), args.warmup)
+        gbs = p.step_bytes() / (ms3 * 1e-3) / 1e9
+        rec = {"config": p.config(), "ms_per_step": ms3, "GB/s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+               "seqs_per_s": p.B / (ms3 * 1e-3), "step_bytes": p.step_bytes(),
+               "roofline": {"bound": "hbm", "kernel": "attn_decode_append per layer (decode_partition vector pass "
+                            "with the key mask and fused append, then decode_merge)",
+                            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                            "bytes_per_launch": p.layer_bytes(), "traffic": traffic("padded32")}}
+        if cpu:
+            rec["cpu_baseline"], rec["parity_max_abs_err_vs_oracle"] = p.cpu_baseline()
+        return rec
+    if name == "longctx70b":
+        lw = LongContextFp8Decode()
+        warm_clocks(lw)
+        ms5, _ = time_steps(lw, max(5, args.steps // 2), args.warmup)
+        gbs = lw.step_bytes() / (ms5 * 1e-3) / 1e9
+        rec = {"config": lw.config(), "ms_per_step": ms5, "GB/s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+               "seqs_per_s": 1 / (ms5 * 1e-3), "step_bytes": lw.step_bytes(),
+               "roofline": {"bound": "hbm", "kernel": "attn_decode_append per layer (decode_partition_fp8_mfma "
+                            "with the fused append, then decode_merge)",
+                            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                            "bytes_per_launch": lw.step_bytes() // lw.L, "traffic": traffic("longctx70b")}}
+        if cpu:
+            rec["cpu_baseline"], rec["parity_max_abs_err_vs_quantised_oracle"] = lw.cpu_baseline()
+        return rec
+    if name == "verify8b":
+        vw = PagedVerify()
+        warm_clocks(vw)
+        msv, _ = time_steps(vw, max(10, args.steps), args.warmup)
+        gbs = vw.step_bytes() / (msv * 1e-3) / 1e9
+        return {"config": vw.config(), "ms_per_step": msv, "GB/s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+                "seqs_per_s": vw.B / (msv * 1e-3), "step_bytes": vw.step_bytes()}
+    if name == "prefill8k":
+        pf = CausalPrefill()
+        # the first calls run below the steady-state rate (clocks ramp under sustained
+        # matrix-core load): a second of untimed calls first, then at least 20 timed
+        warm_clocks(pf, 1.0)
+        msp, _ = time_steps(pf, max(20, args.steps), args.warmup)
+        tf = pf.flops() / (msp * 1e-3) / 1e12
+        rec = {"config": pf.config(), "ms_per_step": msp, "TFLOP/s": tf, "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS,
+               "flops": pf.flops(),
+               "roofline": {"bound": "mfma", "kernel": "attn_prefill (prefill_mfma_kernel, which also writes the cache)",
+                            "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                            "traffic": traffic("prefill8k")}}
+        if cpu:
+            rec["cpu_baseline"], rec["parity_max_abs_err_vs_oracle"] = pf.cpu_baseline()
+        return rec
+    if name == "chunkprefill":
+        cp = ChunkedPrefill()
+        warm_clocks(cp, 1.0)
+        msc, _ = time_steps(cp, max(20, args.steps), args.warmup)
+        tf = cp.flops() / (msc * 1e-3) / 1e12
+        return {"config": cp.config(), "ms_per_step": msc, "TFLOP/s": tf, "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS,
+                "flops": cp.flops(),
+                "roofline": {"bound": "mfma", "kernel": "attn_prefill (prefill_mfma_kernel, cached prefix gathered "
+                             "through the block table)", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
+    if name in ("cowcopy", "beamreorder"):
+        cw = CowBlockCopy() if name == "cowcopy" else BeamReorder()
+        warm_clocks(cw)
+        msc, _ = time_steps(cw, max(10, args.steps), args.warmup)
+        gbs = cw.step_bytes() / (msc * 1e-3) / 1e9
+        return {"config": cw.config(), "ms_per_launch": msc, "GB/s": gbs, "bytes_per_launch": cw.step_bytes(),
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+    if name == "stream":
+        sr = StreamRead()
+        rec = {}
+        for phase in ("read", "copy"):
+            sr.phase = phase
+            msx, _ = time_steps(sr, 10, 3)
+            rec["%s_GB/s" % phase] = sr.bytes() / (msx * 1e-3) / 1e9
+        rec["kernels"] = "read: torch.sum over 4 GiB fp32; copy: torch copy_ of 2 GiB fp32 (4 GiB moved)"
+        return rec
+    raise ValueError("unknown workload %r" % name)
+
+
+def leg_in_child(name, args):
+    """Runs one leg in a fresh process (`bench.py --leg NAME`): each workload
+    then starts from an empty device allocator, as a serving process that
+    sizes its cache at start-up does, instead of inheriting the address
+    space the previous legs fragmented (that history alone moved the fp8
+    long-context step by 5%)."""
+    import subprocess
+
+    cmd = [sys.executable, os.path.abspath(__file__), "--leg", name, "--steps", str(args.steps),
+           "--warmup", str(args.warmup)] + (["--no-cpu-baseline"] if args.no_cpu_baseline else [])
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    lines = [x for x in r.stdout.splitlines() if x.startswith("{")]
+    if r.returncode != 0 or not lines:
+        sys.stderr.write(r.stderr[-4000:])
+        return {"error": "leg %s exited with status %d" % (name, r.returncode)}
+    return json.loads(lines[-1])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads",
-                    default="tiny,padded32,longctx70b,verify8b,prefill8k,chunkprefill,cowcopy,beamreorder,stream",
-                    help="comma list of workloads timed besides the headline (decode8b, always run): tiny, padded32, "
-                         "longctx70b, verify8b, prefill8k, chunkprefill, cowcopy, beamreorder, stream")
+    ap.add_argument("--workloads", default=",".join(LEGS),
+                    help="comma list of workloads timed besides the headline (decode8b, always run), each in a "
+                         "process of its own: " + ", ".join(LEGS))
+    ap.add_argument("--leg", default=None, help="run only this workload, in this process, and print its record")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip every oracle timing and parity sample")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: the library is a single-GPU kernel library and this build runs on a "
               "one-GPU box (how the path would shard is described in the design notes).", file=sys.stderr)
         return 2
-    torch.cuda.set_device(0)
-    names = [x for x in args.workloads.split(",") if x]
     cpu = not args.no_cpu_baseline
-
+    if args.leg:
+        torch.cuda.set_device(0)
+        print(json.dumps(run_leg(args.leg, args, cpu)))
+        return 0
+    names = [x for x in args.workloads.split(",") if x]
+    torch.cuda.set_device(0)
     w = PagedDecode()
+    warm_clocks(w)
     # the same step as two calls (kv_append, attn_decode), for reference
     w.fused = False
     ms2, _ = time_steps(w, args.steps, args.warmup)
@@ -832,114 +967,9 @@ def main(argv=None):
     del w
     torch.cuda.empty_cache()
 
-    extra = {}
-    if "tiny" in names:
-        t = TinySequence()
-        rec = {"config": t.config()}
-        for phase, reps in (("prefill", 200), ("decode", 200)):
-            t.phase = phase
-            msx, _ = time_steps(t, reps, 20)
-            rec["%s_us_per_call" % phase] = msx * 1e3
-        rec["sequence_us"] = rec["prefill_us_per_call"] + rec["decode_us_per_call"]
-        rec["note"] = "launch-bound: latency only (the 112 positions appended in between are set-up, not timed)"
-        if cpu:
-            rec["parity_max_abs_err_vs_oracle"], rec["prefill_parity_max_abs_err_vs_oracle"] = t.parity()
-        extra["tiny"] = rec
-        del t
-        torch.cuda.empty_cache()
-    if "padded32" in names:
-        p = PaddedDecode()
-        ms3, _ = time_steps(p, max(5, args.steps // 2), args.warmup)
-        gbs = p.step_bytes() / (ms3 * 1e-3) / 1e9
-        extra["padded32"] = {"config": p.config(), "ms_per_step": ms3, "GB/s": gbs,
-                             "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "seqs_per_s": p.B / (ms3 * 1e-3),
-                             "step_bytes": p.step_bytes(),
-                             "roofline": {"bound": "hbm", "kernel": "attn_decode_append per layer (decode_partition "
-                                          "vector pass with the key mask and fused append, then decode_merge)",
-                                          "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                          "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": p.layer_bytes(),
-                                          "traffic": traffic("padded32")}}
-        if cpu:
-            extra["padded32"]["cpu_baseline"], extra["padded32"]["parity_max_abs_err_vs_oracle"] = p.cpu_baseline()
-        del p
-        torch.cuda.empty_cache()
-    if "longctx70b" in names:
-        lw = LongContextFp8Decode()
-        ms5, _ = time_steps(lw, max(5, args.steps // 2), args.warmup)
-        gbs = lw.step_bytes() / (ms5 * 1e-3) / 1e9
-        extra["longctx70b"] = {"config": lw.config(), "ms_per_step": ms5, "GB/s": gbs,
-                               "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "seqs_per_s": 1 / (ms5 * 1e-3),
-                               "step_bytes": lw.step_bytes(),
-                               "roofline": {"bound": "hbm", "kernel": "attn_decode_append per layer "
-                                            "(decode_partition_fp8_mfma with the fused append, then decode_merge)",
-                                            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                            "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": lw.step_bytes() // lw.L,
-                                            "traffic": traffic("longctx70b")}}
-        if cpu:
-            rec, err = lw.cpu_baseline()
-            extra["longctx70b"]["cpu_baseline"] = rec
-            extra["longctx70b"]["parity_max_abs_err_vs_quantised_oracle"] = err
-        del lw
-        torch.cuda.empty_cache()
-    if "verify8b" in names:
-        vw = PagedVerify()
-        msv, _ = time_steps(vw, max(10, args.steps), args.warmup)
-        gbs = vw.step_bytes() / (msv * 1e-3) / 1e9
-        extra["verify8b"] = {"config": vw.config(), "ms_per_step": msv, "GB/s": gbs,
-                             "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "seqs_per_s": vw.B / (msv * 1e-3),
-                             "step_bytes": vw.step_bytes()}
-        del vw
-        torch.cuda.empty_cache()
-    if "prefill8k" in names:
-        pf = CausalPrefill()
-        # the first few dozen calls run below the steady-state rate (clocks ramp under sustained
-        # matrix-core load): 50 untimed calls (~30 ms) first, then at least 20 timed
-        msp, _ = time_steps(pf, max(20, args.steps), max(50, args.warmup))
-        tf = pf.flops() / (msp * 1e-3) / 1e12
-        extra["prefill8k"] = {"config": pf.config(), "ms_per_step": msp, "TFLOP/s": tf,
-                              "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS, "flops": pf.flops(),
-                              "roofline": {"bound": "mfma",
-                                           "kernel": "attn_prefill (prefill_mfma_kernel, which also writes the cache)",
-                                           "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                           "frac": tf / BF16_PEAK_TFLOPS, "traffic": traffic("prefill8k")}}
-        if cpu:
-            extra["prefill8k"]["cpu_baseline"], extra["prefill8k"]["parity_max_abs_err_vs_oracle"] = pf.cpu_baseline()
-        del pf
-        torch.cuda.empty_cache()
-    if "chunkprefill" in names:
-        cp = ChunkedPrefill()
-        msc, _ = time_steps(cp, max(20, args.steps), max(50, args.warmup))
-        tf = cp.flops() / (msc * 1e-3) / 1e12
-        extra["chunkprefill"] = {"config": cp.config(), "ms_per_step": msc, "TFLOP/s": tf,
-                                 "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS, "flops": cp.flops(),
-                                 "roofline": {"bound": "mfma", "kernel": "attn_prefill (prefill_mfma_kernel, "
-                                              "cached prefix gathered through the block table)",
-                                              "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                              "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
-        del cp
-        torch.cuda.empty_cache()
-    for key, cls_ in (("cowcopy", CowBlockCopy), ("beamreorder", BeamReorder)):
-        if key not in names:
-            continue
-        cw = cls_()
-        msc, _ = time_steps(cw, max(10, args.steps), args.warmup)
-        gbs = cw.step_bytes() / (msc * 1e-3) / 1e9
-        extra[key] = {"config": cw.config(), "ms_per_launch": msc, "GB/s": gbs, "bytes_per_launch": cw.step_bytes(),
-                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
-        del cw
-        torch.cuda.empty_cache()
+    extra = {name: leg_in_child(name, args) for name in names if name != "stream"}
     if "stream" in names:
-        sr = StreamRead()
-        rec = {}
-        for phase in ("read", "copy"):
-            sr.phase = phase
-            msx, _ = time_steps(sr, 10, 3)
-            rec["%s_GB/s" % phase] = sr.bytes() / (msx * 1e-3) / 1e9
-        rec["kernels"] = "read: torch.sum over 4 GiB fp32; copy: torch copy_ of 2 GiB fp32 (4 GiB moved)"
-        line["hbm_context"] = rec
-        del sr
-        torch.cuda.empty_cache()
+        line["hbm_context"] = leg_in_child("stream", args)
     if extra:
         line["workloads"] = extra
     print(json.dumps(line))

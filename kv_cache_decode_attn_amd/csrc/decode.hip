@@ -142,10 +142,10 @@ constexpr int kWaves = 4;
 #define KVATTN_RING_VEC 2
 #endif
 #ifndef KVATTN_RING_BF16
-#define KVATTN_RING_BF16 2
+#define KVATTN_RING_BF16 3
 #endif
 #ifndef KVATTN_RING_FP8
-#define KVATTN_RING_FP8 2
+#define KVATTN_RING_FP8 3
 #endif
 constexpr int kRingVec = KVATTN_RING_VEC;
 constexpr int kRingBf16 = KVATTN_RING_BF16;
