@@ -203,8 +203,9 @@ int32_t kvattn_decode_default_part_tokens(int32_t cache_dtype, int32_t batch, in
  *  workspace   device, >= kvattn_decode_workspace_bytes(...) bytes, 16-byte
  *              aligned; contents on entry are ignored
  *  part_tokens keys per partition: 0 = default, else a multiple of 64 in
- *              [64, 8192]; with a bf16/f32 cache (and fp8 with G < 4) also
- *              part_tokens * G <= 8192
+ *              [64, 8192]; also part_tokens * G <= 8192 for the passes
+ *              that keep every key's scores in LDS (f32 caches, bf16 with
+ *              G < 16, fp8 with G < 4)
  * Bitwise deterministic for fixed arguments (fixed partitioning, no atomics).
  */
 int kvattn_attn_decode(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads,
@@ -313,7 +314,7 @@ int kvattn_attn_decode_append_noalloc(const kvattn_cache* cache, int32_t batch, 
  *               num_q_heads * n_q, num_kv_heads, head_dim, max_seq_len,
  *               part_tokens) bytes (the query columns count as heads)
  *  every other argument as in kvattn_attn_decode (part_tokens * G * n_q
- *  <= 8192 with a bf16 cache).
+ *  <= 8192 with a bf16 cache and G * n_q < 16).
  */
 int kvattn_attn_decode_multi(const kvattn_cache* cache, int32_t batch, int32_t num_q_heads, int32_t n_q,
                              const void* q, int32_t q_dtype,

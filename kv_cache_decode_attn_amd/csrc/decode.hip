@@ -313,6 +313,22 @@ __device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* dst) 
 #endif
 }
 
+// The same transfer issued as inline assembly: the compiler then does not
+// count it among the loads in flight, so it does not wait for it before every
+// LDS read or before the use of any older load; completion is awaited
+// explicitly.
+__device__ __forceinline__ void copy16_to_lds_async(const uint8_t* src, uint8_t* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)dst;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, off nt"
+      :
+      : "s"(m0), "v"(src)
+      : "memory", "m0");
+#endif
+}
+
 // Four OCP E4M3FN codes -> two words of two bf16 each (codes 0, 1 and codes
 // 2, 3), exactly: every E4M3FN value is a bf16 value, and gfx950 converts a
 // pair of codes to a bf16 pair in one instruction (scale 1).
@@ -831,6 +847,329 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
 }
 
 // ---------------------------------------------------------------------------
+// bf16 cache, many query columns per KV head (several queries per sequence):
+// the bf16 matrix-core pass in one sweep over the blocks, with the running
+// softmax of the fp8 pass instead of a per-partition score buffer.  With 16
+// columns per KV head the three-phase pass above keeps 16 scores per key in
+// LDS, which caps its partitions at 512 keys and its occupancy at three
+// workgroups per compute unit; here the LDS holds only the K slots and the
+// final cross-wave combine, so partitions can be long and the split-K
+// partials few.
+//   per 16-token block: S^T = K Q^T on MFMA (K staged through the wave's LDS
+//   slot exactly as in decode_partition_bf16_mfma), mask, block max and the
+//   lazily raised running max (as in decode_partition_fp8_mfma), weights
+//   exp2(z - m) split into bf16 hi + lo, then O^T += V^T P^T with V^T built
+//   by 16-bit v_perm_b32 transposes of the lane's own V loads.
+// Each wave keeps its own (max, sum, O) over its blocks; the four waves are
+// combined through LDS.
+// s_waitcnt vmcnt(n) for a count known only at run time (0 <= n <= 31).
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  switch (n) {
+#define KVATTN_WAIT_CASE(k) \
+  case k: __builtin_amdgcn_s_waitcnt(wait_vm(k)); break;
+    KVATTN_WAIT_CASE(1) KVATTN_WAIT_CASE(2) KVATTN_WAIT_CASE(3) KVATTN_WAIT_CASE(4) KVATTN_WAIT_CASE(5)
+    KVATTN_WAIT_CASE(6) KVATTN_WAIT_CASE(7) KVATTN_WAIT_CASE(8) KVATTN_WAIT_CASE(9) KVATTN_WAIT_CASE(10)
+    KVATTN_WAIT_CASE(11) KVATTN_WAIT_CASE(12) KVATTN_WAIT_CASE(13) KVATTN_WAIT_CASE(14) KVATTN_WAIT_CASE(15)
+    KVATTN_WAIT_CASE(16) KVATTN_WAIT_CASE(17) KVATTN_WAIT_CASE(18) KVATTN_WAIT_CASE(19) KVATTN_WAIT_CASE(20)
+    KVATTN_WAIT_CASE(21) KVATTN_WAIT_CASE(22) KVATTN_WAIT_CASE(23) KVATTN_WAIT_CASE(24) KVATTN_WAIT_CASE(25)
+    KVATTN_WAIT_CASE(26) KVATTN_WAIT_CASE(27) KVATTN_WAIT_CASE(28) KVATTN_WAIT_CASE(29) KVATTN_WAIT_CASE(30)
+    KVATTN_WAIT_CASE(31)
+#undef KVATTN_WAIT_CASE
+    default: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
+  }
+}
+
+// LDS of decode_partition_bf16_online: block offsets, (max, sum) per wave and
+// head, the key mask flags (MASK), then one area that holds the waves' K
+// slots (two per wave) during the sweep and the cross-wave reduction
+// [kWaves][G][D] afterwards.
+__host__ __device__ constexpr int bf16_online_area_offset(int T, int G, bool mask) {
+  return kslot_offset(decode_off_floats(T) + kWaves * G * 2 + (mask ? T / 4 : 0));
+}
+__host__ __device__ constexpr int bf16_online_lds_bytes(int T, int G, int D, bool mask) {
+  // two K slots per wave of one 16-token block of bf16 rows (2 D bytes each)
+  return bf16_online_area_offset(T, G, mask) + (kWaves * G * D * 4 > kWaves * 2 * kBlockTokens * 2 * D
+                                                    ? kWaves * G * D * 4
+                                                    : kWaves * 2 * kBlockTokens * 2 * D);
+}
+
+template <int D, int G, bool MASK, bool TAIL>
+__global__ void __launch_bounds__(256) decode_partition_bf16_online(const DecodeLaunch p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  constexpr int ROWB = 2 * D;       // bytes per token row
+  constexpr int KC = ROWB / 64;     // 16-byte K chunks per lane and block
+  constexpr int HALVES = D / 64;    // 64-wide d halves of the V^T tiles
+  constexpr int NT = 4 * HALVES;    // output tiles of 16 d rows
+  constexpr float kRescale = 8.f;
+  static_assert(G >= 4 && G <= 16 && KC >= 1, "shape");
+
+  extern __shared__ float lds[];
+  const int g = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int r16 = lane & 15, lg = lane >> 4;
+  const int T = p.part_tokens;
+  const int ctx = min(max(p.seq_lens[b], 0), p.ctx_limit);
+  const int hq0 = g * G;
+  const int t0 = part * T;
+  if (t0 >= ctx) {
+    if (part == 0)
+      for (int i = tid; i < G * D; i += 256) p.out[((int64_t)b * p.num_q_heads + hq0) * D + i] = 0.f;
+    return;
+  }
+  const int t1 = min(t0 + T, ctx);
+  const int n = t1 - t0;
+  const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
+  const int j0 = t0 / kBlockTokens;
+
+  int64_t* offs = reinterpret_cast<int64_t*>(lds);
+  float* wstat = lds + decode_off_floats(T);                            // [kWaves][G][2]
+  uint8_t* mflag = reinterpret_cast<uint8_t*>(wstat + kWaves * G * 2);  // [T] mask (MASK only)
+  // the K slots during the sweep, then the cross-wave reduction [kWaves][G][D]
+  uint8_t* area = reinterpret_cast<uint8_t*>(lds) + bf16_online_area_offset(T, G, MASK);
+  float* red = reinterpret_cast<float*>(area);
+  for (int i = tid; i < nblk; i += 256) offs[i] = block_offset(p.c, b, g, j0 + i);
+  if constexpr (MASK) {
+    const uint8_t* mask_row = p.key_mask + (int64_t)b * p.key_mask_stride + t0;
+    for (int t = tid; t < n; t += 256) mflag[t] = mask_row[t];
+  }
+  // fused append (as in decode_partition)
+  if (p.k_new != nullptr && p.seq_lens[b] == ctx) {
+    for (int i = 0; i < p.n_tail; ++i) {
+      const int tn = ctx - p.n_tail + i;
+      if (tn >= t0 && tn < t1) store_new_row<KVATTN_BF16, D>(p, b, g, tn, i);
+    }
+  }
+
+  // q of head r16 in the k order of the K chunks: k-step s = 2c + u uses
+  // d 32c + 8*lg + 4u + 0..3 (zero for heads >= G)
+  uint32_t qb[2 * KC][2];
+  {
+    const int hr = r16 < G ? r16 : 0;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)b * p.num_q_heads + hq0 + hr) * D;
+#pragma unroll
+    for (int sd = 0; sd < 2 * KC; ++sd) {
+      const uint2 w = *reinterpret_cast<const uint2*>(qrow + 32 * (sd / 2) + 8 * lg + 4 * (sd % 2));
+      qb[sd][0] = r16 < G ? w.x : 0u;
+      qb[sd][1] = r16 < G ? w.y : 0u;
+    }
+  }
+  const float zscale = p.scale * kLog2e;
+  __syncthreads();  // also publishes the fused append's stores to every wave
+
+  auto key_ok = [&](int t) -> bool {
+    if (t >= n) return false;
+    if constexpr (MASK) return mflag[t] != 0;
+    return true;
+  };
+  auto load_off = [&](int jb) -> int64_t {
+    const int64_t o = offs[jb];
+    return uniform64(o >= 0 ? o : 0);
+  };
+  // K through the wave's LDS slot (see KStage), V into registers: 8 bytes
+  // (d 64*hf + 4*r16 ..+3) of each of keys 4*lg + i
+  using KST = KStage<ROWB>;
+  uint8_t* kslots = area + wave * 2 * KST::BYTES;  // this wave's two K slots
+  int ksrc[KST::XFERS], kat[KC];
+#pragma unroll
+  for (int x = 0; x < KST::XFERS; ++x) ksrc[x] = KST::src(x, lane);
+#pragma unroll
+  for (int c = 0; c < KC; ++c) kat[c] = KST::at(r16, 4 * c + lg);
+  // block jb goes to slot (jb / kWaves) % 2
+  auto issue_k = [&](int jb) {
+    const uint8_t* blk = p.c.k + load_off(jb);
+    uint8_t* slot = kslots + ((jb / kWaves) & 1) * KST::BYTES;
+#pragma unroll
+    for (int x = 0; x < KST::XFERS; ++x) copy16_to_lds_async(blk + ksrc[x], slot + x * 1024);
+  };
+  const uint8_t* vbase = p.c.v + (4 * lg) * ROWB + 8 * r16;
+  auto load_v = [&](int jb, uint2 (*vr)[4]) {
+    const int64_t off = load_off(jb);
+#pragma unroll
+    for (int hf = 0; hf < HALVES; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vr[hf][i] = __builtin_bit_cast(
+            uint2, __builtin_nontemporal_load(reinterpret_cast<const v2u*>(vbase + off + i * ROWB + 128 * hf)));
+  };
+
+  v4f o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lsum = 0.f;
+
+  auto process = [&](int jb, const U4* kr, const uint2 (*vr)[4]) {
+    if (uniform64(offs[jb]) < 0) return;  // block outside the cache: fully masked
+    // ---- scores S^T (keys 4*lg + r, head r16), two accumulation chains ----
+    v4f sacc = v4f{0.f, 0.f, 0.f, 0.f}, sacc2 = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const v4s a0 = __builtin_bit_cast(v4s, v2u{kr[c].x, kr[c].y});
+      const v4s a1 = __builtin_bit_cast(v4s, v2u{kr[c].z, kr[c].w});
+      const v4s b0 = __builtin_bit_cast(v4s, v2u{qb[2 * c][0], qb[2 * c][1]});
+      const v4s b1 = __builtin_bit_cast(v4s, v2u{qb[2 * c + 1][0], qb[2 * c + 1][1]});
+      sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, b0, sacc, 0, 0, 0);
+      sacc2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, b1, sacc2, 0, 0, 0);
+    }
+    sacc += sacc2;
+    // ---- mask, block max, lazily raised running max ----
+    const int tk = kBlockTokens * jb + 4 * lg;
+    // several queries per sequence (TAIL): column r16 is query r16 % n_tail,
+    // which sees keys below ctx - (n_tail - 1 - r16 % n_tail)
+    const int ncol = TAIL ? ctx - (p.n_tail - 1 - r16 % p.n_tail) - t0 : n;
+    float z[4];
+    bool live[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      live[r] = key_ok(tk + r);
+      z[r] = (live[r] && tk + r < ncol) ? sacc[r] * zscale : -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    {
+      auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      bm = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      bm = fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+    }
+    const bool need = bm > mrun + kRescale;
+    if (__any(need)) {
+      const float mnew = need ? bm : mrun;
+      const float alpha = need ? exp2f(mrun - mnew) : 1.f;  // 0 when mrun = -inf
+#pragma unroll
+      for (int t = 0; t < NT; ++t) o[t] *= alpha;
+      lsum *= alpha;
+      mrun = mnew;
+    }
+    const float msub = (mrun == -INFINITY) ? 0.f : mrun;
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pw[r] = __builtin_amdgcn_exp2f(z[r] - msub);
+      lsum += pw[r];
+    }
+    // weights as bf16 hi + lo (B operand: keys 4*lg + i)
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 h01, h23, l01, l23;
+    h01[0] = (__bf16)pw[0];
+    h01[1] = (__bf16)pw[1];
+    h23[0] = (__bf16)pw[2];
+    h23[1] = (__bf16)pw[3];
+    l01[0] = (__bf16)(pw[0] - (float)h01[0]);
+    l01[1] = (__bf16)(pw[1] - (float)h01[1]);
+    l23[0] = (__bf16)(pw[2] - (float)h23[0]);
+    l23[1] = (__bf16)(pw[3] - (float)h23[1]);
+    const v4s phi = __builtin_bit_cast(v4s, v2u{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
+    const v4s plo = __builtin_bit_cast(v4s, v2u{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+    // ---- O^T += V^T P^T: 4 keys x 4 d (16-bit) transposed per half ----
+#pragma unroll
+    for (int hf = 0; hf < HALVES; ++hf) {
+      uint2 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = live[i] ? vr[hf][i] : uint2{0u, 0u};  // dead keys never reach O
+      const uint32_t x01l = __builtin_amdgcn_perm(a[1].x, a[0].x, 0x05040100u);
+      const uint32_t x23l = __builtin_amdgcn_perm(a[3].x, a[2].x, 0x05040100u);
+      const uint32_t x01h = __builtin_amdgcn_perm(a[1].x, a[0].x, 0x07060302u);
+      const uint32_t x23h = __builtin_amdgcn_perm(a[3].x, a[2].x, 0x07060302u);
+      const uint32_t y01l = __builtin_amdgcn_perm(a[1].y, a[0].y, 0x05040100u);
+      const uint32_t y23l = __builtin_amdgcn_perm(a[3].y, a[2].y, 0x05040100u);
+      const uint32_t y01h = __builtin_amdgcn_perm(a[1].y, a[0].y, 0x07060302u);
+      const uint32_t y23h = __builtin_amdgcn_perm(a[3].y, a[2].y, 0x07060302u);
+      const v4s av[4] = {__builtin_bit_cast(v4s, v2u{x01l, x23l}), __builtin_bit_cast(v4s, v2u{x01h, x23h}),
+                         __builtin_bit_cast(v4s, v2u{y01l, y23l}), __builtin_bit_cast(v4s, v2u{y01h, y23h})};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], phi, o[4 * hf + j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[4 * hf + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], plo, o[4 * hf + j], 0, 0, 0);
+    }
+  };
+
+  // The wave's blocks jb = wave + kWaves i stream through the V register ring
+  // (stream_ring); K goes through the wave's two slots two blocks ahead, with
+  // transfers the compiler does not count (the waits below are the only ones
+  // on them).  Issue order: V of the first kRingBf16 - 1 blocks, K of the
+  // first two; then each step issues V of the block kRingBf16 - 1 places
+  // ahead and, inside the body, once the slot is read out, K of the block two
+  // places ahead into it.  So when block i's K transfer must have landed, the
+  // loads issued after it are: V of block i + 1 (issued a step earlier, when
+  // kRingBf16 = 3), K of block i + 1 and V of block i + kRingBf16 - 1 -
+  // whichever exist - and the load-count wait releases exactly the transfer.
+  static_assert(kRingBf16 == 3, "wait accounting below");
+  constexpr int VL = 4 * HALVES;     // V loads per block
+  constexpr int KL = KST::XFERS;     // K transfers per block
+  uint2 vring[kRingBf16][HALVES][4];
+  auto body = [&](int jb, const uint2 (*vr)[4]) {
+    const bool b1 = jb + kWaves < nblk, b2 = jb + 2 * kWaves < nblk;
+    // after K of block jb: V of jb + 1 and K of jb + 1 (if jb + 1 exists; V of
+    // jb + 1 was issued before K of jb only for the first block), V of jb + 2
+    const bool first = jb < kWaves;
+    const int after = (b1 ? (first ? 0 : VL) + KL : 0) + (b2 ? VL : 0);
+    wait_vm_dyn(after);
+    const uint8_t* slot = kslots + ((jb / kWaves) & 1) * KST::BYTES;
+    U4 kr[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const U4*>(slot + kat[c]);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot is read out before its next transfer
+    if (b2) issue_k(jb + 2 * kWaves);
+    process(jb, kr, vr);
+  };
+  ring_fill(wave, nblk, vring, load_v);
+  if (wave < nblk) issue_k(wave);
+  if (wave + kWaves < nblk) issue_k(wave + kWaves);
+  stream_ring(wave, nblk, vring, load_v, body);
+  __syncthreads();  // every wave is done with its K slots: the area becomes the reduction
+
+  // ---- combine the waves (as in decode_partition_fp8_mfma) ----
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (lg == 0 && r16 < G) {
+    wstat[(wave * G + r16) * 2] = mrun;
+    wstat[(wave * G + r16) * 2 + 1] = lsum;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  if (r16 < G)
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wstat[(w * G + r16) * 2]);
+  const float mine = (mrun == -INFINITY || M == -INFINITY) ? 0.f : exp2f(mrun - M);
+  if (r16 < G) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int hf = t / 4, j = t % 4;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) red[(wave * G + r16) * D + 64 * hf + 4 * (4 * lg + rr) + j] = o[t][rr] * mine;
+    }
+  }
+  __syncthreads();
+  const int nparts_b = (ctx + T - 1) / T;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx - h * D;
+    float Mh = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) Mh = fmaxf(Mh, wstat[(w * G + h) * 2]);
+    float acc = 0.f, L = 0.f;
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = wstat[(w * G + h) * 2];
+      const float sw = (mw == -INFINITY) ? 0.f : exp2f(mw - Mh);
+      L = fmaf(sw, wstat[(w * G + h) * 2 + 1], L);
+      acc += red[(w * G + h) * D + d];
+    }
+    const int hq = hq0 + h;
+    if (nparts_b == 1) {
+      p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = (L > 0.f) ? acc / L : 0.f;
+    } else {
+      const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.num_parts + part;
+      p.ws_o[slot * D + d] = acc;
+      if (d == 0) {
+        p.ws_ml[slot * 2] = Mh;
+        p.ws_ml[slot * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp8 cache with G >= 4 query heads per KV head: the partition pass on MFMA.
 //
 // With 8 heads per KV head an fp8 byte costs 8 multiply-adds on each of K and
@@ -1242,6 +1581,9 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
     const size_t lds = (size_t)(decode_off_floats(a.part_tokens) + kWaves * G * D + kWaves * G * 2 +
                                 (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
     hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
+  } else if constexpr (KVT == KVATTN_BF16 && G >= KVATTN_BF16_ONLINE_MIN_G) {
+    const size_t lds = (size_t)bf16_online_lds_bytes(a.part_tokens, G, D, MASK);
+    hipLaunchKernelGGL((decode_partition_bf16_online<D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
   } else if constexpr (KVT == KVATTN_BF16 && G >= 4) {
     const size_t lds = (size_t)kslot_offset(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) +
                        (size_t)kWaves * KStage<2 * D>::BYTES;

@@ -154,8 +154,10 @@ int32_t default_part_tokens(int32_t dtype, int32_t batch, int32_t hq, int32_t hk
     const int64_t t = ((max_seq_len + per - 1) / per + 63) / 64 * 64;
     return (int32_t)(t < 256 ? 256 : t > kMaxPartTokens ? kMaxPartTokens : t);
   }
-  int32_t t = group >= 4 ? 512 : 256;
-  while (t * group > kMaxPartScores) t /= 2;
+  // the single-sweep bf16 pass keeps no scores in LDS: longer partitions, fewer partials
+  int32_t t = kvattn::decode_single_pass(dtype, group) ? 1024 : group >= 4 ? 512 : 256;
+  if (!kvattn::decode_single_pass(dtype, group))
+    while (t * group > kMaxPartScores) t /= 2;
   while (t > 64 && wgs(t) < 2048) t /= 2;
   return t;
 }
@@ -203,8 +205,8 @@ int attn_decode_impl(const char* who, const kvattn_cache* cache, int32_t batch, 
   const int32_t group = num_q_heads / cache->num_kv_heads;
   int32_t t = part_tokens;
   if (t == 0) t = default_part_tokens(cache->dtype, batch, num_q_heads, cache->num_kv_heads, max_seq_len);
-  // the fp8 matrix-core pass (group >= 4) keeps no per-key scores in LDS
-  const bool scores_in_lds = !fp8_mfma_pass(cache->dtype, group);
+  // the single-sweep passes keep no per-key scores in LDS
+  const bool scores_in_lds = !kvattn::decode_single_pass(cache->dtype, group);
   if (t < 64 || t > kMaxPartTokens || t % 64 != 0 || (scores_in_lds && t * group > kMaxPartScores))
     return fail(KVATTN_EINVAL, "%s: part_tokens %d: need a multiple of 64 in [64, %d] with part_tokens*group <= %d",
                 who, t, kMaxPartTokens, kMaxPartScores);

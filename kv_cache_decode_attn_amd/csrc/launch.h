@@ -55,6 +55,17 @@ struct DecodeLaunch {
   int32_t n_tail;
 };
 int launch_decode(const DecodeLaunch& a, hipStream_t stream);
+// Whether the decode partition pass for this cache type and group (query
+// columns per KV head) keeps a running softmax per wave (no per-key scores
+// in LDS, so no cap on part_tokens * group): the fp8 matrix-core pass
+// (group >= 4) and the single-sweep bf16 matrix-core pass (16 columns).
+#ifndef KVATTN_BF16_ONLINE_MIN_G
+#define KVATTN_BF16_ONLINE_MIN_G 16
+#endif
+inline bool decode_single_pass(int32_t cache_dtype, int32_t group) {
+  return (cache_dtype == KVATTN_FP8_E4M3 && group >= 4) ||
+         (cache_dtype == KVATTN_BF16 && group >= KVATTN_BF16_ONLINE_MIN_G);
+}
 // Dynamic LDS bytes of the decode partition kernel.
 int decode_lds_bytes(int part_tokens, int group, int head_dim);
 

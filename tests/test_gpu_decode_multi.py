@@ -22,7 +22,7 @@ _TORCH = {K.F32: torch.float32, K.BF16: torch.bfloat16, K.FP8_E4M3: torch.bfloat
 _OC = {K.F32: OC.F32, K.BF16: OC.BF16, K.FP8_E4M3: OC.FP8_E4M3}
 
 
-def _case(lens, n_q, Hq, Hkv, d, dtype, layout, seed, mask=None):
+def _case(lens, n_q, Hq, Hkv, d, dtype, layout, seed, mask=None, parts=(64,)):
     """Cache holding every sequence's lens[b] positions, the last n_q of them
     the new tokens (appended like any other); q [B, Hq, n_q, d].  Returns the
     GPU output and the oracle's."""
@@ -50,7 +50,9 @@ def _case(lens, n_q, Hq, Hkv, d, dtype, layout, seed, mask=None):
     K.kv_append(cache, kx.to(DEV), vx.to(DEV), zeros, block_table=tdev, n_valid=torch.from_numpy(lens).to(DEV))
     seq = torch.from_numpy(lens).to(DEV)
     kmask = torch.from_numpy(mask).to(DEV) if mask is not None else None
-    got = K.attn_decode_multi(cache, q.to(DEV), seq, total, block_table=tdev, key_mask=kmask, part_tokens=64)
+    got = [K.attn_decode_multi(cache, q.to(DEV), seq, total, block_table=tdev, key_mask=kmask,
+                               part_tokens=pt).cpu().numpy() for pt in parts]
+    got = got[0] if len(got) == 1 else got
     got_default = K.attn_decode_multi(cache, q.to(DEV), seq, total, block_table=tdev, key_mask=kmask)
     # oracle: the keys are the cached values as the cache holds them (fp8:
     # the oracle's own encoding, dequantised)
@@ -81,7 +83,7 @@ def _case(lens, n_q, Hq, Hkv, d, dtype, layout, seed, mask=None):
     want = np.zeros_like(want_o)
     for b in range(B):
         want[b, :, n_q - nq[b]:] = want_o[b, :, :nq[b]]
-    return got.cpu().numpy(), got_default.cpu().numpy(), want
+    return got, got_default.cpu().numpy(), want
 
 
 @pytest.mark.parametrize("dtype,G,n_q", [
@@ -111,6 +113,23 @@ def test_decode_multi_key_mask(d):
     got, got_d, want = _case(lens, 4, 16, 4, d, K.BF16, K.PAGED, 82, mask=mask)
     assert max_abs(got, want) <= TOL
     assert max_abs(got_d, want) <= TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask_on", [False, True])
+def test_decode_multi_16_columns_long_partitions(d, mask_on):
+    """The 16-column bf16 pass keeps no per-key scores, so any partition size
+    is allowed: 64 (many partials), 1024 (the default), 3072 and 8192 (one
+    partition per sequence, with lengths past and below it)."""
+    lens = [5000, 1025, 3072, 31, 4097]
+    mask = None
+    if mask_on:
+        mask = synth.random_mask((5, 5008), 0.8, (85, synth.T_MASK))
+        mask[:, 0] = 1
+    got, got_d, want = _case(lens, 4, 16, 4, d, K.BF16, K.PAGED, 84, mask=mask, parts=(64, 1024, 3072, 8192))
+    for g in got + [got_d]:
+        assert np.isfinite(g).all()
+        assert max_abs(g, want) <= TOL
 
 
 def test_decode_multi_one_query_is_decode_bitwise():
