@@ -346,13 +346,13 @@ int kvattn_attn_decode_multi(const kvattn_cache* cache, int32_t batch, int32_t n
  *  cache       NULL: no cache access (positions may then be NULL = all 0;
  *              attend_prefix must be 0).  Else the layer's cache: the new
  *              K/V are stored at positions P .. P + q_lens[b] - 1 (as
- *              kvattn_kv_append would) by the end of the call.  With bf16
- *              inputs into a bf16 cache the matrix-core kernel stores them
- *              itself, each workgroup the rows of its own query tile after
- *              its output; otherwise (an fp8 cache, f32) an append kernel
- *              runs before the attention kernel.  The attention never reads
- *              these rows from the cache (keys s >= P come from k / v), so
- *              the order does not change the result.
+ *              kvattn_kv_append would) by the end of the call.  With the
+ *              same element type in and out the attention kernel stores them
+ *              itself after its output (bf16: each matrix-core workgroup the
+ *              rows of its own query tile); into an fp8 cache an append
+ *              kernel quantises them before the attention kernel runs.  The
+ *              attention never reads these rows from the cache (keys s >= P
+ *              come from k / v), so the order does not change the result.
  *  num_kv_heads, head_dim: shapes of q/k/v (must equal the cache's if given)
  *  q           device [batch, num_q_heads, n_max, head_dim] of dtype
  *  k, v        device [batch, num_kv_heads, n_max, head_dim] of dtype

@@ -134,6 +134,7 @@ int64_t compute_units() {
 constexpr int32_t kMaxPartScores = 8192;  // part_tokens * group, bounds the LDS
 
 // Default keys per partition, per partition kernel (measured on MI355X):
+//  - up to 512 keys: one partition (no merge launch);
 //  - fp8 cache with G >= 4 (matrix-core pass): long partitions amortise the
 //    per-workgroup combine and shrink the merge, and the pass runs best at
 //    one workgroup per compute unit (a unit given two workgroups finishes
@@ -147,6 +148,10 @@ bool fp8_mfma_pass(int32_t dtype, int32_t group) { return dtype == KVATTN_FP8_E4
 int32_t default_part_tokens(int32_t dtype, int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len) {
   const int32_t group = hq / hkv;
   auto wgs = [&](int32_t t) { return (int64_t)batch * hkv * (((int64_t)max_seq_len + t - 1) / t); };
+  // Up to 512 keys: one partition per sequence.  The whole decode is then a
+  // single launch (no merge pass), which is what a latency-bound short
+  // context wants; 512 keys x 16 columns still fit the per-key score buffer.
+  if (max_seq_len <= 512) return max_seq_len <= 64 ? 64 : (max_seq_len + 63) / 64 * 64;
   if (fp8_mfma_pass(dtype, group)) {
     const int64_t heads = (int64_t)batch * hkv;
     const int64_t units = compute_units();
@@ -507,10 +512,11 @@ int kvattn_attn_prefill(const kvattn_cache* cache, int32_t batch, int32_t num_q_
   a.scale = scale;
   a.out = out;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The bf16 MFMA kernel writes a bf16 cache itself: each of its workgroups
-  // stores the rows of the query tile it owns.  Otherwise the append kernel
-  // runs first.
-  a.write_cache = cache && cache->dtype == dtype && kvattn::prefill_mfma_supports(a);
+  // With the same element type in and out, the attention kernel writes the
+  // cache itself (the bf16 MFMA kernel: each workgroup the rows of the query
+  // tile it owns; the general kernel: each query row's wave of the group's
+  // first head).  An fp8 cache (quantised rows) gets the append kernel first.
+  a.write_cache = cache && cache->dtype == dtype;
   if (cache && !a.write_cache) {
     kvattn::AppendLaunch w{};
     w.c = a.c;

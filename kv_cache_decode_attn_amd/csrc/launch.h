@@ -88,8 +88,8 @@ struct PrefillLaunch {
   int32_t causal, attend_prefix;
   float scale;
   float* out;
-  // The MFMA kernel stores the new K/V rows into the cache itself (same
-  // dtype in and out); otherwise the caller launches the append.
+  // The attention kernel stores the new K/V rows into the cache itself
+  // (same dtype in and out); otherwise the caller launches the append.
   int32_t write_cache;
 };
 int launch_prefill(const PrefillLaunch& a, hipStream_t stream);

@@ -150,6 +150,25 @@ __global__ void __launch_bounds__(64) prefill_generic(const PrefillLaunch a) {
   const float inv = (l > 0.f) ? 1.f / l : 0.f;
   orow[lane] = o0 * inv;
   if (D > 64) orow[lane + 64] = o1 * inv;
+
+  // Cache write (same element type in and out: the bits are copied): the
+  // wave of the group's first query head stores new row t of its KV head at
+  // position P + t, as kv_append would; skipped outside the cache.  The
+  // attention above never reads these positions from the cache.
+  if (a.write_cache && h % G == 0) {
+    const int64_t off = position_offset(a.c, b, g, (int64_t)P + t);
+    if (off >= 0) {
+      constexpr int W = D * ES / 4;  // 32-bit words per row
+      const uint32_t* ks = reinterpret_cast<const uint32_t*>(src.newk + (int64_t)t * D * ES);
+      const uint32_t* vs = reinterpret_cast<const uint32_t*>(src.newv + (int64_t)t * D * ES);
+      uint32_t* kd = reinterpret_cast<uint32_t*>(a.c.k + off);
+      uint32_t* vd = reinterpret_cast<uint32_t*>(a.c.v + off);
+      for (int w = lane; w < W; w += 64) {
+        kd[w] = ks[w];
+        vd[w] = vs[w];
+      }
+    }
+  }
 }
 
 template <int DT, int CDT, int D>
