@@ -64,7 +64,8 @@ KERNEL_SOURCES = {
     "decode": (CSRC + "decode.hip", CSRC + "common.h", "DecodeLaunch"),
     "prefill": (CSRC + "prefill_mfma.hip", CSRC + "common.h", "PrefillLaunch"),
 }
-WORKLOAD_KERNELS = {"decode8b": "decode", "padded32": "decode", "longctx70b": "decode", "prefill8k": "prefill"}
+WORKLOAD_KERNELS = {"decode8b": "decode", "padded32": "decode", "longctx70b": "decode", "verify8b": "decode",
+                    "prefill8k": "prefill"}
 
 
 def _launch_struct(text, name):
@@ -831,7 +832,11 @@ def run_leg(name, args, cpu):
         msv, _ = time_steps(vw, max(10, args.steps), args.warmup)
         gbs = vw.step_bytes() / (msv * 1e-3) / 1e9
         return {"config": vw.config(), "ms_per_step": msv, "GB/s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
-                "seqs_per_s": vw.B / (msv * 1e-3), "step_bytes": vw.step_bytes()}
+                "seqs_per_s": vw.B / (msv * 1e-3), "step_bytes": vw.step_bytes(),
+                "roofline": {"bound": "hbm", "kernel": "attn_decode_append with 4 queries per sequence "
+                             "(decode_partition_bf16_online with the fused append, then decode_merge)",
+                             "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                             "bytes_per_launch": vw.step_bytes(), "traffic": traffic("verify8b")}}
     if name == "prefill8k":
         pf = CausalPrefill()
         # the first calls run below the steady-state rate (clocks ramp under sustained
