@@ -488,20 +488,29 @@ class CausalPrefill:
 
 
 class ChunkedPrefill:
-    """Chunked prefill against a paged bf16 cache: a 2,048-token chunk of a
+    """Chunked prefill against a paged cache: a 2,048-token chunk of a
     Llama-3-8B-shaped layer (32/8 heads, d 128) at positions 6,144..8,191 that
     attends the 6,144 cached positions and, causally, itself, and stores its
-    rows in the cache (attn_prefill with attend_prefix)."""
+    rows in the cache (attn_prefill with attend_prefix).  The cache is bf16,
+    or fp8 E4M3FN with per-head scales of about max|x| / 448 (the chunk's
+    rows are then quantised into the cache before the attention)."""
 
     name = "chunked-prefill-6144-cached-2048-new-gqa"
 
-    def __init__(self, wid=8, P=6144, n=2048):
+    def __init__(self, wid=8, P=6144, n=2048, kv_dtype=K.BF16):
         self.Hq, self.Hkv, self.D, self.P, self.n = 32, 8, 128, P, n
+        self.kv_dtype = kv_dtype
         std = 1.0 / math.sqrt(self.D)
         nb = synth.blocks_for(P + n)
         table, nblk = synth.block_table([nb], nb, (wid, synth.T_PERM))
         self.table = torch.from_numpy(table).to(DEV)
-        self.cache = K.KVCache.paged(nblk, self.Hkv, self.D, K.BF16, DEV)
+        ks = vs = None
+        if kv_dtype == K.FP8_E4M3:
+            self.name = "chunked-prefill-6144-cached-fp8-2048-new-gqa"
+            sc = synth.fp8_scales(2 * self.Hkv, (wid, synth.T_SCALE), lo=0.5e-3, hi=1.0e-3)
+            ks = torch.from_numpy(sc[:self.Hkv].copy()).to(DEV)
+            vs = torch.from_numpy(sc[self.Hkv:].copy()).to(DEV)
+        self.cache = K.KVCache.paged(nblk, self.Hkv, self.D, kv_dtype, DEV, ks, vs)
         kp = synth.normal_device((1, self.Hkv, P, self.D), (wid, synth.T_K), std=std)
         vp = synth.normal_device((1, self.Hkv, P, self.D), (wid, synth.T_V), std=std)
         K.kv_append(self.cache, kp, vp, torch.zeros(1, dtype=torch.int32, device=DEV), block_table=self.table)
@@ -525,7 +534,9 @@ class ChunkedPrefill:
 
     def config(self):
         return {"workload": self.name, "batch": 1, "q_heads": self.Hq, "kv_heads": self.Hkv, "cached": self.P,
-                "new": self.n, "head_dim": self.D, "dtype": "bf16", "causal": True, "writes_paged_cache": True}
+                "new": self.n, "head_dim": self.D, "dtype": "bf16",
+                "kv_dtype": "fp8_e4m3" if self.kv_dtype == K.FP8_E4M3 else "bf16", "causal": True,
+                "writes_paged_cache": True}
 
 
 class PagedVerify:
@@ -780,7 +791,8 @@ def time_steps(w, steps, warmup, per_launch=False):
     return total_ms / steps, launch
 
 
-LEGS = ("tiny", "padded32", "longctx70b", "verify8b", "prefill8k", "chunkprefill", "cowcopy", "beamreorder", "stream")
+LEGS = ("tiny", "padded32", "longctx70b", "verify8b", "prefill8k", "chunkprefill", "chunkprefill_fp8", "cowcopy",
+        "beamreorder", "stream")
 
 
 def run_leg(name, args, cpu):
@@ -852,15 +864,18 @@ def run_leg(name, args, cpu):
         if cpu:
             rec["cpu_baseline"], rec["parity_max_abs_err_vs_oracle"] = pf.cpu_baseline()
         return rec
-    if name == "chunkprefill":
-        cp = ChunkedPrefill()
+    if name in ("chunkprefill", "chunkprefill_fp8"):
+        cp = ChunkedPrefill(kv_dtype=K.FP8_E4M3 if name == "chunkprefill_fp8" else K.BF16)
         warm_clocks(cp, 1.0)
         msc, _ = time_steps(cp, max(20, args.steps), args.warmup)
         tf = cp.flops() / (msc * 1e-3) / 1e12
         return {"config": cp.config(), "ms_per_step": msc, "TFLOP/s": tf, "frac_of_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS,
                 "flops": cp.flops(),
                 "roofline": {"bound": "mfma", "kernel": "attn_prefill (prefill_mfma_kernel, cached prefix gathered "
-                             "through the block table)", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "through the block table" + (
+                                 "; fp8 codes expanded to bf16 in LDS, after kv_append_kernel quantises the chunk "
+                                 "into the cache)" if cp.kv_dtype == K.FP8_E4M3 else ")"),
+                             "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
     if name in ("cowcopy", "beamreorder"):
         cw = CowBlockCopy() if name == "cowcopy" else BeamReorder()

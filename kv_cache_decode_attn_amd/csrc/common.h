@@ -39,6 +39,18 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
   f[3] = hi[1];
 }
 
+// Four OCP E4M3FN codes -> two words of two bf16 each (codes 0, 1 and codes
+// 2, 3), exactly: every E4M3FN value is a bf16 value, and gfx950 converts a
+// pair of codes to a bf16 pair in one instruction (scale 1).
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+#else
+  lo = hi = w;
+#endif
+}
+
 // float -> OCP E4M3FN code: round to nearest, ties to even, saturate to
 // +-448, NaN -> 0x7F, sign of x kept.  Written on the fp32 bit pattern:
 // magnitudes below 2^-6 are subnormal codes in steps of 2^-9; above that the

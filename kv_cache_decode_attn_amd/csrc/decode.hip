@@ -329,18 +329,6 @@ __device__ __forceinline__ void copy16_to_lds_async(const uint8_t* src, uint8_t*
 #endif
 }
 
-// Four OCP E4M3FN codes -> two words of two bf16 each (codes 0, 1 and codes
-// 2, 3), exactly: every E4M3FN value is a bf16 value, and gfx950 converts a
-// pair of codes to a bf16 pair in one instruction (scale 1).
-__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-#else
-  lo = hi = w;
-#endif
-}
-
 // Byte offset of the K slots in the dynamic LDS of an MFMA partition pass
 // whose other arrays take `floats` floats (rounded up to 16 bytes).
 __host__ __device__ constexpr int kslot_offset(int floats) { return ((floats * 4 + 15) / 16) * 16; }

@@ -69,6 +69,21 @@
 // a new row from the new K/V, with per-lane global-to-LDS transfers.  The
 // workgroup first checks that every prefix block id is valid; if one is not,
 // its positions are masked keys and every tile takes the masked step.
+//
+// fp8 cache prefix.  An E4M3FN code is exactly a bf16 value, so a cached row
+// is staged as its codes (not yet scaled).  The 32-key tile grid is shifted
+// so that a tile starts at key P: a tile then holds only cached keys or only
+// new ones.  The codes of a cached tile (half the bytes of its bf16 rows)
+// take one 16-byte global-to-LDS transfer per lane into a staging ring, and
+// when the tile is published each wave expands its piece into the bf16
+// slots.  The dequantisation
+// scales ("KV Cache Fully Explained", section "(1) FP8 quantization": values
+// are stored at 8 bits with a scale) enter as factors: the K scale is folded
+// into the score scale of the tiles of cached keys, and since every cached
+// key precedes every new one, the output accumulates the cached keys' V
+// codes unscaled and is multiplied by the V scale once, before the PV
+// product of the tile that starts at P.  The row sums take the weights as
+// they are.
 #include <math.h>
 
 #include <type_traits>
@@ -208,9 +223,22 @@ __device__ __forceinline__ s16x4 read_tr16(const uint8_t* lds) {
 #endif
 }
 
-template <int D, bool CAUSAL, bool MASK, bool PREFIX>
+// LDS tile buffers of the kernel: with an fp8 prefix one fewer (seven
+// still hold tiles it - 1 .. it + kAhead), and after them a staging ring of
+// kStage tiles of fp8 codes (per loading wave 512 bytes of K codes, then 512
+// of V).
+constexpr int kStage = kAhead;  // tiles whose transfers can be in flight at once
+template <int D, bool FP8P>
+constexpr int ring_bufs() { return FP8P ? kBufs - 1 : kBufs; }
+template <int D, bool FP8P>
+constexpr int prefill_lds_bytes() { return ring_bufs<D, FP8P>() * Geo<D>::BUF + (FP8P ? kStage * 2 * kKeys * D : 0); }
+
+template <int D, bool CAUSAL, bool MASK, bool PREFIX, bool FP8P>
 __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const PrefillLaunch a, int hw) {
+  static_assert(PREFIX || !FP8P, "fp8 rows come only from a cached prefix");
   using GE = Geo<D>;
+  constexpr int NB = ring_bufs<D, FP8P>();  // tile buffers in the ring
+  constexpr int S8 = kKeys * D;             // bytes of one operand's fp8 codes per tile
   constexpr int DK = D / 16;  // 16-wide d chunks of the QK^T contraction
   constexpr int DT = D / 32;  // 32-row d tiles of the output
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -259,10 +287,14 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     }
     return;
   }
+  // Tile t holds keys 32t - ksh .. 32t - ksh + 31.  With an fp8 prefix the
+  // grid is shifted so that a tile starts at key P: no tile then holds both
+  // cached and new keys (keys below 0 are absent, masked in the first tile).
+  const int ksh = FP8P ? (kKeys - P % kKeys) % kKeys : 0;
   const int key_end = CAUSAL ? min(Ltot, QO + q_wg + rows_wg) : Ltot;  // workgroup bound
   const int wave_end = CAUSAL ? min(Ltot, QO + row_hi) : Ltot;          // this wave's bound
-  const int ntiles = (key_end + kKeys - 1) / kKeys;
-  const int wave_tiles = (wave_end + kKeys - 1) / kKeys;
+  const int ntiles = (key_end + ksh + kKeys - 1) / kKeys;
+  const int wave_tiles = (wave_end + ksh + kKeys - 1) / kKeys;
   // Whether every prefix position lies in the cache (a valid block id for
   // each of its blocks): one scan of the sequence's table row by the
   // workgroup.  Prefix positions outside the cache are masked keys.
@@ -287,11 +319,21 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     __syncthreads();
     prefix_ok = __builtin_amdgcn_readfirstlane(bad) == 0;  // uniform (the loop bounds depend on it)
   }
+  // fp8 prefix: the dequantisation scales of KV head g.  The tile that
+  // starts at key P (the first new key) is where the output takes the V
+  // scale, before its PV product.
+  float ksc = 1.f, vsc = 1.f;
+  if constexpr (FP8P) {
+    ksc = a.k_scale[g];
+    vsc = a.v_scale[g];
+  }
   // Tiles below fast_end need no mask: every key is real, in the cache and
   // causally visible to every query of the wave.
-  const int fast_end = (MASK || !prefix_ok)
+  // With an fp8 prefix, a K scale <= 0 (which cannot be folded into the
+  // score scale of the running maximum) makes every step masked.
+  const int fast_end = (MASK || !prefix_ok || (FP8P && !(ksc > 0.f)))
                            ? 0
-                           : min(wave_tiles, (CAUSAL ? min(Ltot, QO + row_lo + 1) : Ltot) / kKeys);
+                           : min(wave_tiles, ((CAUSAL ? min(Ltot, QO + row_lo + 1) : Ltot) + ksh) / kKeys);
 
   const int64_t head_bytes = (int64_t)n_max * D * 2;
   const uint8_t* kg = a.k + ((int64_t)b * a.num_kv_heads + g) * head_bytes;
@@ -322,7 +364,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // it return zeros, so rows of absent keys are staged as zeros.  With a key
   // mask, rows of masked keys are zeroed by the loading wave once its loads
   // have landed, so no non-finite padding reaches the PV product.
-  const int key_lim = min(Ltot, ntiles * kKeys);
+  const int key_lim = min(Ltot, ntiles * kKeys - ksh);
   int koff[GE::LOADS], voff[GE::LOADS], lrow[GE::LOADS];  // per lane, tile independent
 #pragma unroll
   for (int i = 0; i < GE::LOADS; ++i) {
@@ -344,8 +386,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   const int mask_last = MASK ? (int)min<int64_t>(a.key_mask_stride, (int64_t)INT32_MAX) - 1 : 0;
   auto key_valid = [&](int key) -> bool {
     bool ok = key < Ltot;
+    if (FP8P) ok = ok & (key >= 0);  // the shifted first tile
     if (MASK) {
-      const uint8_t mb = mrow[min(kbase + key, mask_last)];  // always inside the mask row
+      const int mi = FP8P ? max(kbase + key, 0) : kbase + key;
+      const uint8_t mb = mrow[min(mi, mask_last)];  // always inside the mask row
       ok = ok & (kbase + key <= mask_last) & (mb != 0);
     }
     if (PREFIX && !prefix_ok) {  // uniform: only with prefix positions outside the cache
@@ -354,14 +398,28 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     }
     return ok;
   };
-  // With a key mask, per lane and tile in flight: bit i = this lane's V
-  // piece of load i belongs to a masked key.  A queue, oldest tile in the
-  // low byte: load_tile appends at byte `slot` (the number of tiles already
-  // queued), finish_tile pops the low byte.
+  // With a key mask or a prefix, per lane and tile in flight: bit i = this
+  // lane's V piece of load i belongs to a masked key; bit 4 (fp8 prefix) =
+  // the tile's keys are cached rows whose codes are in the staging ring.  A
+  // queue, oldest tile in the low byte: load_tile appends at byte `slot`
+  // (the number of tiles already queued), finish_tile pops the low byte.
+  static_assert(GE::LOADS <= 4, "per-tile flags fit a byte");
+  static_assert(!FP8P || GE::LOADS == 1, "fp8 staging: one piece of K and V per loading wave");
   uint64_t pending = 0;
+  // fp8 prefix, a tile of cached keys: lane L fetches the 16 codes of the
+  // two slots 2(L % 32) and 2(L % 32) + 1 of its wave's piece (K for L < 32,
+  // V above) into the staging ring at 16 L.  The two slots are adjacent
+  // chunks of one row, and the swizzle XORs chunk indices with a value that
+  // keeps such a pair together, so their codes are one aligned 16 bytes of
+  // the cached row.
+  const int f_op = lane >> 5;
+  const int f_slot = wave * 64 + 2 * (lane & 31);
+  const int f_row = f_slot / GE::NC;
+  const int f_chunk = (((f_slot % GE::NC) ^ (f_op ? GE::swz_v(f_row) : GE::swz_k(f_row))) >> 1) * 16;
+  uint8_t* const stage = smem + NB * GE::BUF;  // [kStage][pieces][K 512 B, V 512 B] (fp8 prefix)
   auto load_tile = [&](int t, int slot) {
-    const int kt0 = t * kKeys;
-    uint8_t* kl = smem + (t % kBufs) * GE::BUF;
+    const int kt0 = t * kKeys - ksh;
+    uint8_t* kl = smem + (t % NB) * GE::BUF;
     uint8_t* vl = kl + GE::KBYTES;
     if (wave >= GE::LWAVES) return;
     if constexpr (zero_rows) {
@@ -375,6 +433,20 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
       pending |= (uint64_t)info << (8 * slot);
     }
     if constexpr (PREFIX) {
+      if (FP8P && kt0 < P) {  // uniform: a tile of cached keys (the grid has no mixed tile)
+        const int key = kt0 + f_row;
+        const uint8_t* src = kg;  // new token 0: the stand-in for rows outside the cache
+        if (key >= 0) {
+          const int64_t off = position_offset(a.c, b, g, kbase + key);
+          if (off >= 0) src = (f_op ? a.c.v : a.c.k) + off + f_chunk;
+        }
+        // issued twice (the same bytes to the same place): every tile then
+        // takes two transfers per lane, and the waits stay constants
+        load_lds16_ptr(src, stage + (t % kStage) * 2 * S8 + wave * 1024);
+        load_lds16_ptr(src, stage + (t % kStage) * 2 * S8 + wave * 1024);
+        pending |= (uint64_t)16 << (8 * slot);
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < GE::LOADS; ++i) {
         const int key = kt0 + lrow[i];
@@ -410,16 +482,36 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     }
   };
   // Waits until at most `younger` tiles' loads of this wave are in flight
-  // (so the oldest pending tile, t, has landed), then (key mask) zeroes its
-  // masked V rows.
+  // (so the oldest pending tile, t, has landed), then (fp8 prefix) expands
+  // the staged codes of a tile of cached keys into its bf16 slots and (key
+  // mask, prefix) zeroes its masked V rows.  Each loading lane issues two
+  // transfers per tile and load.
   auto finish_tile = [&](int t, auto younger) {
-    constexpr int vm = decltype(younger)::value * 2 * GE::LOADS;  // loads per tile: K and V
+    constexpr int vm = decltype(younger)::value * 2 * GE::LOADS;
     static_assert(vm < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8));  // vmcnt(vm)
     if constexpr (zero_rows) {
-      uint8_t* vl = smem + (t % kBufs) * GE::BUF + GE::KBYTES;
+      // the LDS accesses below touch bytes the transfers wrote: keep them after the wait
+      __asm__ volatile("" ::: "memory");
+      uint8_t* vl = smem + (t % NB) * GE::BUF + GE::KBYTES;
       const uint32_t info = (uint32_t)pending & 0xffu;
       pending >>= 8;
+      if constexpr (FP8P) {
+        if (info & 16u) {  // uniform
+          uint8_t* kl = smem + (t % NB) * GE::BUF;
+          const uint8_t* st = stage + (t % kStage) * 2 * S8 + wave * 1024 + (lane >> 1) * 16;
+          const int gk = (koff[0] - lrow[0] * GE::RB) >> 4, gv = (voff[0] - lrow[0] * GE::RB) >> 4;
+          const U2 ck = *reinterpret_cast<const U2*>(st + (gk & 1) * 8);
+          const U2 cv = *reinterpret_cast<const U2*>(st + 512 + (gv & 1) * 8);
+          U4 wk, wv;
+          fp8x4_to_bf16x4(ck.x, wk.x, wk.y);
+          fp8x4_to_bf16x4(ck.y, wk.z, wk.w);
+          fp8x4_to_bf16x4(cv.x, wv.x, wv.y);
+          fp8x4_to_bf16x4(cv.y, wv.z, wv.w);
+          *reinterpret_cast<U4*>(kl + wave * 1024 + lane * 16) = wk;
+          *reinterpret_cast<U4*>(vl + wave * 1024 + lane * 16) = wv;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < GE::LOADS; ++i)
         if (info & (1u << i)) *reinterpret_cast<U4*>(vl + (wave * GE::LOADS + i) * 1024 + lane * 16) = U4{0, 0, 0, 0};
@@ -460,6 +552,20 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // once the previous tile's PV product is in, and `resc` whether any lane
   // of the wave needs it.
   auto softmax = [&](auto masked, int kt0, int buf, f32x16 (&s)[kCB], U4 (&pf)[kCB][2], float (&alpha)[kCB], bool& resc) {
+    float ct = c;  // score scale (log2 domain) of the tile
+    if constexpr (FP8P) {
+      if (kt0 < P) {  // uniform: a tile of cached keys (codes: the K scale is due)
+        if (ksc > 0.f) {
+          ct = c * ksc;
+        } else if constexpr (decltype(masked)::value) {
+          // every step is masked then; the scale goes in before the mask
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int cb = 0; cb < kCB; ++cb) s[cb][r] *= ksc;
+        }
+      }
+    }
     if constexpr (decltype(masked)::value) {
       // causal edge, keys beyond q_len, key mask (keys kt0 + 8gq + 4hh + e)
 #pragma unroll
@@ -485,7 +591,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
       for (int r = 2; r < 16; r += 2) tm = fmaxf(tm, fmaxf(s[cb][r], s[cb][r + 1]));
       {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
-        tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+        tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * ct;
       }
       const bool need = tm > mrun[cb] + kRescale;
       const float mnew = need ? tm : mrun[cb];
@@ -496,7 +602,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
       float l = lpart[cb] * alpha[cb];
       float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[cb][r], c, -msub));
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[cb][r], ct, -msub));
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         pf[cb][m] = U4{pack_bf16(p[8 * m], p[8 * m + 1]), pack_bf16(p[8 * m + 2], p[8 * m + 3]),
@@ -509,6 +615,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
       lpart[cb] = l;
     }
     resc = __any(any_need);
+    if constexpr (FP8P) {
+      // the tile that starts at key P: the cached keys' V codes accumulated
+      // so far take the V scale before its PV product (with any rescale of
+      // the running maximum); l is not scaled
+      if (kt0 == P) {
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) alpha[cb] *= vsc;
+        resc = true;
+      }
+    }
   };
 
   // O^T += V^T P^T for the tile in buffer `buf`; each V^T fragment feeds
@@ -557,7 +673,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // Step it: scores of tile it + 1, softmax of tile it and the PV product of
   // tile it - 1.  Tile it + kAhead is loaded meanwhile and tile it + 2,
   // loaded kAhead - 2 steps earlier, is published by the barrier that ends
-  // the step.  Buffers t % 8 hold tiles it - 1 .. it + kAhead.  Every wave
+  // the step.  Buffers t % NB hold tiles it - 1 .. it + kAhead.  Every wave
   // runs the same number of steps (ntiles + 1), so the barriers match.  The
   // three parts are independent: the compiler interleaves them, and the
   // other wave of the SIMD fills the matrix or vector units while this one
@@ -569,9 +685,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   auto fast_step = [&](int it, f32x16 (&s_cur)[kCB], f32x16 (&s_nxt)[kCB], const U4 (&p_prev)[kCB][2],
                        U4 (&p_cur)[kCB][2], float (&alpha)[kCB], bool& resc, f32x16 (&o)[kCB][DT]) {
     load_tile(it + kAhead, kAhead - 2);
-    scores((it + 1) % kBufs, s_nxt);
-    softmax(std::false_type{}, it * kKeys, it % kBufs, s_cur, p_cur, alpha, resc);
-    pv((it + kBufs - 1) % kBufs, p_prev, o);
+    scores((it + 1) % NB, s_nxt);
+    softmax(std::false_type{}, it * kKeys - ksh, it % NB, s_cur, p_cur, alpha, resc);
+    pv((it + NB - 1) % NB, p_prev, o);
     finish_tile(it + 2, std::integral_constant<int, kAhead - 2>{});
     __syncthreads();
   };
@@ -583,9 +699,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) alpha[cb] = 1.f;
     bool resc = false;
-    if (it + 1 < wave_tiles) scores((it + 1) % kBufs, s_nxt);
-    if (it < wave_tiles) softmax(std::true_type{}, it * kKeys, it % kBufs, s_cur, p_cur, alpha, resc);
-    if (it >= 1 && it - 1 < wave_tiles) pv((it + kBufs - 1) % kBufs, p_prev, o);
+    if (it + 1 < wave_tiles) scores((it + 1) % NB, s_nxt);
+    if (it < wave_tiles) softmax(std::true_type{}, it * kKeys - ksh, it % NB, s_cur, p_cur, alpha, resc);
+    if (it >= 1 && it - 1 < wave_tiles) pv((it + NB - 1) % NB, p_prev, o);
     finish_tile(it + 2, std::integral_constant<int, kAhead - 2>{});
     if (resc) rescale(alpha, o);
     __syncthreads();
@@ -693,27 +809,30 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   }
 }
 
-template <int D, bool CAUSAL, bool MASK, bool PREFIX>
+template <int D, bool CAUSAL, bool MASK, bool PREFIX, bool FP8P>
 int launch_typed(const PrefillLaunch& a, hipStream_t s) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int hw = G < kBlocks ? G : kBlocks;
   const int rows = 32 * kBlocks / hw;
   const dim3 grid(a.num_q_heads / hw, (a.n_max + rows - 1) / rows, a.batch);
-  const size_t lds = kBufs * Geo<D>::BUF;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, CAUSAL, MASK, PREFIX>), grid, dim3(kThreads), lds, s, a, hw);
+  const size_t lds = prefill_lds_bytes<D, FP8P>();
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, CAUSAL, MASK, PREFIX, FP8P>), grid, dim3(kThreads), lds, s, a, hw);
   return hipGetLastError() == hipSuccess ? KVATTN_OK : KVATTN_ELAUNCH;
 }
 
-template <int D, bool PREFIX>
+template <int D, bool PREFIX, bool FP8P>
 int launch_flags(const PrefillLaunch& a, hipStream_t s) {
   if (a.causal)
-    return a.key_mask ? launch_typed<D, true, true, PREFIX>(a, s) : launch_typed<D, true, false, PREFIX>(a, s);
-  return a.key_mask ? launch_typed<D, false, true, PREFIX>(a, s) : launch_typed<D, false, false, PREFIX>(a, s);
+    return a.key_mask ? launch_typed<D, true, true, PREFIX, FP8P>(a, s)
+                      : launch_typed<D, true, false, PREFIX, FP8P>(a, s);
+  return a.key_mask ? launch_typed<D, false, true, PREFIX, FP8P>(a, s)
+                    : launch_typed<D, false, false, PREFIX, FP8P>(a, s);
 }
 
 template <int D>
 int launch_prefix(const PrefillLaunch& a, hipStream_t s) {
-  return (a.has_cache && a.attend_prefix) ? launch_flags<D, true>(a, s) : launch_flags<D, false>(a, s);
+  if (!(a.has_cache && a.attend_prefix)) return launch_flags<D, false, false>(a, s);
+  return a.cache_dtype == KVATTN_FP8_E4M3 ? launch_flags<D, true, true>(a, s) : launch_flags<D, true, false>(a, s);
 }
 
 }  // namespace
@@ -721,9 +840,11 @@ int launch_prefix(const PrefillLaunch& a, hipStream_t s) {
 bool prefill_mfma_supports(const PrefillLaunch& a) {
   if (a.dtype != KVATTN_BF16) return false;
   if (a.head_dim != 64 && a.head_dim != 128) return false;
-  // a cached prefix is read by this kernel from a bf16 cache (same rows as
-  // the new K/V); other cache types take the general kernel
-  if (a.has_cache && a.attend_prefix && a.cache_dtype != KVATTN_BF16) return false;
+  // a cached prefix is read from a bf16 cache or an fp8 cache (its codes
+  // expanded to bf16 in LDS, the scales applied as factors)
+  if (a.has_cache && a.attend_prefix && a.cache_dtype != KVATTN_BF16 && a.cache_dtype != KVATTN_FP8_E4M3) return false;
+  // the running maximum is taken as max(scores) * scale, which needs scale > 0
+  if (!(a.scale > 0.f)) return false;
   if ((int64_t)a.n_max * a.head_dim * 2 >= ((int64_t)1 << 31) - 4096) return false;  // 32-bit buffer offsets
   const int G = a.num_q_heads / a.num_kv_heads;
   return G == 1 || G == 2 || G == 4 || G == 8;

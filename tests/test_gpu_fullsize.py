@@ -205,3 +205,46 @@ def test_chunked_prefill_6144_cached_2048_new_full_size():
     assert torch.equal(_paged_rows(w.cache.v, w.table, 0, new_pos).transpose(0, 1), w.v[0])
     prefix_pos = list(range(w.P))
     assert torch.equal(_paged_rows(w.cache.k, w.table, 0, prefix_pos).transpose(0, 1), kp[0])
+
+
+def test_chunked_prefill_fp8_cache_full_size():
+    """The same 2,048-token chunk against an fp8 (E4M3FN) cache of the 6,144
+    positions (the timed chunkprefill_fp8 call): sampled rows of every head
+    against the oracle with the cached rows dequantised by the oracle's own
+    codec, and the chunk's codes in the cache bit for bit against the
+    oracle's encoder."""
+    bench = _bench()
+    from kv_cache_decode_attn_amd import synth
+    w = bench.ChunkedPrefill(kv_dtype=K.FP8_E4M3)
+    w.step(0)
+    torch.cuda.synchronize()
+    std = 1.0 / math.sqrt(w.D)
+    kp = synth.normal_device((1, w.Hkv, w.P, w.D), (8, synth.T_K), std=std)   # the appended prefix
+    vp = synth.normal_device((1, w.Hkv, w.P, w.D), (8, synth.T_V), std=std)
+    ks = w.cache.k_scale.cpu().numpy()
+    vs = w.cache.v_scale.cpu().numpy()
+
+    def deq(x, sc):
+        return np.stack([OC.to_f64(OC.encode_rows(storage(x[0])[g], OC.BF16, OC.FP8_E4M3, sc[g]), OC.FP8_E4M3, sc[g])
+                         for g in range(w.Hkv)])
+    kf = np.concatenate([deq(kp, ks), f64(w.k[0])], axis=1)
+    vf = np.concatenate([deq(vp, vs), f64(w.v[0])], axis=1)
+    rows = sorted({0, 1, 31, 32, 1023, 2046, 2047} |
+                  set(int(x) for x in np.random.default_rng(106).choice(w.n, size=5, replace=False)))
+    got = w.out[0][:, rows].cpu().numpy()
+    qf = f64(w.q[0][:, rows])
+    G = w.Hq // w.Hkv
+    scale = 1.0 / math.sqrt(w.D)
+    allow = np.arange(w.P + w.n)[None, :] <= (w.P + np.asarray(rows))[:, None]
+    for h in range(w.Hq):
+        want = OA.sdpa(qf[h], kf[h // G], vf[h // G], allow, scale)
+        assert max_abs(got[h], want) <= TOL, h
+    new_pos = [0, 1, 15, 16, 1000, 2047]
+    got_k = _paged_rows(w.cache.k, w.table, 0, [w.P + i for i in new_pos]).cpu().numpy()  # [n, Hkv, D] codes
+    got_v = _paged_rows(w.cache.v, w.table, 0, [w.P + i for i in new_pos]).cpu().numpy()
+    for j, i in enumerate(new_pos):
+        for g in range(w.Hkv):
+            np.testing.assert_array_equal(got_k[j, g], OC.encode_rows(storage(w.k[0, g, i]), OC.BF16, OC.FP8_E4M3,
+                                                                     ks[g]))
+            np.testing.assert_array_equal(got_v[j, g], OC.encode_rows(storage(w.v[0, g, i]), OC.BF16, OC.FP8_E4M3,
+                                                                     vs[g]))

@@ -263,16 +263,23 @@ def test_mfma_prefill_each_masked_key_gets_zero_weight(causal):
         assert np.abs(got[rows].sum(axis=1) - 1.0).max() <= 1e-6, masked
 
 
-def _prefix_case(B, Hq, Hkv, d, P, n2, layout, seed, poison=None):
-    """A bf16 cache holding positions 0 .. P[b]-1 of each sequence (appended
-    from seeded rows; `poison` marks prefix positions whose K/V are set to NaN
-    first), and a padded chunk of n2[b] new tokens."""
+def _prefix_case(B, Hq, Hkv, d, P, n2, layout, seed, poison=None, cache_dtype=K.BF16, scales=None):
+    """A cache holding positions 0 .. P[b]-1 of each sequence (appended from
+    seeded bf16 rows; `poison` marks prefix positions whose K/V are set to NaN
+    first), and a padded chunk of n2[b] new tokens.  An fp8 cache takes the
+    per-head (k_scale, v_scale) of `scales`, and the oracle's prefix is then
+    its own decoding of its own E4M3FN encoding of those rows."""
     P = np.asarray(P, np.int32)
     n2 = np.asarray(n2, np.int32)
     n_max = int(n2.max())
     total = int((P + n2).max())
-    kp = synth.normal((B, Hkv, total, d), (seed, synth.T_K), torch.bfloat16, std=1 / math.sqrt(d))
-    vp = synth.normal((B, Hkv, total, d), (seed, synth.T_V), torch.bfloat16, std=1 / math.sqrt(d))
+    std = 1.0 if cache_dtype == K.FP8_E4M3 else 1 / math.sqrt(d)
+    kp = synth.normal((B, Hkv, total, d), (seed, synth.T_K), torch.bfloat16, std=std)
+    vp = synth.normal((B, Hkv, total, d), (seed, synth.T_V), torch.bfloat16, std=std)
+    ks = vs = None
+    if cache_dtype == K.FP8_E4M3:
+        ks = torch.tensor(scales[0], dtype=torch.float32, device=DEV)
+        vs = torch.tensor(scales[1], dtype=torch.float32, device=DEV)
     if poison is not None:
         for b, s in zip(*np.nonzero(poison[:, :total])):
             kp[b, :, s] = float("nan")
@@ -286,16 +293,24 @@ def _prefix_case(B, Hq, Hkv, d, P, n2, layout, seed, poison=None):
     if layout == K.PAGED:
         nbs = [synth.blocks_for(int(P[b] + n2[b])) for b in range(B)]
         table, nblk = synth.block_table(nbs, max(nbs), (seed, synth.T_PERM))
-        cache = K.KVCache.paged(nblk, Hkv, d, K.BF16, DEV)
+        cache = K.KVCache.paged(nblk, Hkv, d, cache_dtype, DEV, ks, vs)
         tdev = torch.from_numpy(table).to(DEV)
     else:
         cap = -(-total // 16) * 16
-        cache = K.KVCache.contiguous(B, Hkv, cap, d, K.BF16, DEV)
+        cache = K.KVCache.contiguous(B, Hkv, cap, d, cache_dtype, DEV, ks, vs)
     cache.k.zero_()
     cache.v.zero_()
     zeros = torch.zeros(B, dtype=torch.int32, device=DEV)
     K.kv_append(cache, kp.to(DEV), vp.to(DEV), zeros, block_table=tdev, n_valid=torch.from_numpy(P).to(DEV))
-    prefix = ([f64(kp[b, :, :P[b]]) for b in range(B)], [f64(vp[b, :, :P[b]]) for b in range(B)])
+    if cache_dtype == K.FP8_E4M3:
+        def deq(x, b, sc):
+            with np.errstate(divide="ignore"):   # a zero scale encodes every value as +-448
+                return np.stack([OC.to_f64(OC.encode_rows(storage(x)[b, g, :P[b]], OC.BF16, OC.FP8_E4M3,
+                                                          np.float32(sc[g])), OC.FP8_E4M3, np.float32(sc[g]))
+                                 for g in range(Hkv)])
+        prefix = ([deq(kp, b, scales[0]) for b in range(B)], [deq(vp, b, scales[1]) for b in range(B)])
+    else:
+        prefix = ([f64(kp[b, :, :P[b]]) for b in range(B)], [f64(vp[b, :, :P[b]]) for b in range(B)])
     return cache, table, tdev, q2, k2, v2, P, n2, prefix
 
 
@@ -387,4 +402,62 @@ def test_mfma_prefix_invalid_block_ids_are_masked():
     mask[0, 16:32] = 0
     mask[0, 64:80] = 0
     want = _oracle(q2, k2, v2, P, n2, key_mask=mask, prefix=prefix)
+    assert max_abs(got, want) <= TOL
+
+
+FP8_SCALES = ([0.011, 0.023], [0.017, 0.009])   # per KV head (k_scale, v_scale): codes up to ~400
+
+
+@pytest.mark.parametrize("G,d", [(4, 128), (8, 64), (1, 128), (2, 64)])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("layout", [K.PAGED, K.CONTIGUOUS])
+@pytest.mark.parametrize("P,n2", [([77, 130], [100, 37]), ([64, 0], [70, 33])])
+def test_mfma_fp8_prefix_chunk(G, d, causal, layout, P, n2):
+    """bf16 chunk against an fp8 (E4M3FN) cached prefix on the matrix-core
+    kernel: the cached rows are dequantised with per-head K and V scales
+    ("KV Cache Fully Explained", section "(1) FP8 quantization"); prefixes
+    that end inside a 32-key tile (77, 130), on a tile edge (64) and empty
+    (0); ragged chunks, causal and not, paged and contiguous."""
+    B, Hkv = 2, 2
+    Hq = G * Hkv
+    cache, table, tdev, q2, k2, v2, P, n2, prefix = _prefix_case(
+        B, Hq, Hkv, d, P, n2, layout, 80 + G + d, cache_dtype=K.FP8_E4M3, scales=FP8_SCALES)
+    got = K.attn_prefill(q2.to(DEV), k2.to(DEV), v2.to(DEV), cache=cache, positions=torch.from_numpy(P).to(DEV),
+                         q_lens=torch.from_numpy(n2).to(DEV), block_table=tdev, causal=causal,
+                         attend_prefix=True).cpu().numpy()
+    want = _oracle(q2, k2, v2, P, n2, causal=causal, prefix=prefix)
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= TOL
+    for b in range(B):
+        assert np.all(got[b, :, n2[b]:] == 0.0)
+
+
+@pytest.mark.parametrize("scales", [([-0.011, 0.023], [0.017, -0.009]), ([0.011, 0.023], [0.0, 0.009])])
+def test_mfma_fp8_prefix_key_mask_and_scale_signs(scales):
+    """fp8 prefix with a key mask over absolute positions, a negative K scale
+    (not foldable into the score scale: every tile takes the masked step), a
+    negative V scale and a zero V scale."""
+    B, Hq, Hkv, d = 2, 8, 2, 128
+    P, n2 = [150, 45], [64, 90]
+    mask = synth.random_mask((B, 240), 0.7, (82, synth.T_MASK))
+    mask[:, 0] = 1
+    cache, table, tdev, q2, k2, v2, P, n2, prefix = _prefix_case(
+        B, Hq, Hkv, d, P, n2, K.PAGED, 83, cache_dtype=K.FP8_E4M3, scales=scales)
+    got = K.attn_prefill(q2.to(DEV), k2.to(DEV), v2.to(DEV), cache=cache, positions=torch.from_numpy(P).to(DEV),
+                         q_lens=torch.from_numpy(n2).to(DEV), block_table=tdev,
+                         key_mask=torch.from_numpy(mask).to(DEV), attend_prefix=True).cpu().numpy()
+    want = _oracle(q2, k2, v2, P, n2, key_mask=mask, prefix=prefix)
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= TOL
+
+
+def test_mfma_fp8_prefix_long_many_tiles():
+    """A 1,000-position fp8 prefix (not a whole number of tiles) and a
+    300-token chunk (GQA 4, d 128): most tiles take the unmasked step."""
+    B, Hq, Hkv, d = 1, 8, 2, 128
+    cache, table, tdev, q2, k2, v2, P, n2, prefix = _prefix_case(
+        B, Hq, Hkv, d, [1000], [300], K.PAGED, 84, cache_dtype=K.FP8_E4M3, scales=FP8_SCALES)
+    got = K.attn_prefill(q2.to(DEV), k2.to(DEV), v2.to(DEV), cache=cache, positions=torch.from_numpy(P).to(DEV),
+                         block_table=tdev, attend_prefix=True).cpu().numpy()
+    want = _oracle(q2, k2, v2, P, n2, prefix=prefix)
     assert max_abs(got, want) <= TOL
