@@ -57,12 +57,14 @@ METRIC = "decode-attn HBM GB/s (% of peak) & seqs/s; prefill TFLOP/s (% MFMA pea
 DEV = "cuda"
 
 
-# Sources each workload's timed kernels are built from: files, and the
-# launch-argument structs of launch.h they compile against.
+# Sources each workload's timed kernels are built from: files (the build
+# script included: it holds the compiler flags), and the launch-argument
+# structs of launch.h they compile against.
 CSRC = "kv_cache_decode_attn_amd/csrc/"
+BUILD_PY = "kv_cache_decode_attn_amd/build.py"
 KERNEL_SOURCES = {
-    "decode": (CSRC + "decode.hip", CSRC + "common.h", "DecodeLaunch"),
-    "prefill": (CSRC + "prefill_mfma.hip", CSRC + "common.h", "PrefillLaunch"),
+    "decode": (CSRC + "decode.hip", CSRC + "common.h", BUILD_PY, "DecodeLaunch"),
+    "prefill": (CSRC + "prefill_mfma.hip", CSRC + "common.h", BUILD_PY, "PrefillLaunch"),
 }
 WORKLOAD_KERNELS = {"decode8b": "decode", "padded32": "decode", "longctx70b": "decode", "verify8b": "decode",
                     "prefill8k": "prefill"}
@@ -81,7 +83,7 @@ def source_sha(kind, read=None):
                 return f.read()
     h = hashlib.sha256()
     for item in KERNEL_SOURCES[kind]:
-        if item.endswith((".hip", ".h")):
+        if item.endswith((".hip", ".h", ".py")):
             h.update(read(item))
         else:
             h.update(_launch_struct(read(CSRC + "launch.h").decode(), item).encode())

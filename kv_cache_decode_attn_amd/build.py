@@ -41,7 +41,12 @@ COMMON = [
 #    softmax right away); with no accumulation registers in use the compiler
 #    can give each of the two waves per SIMD all 256 registers, and the
 #    allocation has no copies between the two register files.
-EXTRA = {"prefill_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# decode.hip: matrix results in vector registers too.  Its passes hold the
+# output accumulator in registers across the whole sweep; without
+# accumulation registers the 16-column pass fits three waves per SIMD
+# instead of two (150 registers in one file against 148 + 40 in two).
+EXTRA = {"prefill_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):
