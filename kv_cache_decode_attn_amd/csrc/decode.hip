@@ -460,7 +460,7 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
     const float mref = (m == -INFINITY) ? 0.f : m;
     float l = 0.f;
     for (int t = lane; t < n; t += kWave) {
-      const float e = exp2f(s_lds[t * G + h] - mref);
+      const float e = __builtin_amdgcn_exp2f(s_lds[t * G + h] - mref);  // argument <= 0
       s_lds[t * G + h] = e;
       l += e;
     }
@@ -736,7 +736,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
     const float mref = (m == -INFINITY) ? 0.f : m;
     float l = 0.f;
     for (int t = lane; t < n; t += kWave) {
-      const float e = exp2f(sh[t] - mref);
+      const float e = __builtin_amdgcn_exp2f(sh[t] - mref);  // argument <= 0
       sh[t] = e;
       l += e;
     }
@@ -1024,7 +1024,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
     const bool need = bm > mrun + kRescale;
     if (__any(need)) {
       const float mnew = need ? bm : mrun;
-      const float alpha = need ? exp2f(mrun - mnew) : 1.f;  // 0 when mrun = -inf
+      const float alpha = need ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.f;  // 0 when mrun = -inf
 #pragma unroll
       for (int t = 0; t < NT; ++t) o[t] *= alpha;
       lsum *= alpha;
@@ -1349,7 +1349,7 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     const bool need = bm > mrun + kRescale;
     if (__any(need)) {
       const float mnew = need ? bm : mrun;
-      const float alpha = need ? exp2f(mrun - mnew) : 1.f;  // 0 when mrun = -inf
+      const float alpha = need ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.f;  // 0 when mrun = -inf
 #pragma unroll
       for (int t = 0; t < NT; ++t) o[t] *= alpha;
       lsum *= alpha;

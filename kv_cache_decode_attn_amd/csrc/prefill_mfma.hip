@@ -595,7 +595,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
       }
       const bool need = tm > mrun[cb] + kRescale;
       const float mnew = need ? tm : mrun[cb];
-      alpha[cb] = need ? exp2f(mrun[cb] - mnew) : 1.f;
+      alpha[cb] = need ? __builtin_amdgcn_exp2f(mrun[cb] - mnew) : 1.f;  // argument < -64 or -inf: 0
       any_need |= need && mrun[cb] != -INFINITY;  // nothing accumulated yet: nothing to rescale
       mrun[cb] = mnew;
       const float msub = (mnew == -INFINITY) ? 0.f : mnew;
