@@ -481,6 +481,20 @@ int kvattn_copy_blocks(const kvattn_cache* cache, int32_t n,
                        const int32_t* src_blocks, const int32_t* dst_blocks,
                        void* stream);
 
+/* kvattn_stream_read - measurement helper, not part of the attention path:
+ * one plain pass over device memory, the context figure for the HBM-bound
+ * calls above (decode reads the whole cache every step, "KV Cache", section
+ * "Prefill and Decode").  Reads [src, src + bytes) once with 16-byte
+ * non-temporal loads (each wave 1 KB contiguous per instruction, 8
+ * workgroups of 256 threads per compute unit) and XORs the XOR of all its
+ * 32-bit words into *sink, so the result can be checked exactly.
+ *
+ *  src    device, 16-byte aligned
+ *  bytes  a multiple of 16 (0 is a no-op)
+ *  sink   device uint32, 4-byte aligned; the caller sets it (e.g. to 0)
+ * Errors: KVATTN_EINVAL (NULL pointer, alignment, bytes). */
+int kvattn_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Host block pool.
  *

@@ -11,13 +11,13 @@ from ._lib import (BF16, BLOCK_TOKENS, CONTIGUOUS, EINVAL, ELAUNCH, ENOSPACE, EU
                    NOALLOC_SCRATCH_BYTES, OK, PAGED, VALIDATE_BLOCK_RANGE, VALIDATE_LEN_RANGE, VALIDATE_POSITION,
                    KvattnError)
 from .api import (BlockPool, KVCache, attn_decode, attn_decode_append, attn_decode_append_noalloc, attn_decode_multi,
-                  attn_prefill, cache_bytes, copy_blocks, decode_default_part_tokens, decode_workspace,
+                  attn_prefill, cache_bytes, copy_blocks, stream_read, decode_default_part_tokens, decode_workspace,
                   decode_workspace_bytes, kv_append, reorder_cache, reorder_rows, validate, version)
 
 __all__ = [
     "KVCache", "attn_decode", "attn_decode_append", "attn_decode_append_noalloc", "attn_decode_multi", "attn_prefill",
     "cache_bytes",
     "decode_default_part_tokens", "decode_workspace", "decode_workspace_bytes", "kv_append", "validate", "version",
-    "KvattnError", "reorder_rows", "reorder_cache", "copy_blocks", "BlockPool",
+    "KvattnError", "reorder_rows", "reorder_cache", "copy_blocks", "stream_read", "BlockPool",
     "F32", "BF16", "FP8_E4M3", "CONTIGUOUS", "PAGED", "BLOCK_TOKENS",
 ]

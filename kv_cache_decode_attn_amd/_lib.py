@@ -21,7 +21,7 @@ EXPORTS = (
     "kvattn_attn_decode", "kvattn_attn_decode_append", "kvattn_attn_decode_append_noalloc",
     "kvattn_attn_decode_multi", "kvattn_attn_prefill",
     "kvattn_validate",
-    "kvattn_reorder_rows", "kvattn_reorder_cache", "kvattn_copy_blocks",
+    "kvattn_reorder_rows", "kvattn_reorder_cache", "kvattn_copy_blocks", "kvattn_stream_read",
     "kvattn_pool_create", "kvattn_pool_destroy", "kvattn_pool_num_blocks", "kvattn_pool_num_free",
     "kvattn_pool_refcount", "kvattn_pool_alloc", "kvattn_pool_retain", "kvattn_pool_release", "kvattn_pool_fork",
     "kvattn_pool_free_seq", "kvattn_pool_prepare_append", "kvattn_pool_reorder",
@@ -82,6 +82,7 @@ _SIGS = {
     "kvattn_reorder_rows": (ctypes.c_int, [_I32, _P, _I32, _P, _P, _I32, _P, _P, _P]),
     "kvattn_reorder_cache": (ctypes.c_int, [_CP, _CP, _I32, _P, _P, _P, _P]),
     "kvattn_copy_blocks": (ctypes.c_int, [_CP, _I32, _P, _P, _P]),
+    "kvattn_stream_read": (ctypes.c_int, [_P, _I64, _P, _P]),
     "kvattn_pool_create": (_P, [_I64]),
     "kvattn_pool_destroy": (None, [_P]),
     "kvattn_pool_num_blocks": (_I64, [_P]),

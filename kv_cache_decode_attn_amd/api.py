@@ -381,6 +381,19 @@ def copy_blocks(cache, src_blocks, dst_blocks):
                                    _ptr(dst_blocks), _stream(cache.device)))
 
 
+def stream_read(x, sink=None):
+    """One plain streaming read of the device tensor x (kvattn_stream_read, a
+    measurement helper): returns sink, an int32 [1] tensor (allocated as 0
+    when None) XORed with the XOR of all 32-bit words of x."""
+    _dev(x, "x")
+    nbytes = x.numel() * x.element_size()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _i32(sink, "sink")
+    check(lib().kvattn_stream_read(_ptr(x), nbytes, _ptr(sink), _stream(x.device)))
+    return sink
+
+
 def _host_i32(a, name, writable=False):
     if not isinstance(a, np.ndarray) or a.dtype != np.int32 or not a.flags.c_contiguous:
         raise TypeError("%s must be a C-contiguous numpy int32 array" % name)

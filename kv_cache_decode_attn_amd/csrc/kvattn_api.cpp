@@ -649,6 +649,26 @@ int kvattn_copy_blocks(const kvattn_cache* cache, int32_t n, const int32_t* src_
   return ok();
 }
 
+int kvattn_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  const char* who = "kvattn_stream_read";
+  if (bytes < 0 || bytes % 16 != 0) return fail(KVATTN_EINVAL, "%s: bytes %lld must be a multiple of 16", who,
+                                                (long long)bytes);
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(KVATTN_EINVAL, "%s: src and sink are required", who);
+  if (!aligned16(src)) return fail(KVATTN_EINVAL, "%s: src not 16-byte aligned", who);
+  if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return fail(KVATTN_EINVAL, "%s: sink not 4-byte aligned", who);
+  // enough workgroups to keep every compute unit's loads in flight: 8 per
+  // unit, fewer for a small buffer (each thread takes at least 4 chunks)
+  const int64_t chunks = bytes / 16;
+  int64_t wgs = (chunks + 256 * 4 - 1) / (256 * 4);
+  const int64_t cap = 8 * compute_units();
+  if (wgs > cap) wgs = cap;
+  kvattn::StreamReadLaunch a{static_cast<const uint8_t*>(src), bytes, sink};
+  int rc = kvattn::launch_stream_read(a, (int32_t)wgs, static_cast<hipStream_t>(stream));
+  if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
+  return ok();
+}
+
 struct kvattn_pool {
   explicit kvattn_pool(int32_t n) : p(n) {}
   kvattn::BlockPool p;

@@ -147,4 +147,13 @@ struct BlockCopyLaunch {
 };
 int launch_copy_blocks(const BlockCopyLaunch& a, hipStream_t stream);
 
+// Streaming read (a measurement helper): the XOR of every 32-bit word of
+// [src, src + bytes) is XORed into *sink; bytes is a multiple of 16.
+struct StreamReadLaunch {
+  const uint8_t* src;
+  int64_t bytes;
+  uint32_t* sink;
+};
+int launch_stream_read(const StreamReadLaunch& a, int32_t workgroups, hipStream_t stream);
+
 }  // namespace kvattn

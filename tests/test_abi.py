@@ -229,3 +229,14 @@ def _decode_multi(c, n_q=4, hq=32, k_new=None, v_new=None, in_dtype=-1, part=0):
 def test_decode_multi_host_errors(kw, want):
     assert _decode_multi(_cache(), **kw) == want
     assert _lib.lib().kvattn_last_error().decode() != ""
+
+
+def test_stream_read_host_errors():
+    L = _lib.lib()
+    assert L.kvattn_stream_read(FAKE, 100, FAKE + 0x1000, None) == _lib.EINVAL       # not a multiple of 16
+    assert L.kvattn_stream_read(FAKE, -16, FAKE + 0x1000, None) == _lib.EINVAL
+    assert L.kvattn_stream_read(None, 64, FAKE + 0x1000, None) == _lib.EINVAL
+    assert L.kvattn_stream_read(FAKE, 64, None, None) == _lib.EINVAL
+    assert L.kvattn_stream_read(FAKE + 8, 64, FAKE + 0x1000, None) == _lib.EINVAL    # src not 16-byte aligned
+    assert L.kvattn_stream_read(FAKE, 64, FAKE + 0x1002, None) == _lib.EINVAL        # sink not 4-byte aligned
+    assert L.kvattn_stream_read(None, 0, None, None) == _lib.OK                     # nothing to read
