@@ -223,21 +223,20 @@ __device__ __forceinline__ s16x4 read_tr16(const uint8_t* lds) {
 #endif
 }
 
-// LDS tile buffers of the kernel: with an fp8 prefix one fewer (seven
-// still hold tiles it - 1 .. it + kAhead), and after them a staging ring of
-// kStage tiles of fp8 codes (per loading wave 512 bytes of K codes, then 512
-// of V).
-constexpr int kStage = kAhead;  // tiles whose transfers can be in flight at once
+// LDS of the kernel: the kBufs tile buffers, then (fp8 prefix) a staging
+// ring of kStage tiles of fp8 codes (per loading wave 512 bytes of K codes,
+// then 512 of V).  Codes wait in it from their transfer until the tile is
+// published: at most tiles it + 2 .. it + kAhead, four (the prologue publishes
+// tile 0 before it issues tile 4).  At d = 128 the two fill the 160 KB.
+constexpr int kStage = kAhead - 1;
 template <int D, bool FP8P>
-constexpr int ring_bufs() { return FP8P ? kBufs - 1 : kBufs; }
-template <int D, bool FP8P>
-constexpr int prefill_lds_bytes() { return ring_bufs<D, FP8P>() * Geo<D>::BUF + (FP8P ? kStage * 2 * kKeys * D : 0); }
+constexpr int prefill_lds_bytes() { return kBufs * Geo<D>::BUF + (FP8P ? kStage * 2 * kKeys * D : 0); }
 
 template <int D, bool CAUSAL, bool MASK, bool PREFIX, bool FP8P>
 __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const PrefillLaunch a, int hw) {
   static_assert(PREFIX || !FP8P, "fp8 rows come only from a cached prefix");
   using GE = Geo<D>;
-  constexpr int NB = ring_bufs<D, FP8P>();  // tile buffers in the ring
+  constexpr int NB = kBufs;                 // tile buffers in the ring
   constexpr int S8 = kKeys * D;             // bytes of one operand's fp8 codes per tile
   constexpr int DK = D / 16;  // 16-wide d chunks of the QK^T contraction
   constexpr int DT = D / 32;  // 32-row d tiles of the output
@@ -300,7 +299,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // workgroup.  Prefix positions outside the cache are masked keys.
   bool prefix_ok = true;
   if (PREFIX && P > 0) {
-    __shared__ int bad;
+    // the flag lives in the first bytes of the tile ring (no static LDS: with
+    // an fp8 prefix the dynamic LDS is the whole 160 KB); a barrier after it
+    // is read keeps the first tile transfers from overwriting it early
+    int& bad = *reinterpret_cast<int*>(smem);
     if (tid == 0) bad = 0;
     __syncthreads();
     const CacheView& cv = a.c;
@@ -318,6 +320,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     }
     __syncthreads();
     prefix_ok = __builtin_amdgcn_readfirstlane(bad) == 0;  // uniform (the loop bounds depend on it)
+    __syncthreads();
   }
   // fp8 prefix: the dequantisation scales of KV head g.  The tile that
   // starts at key P (the first new key) is where the output takes the V
@@ -709,9 +712,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
 
   // prologue: tiles 0 .. kAhead - 1 in flight, tiles 0 and 1 published,
   // scores of tile 0
+  if constexpr (FP8P) {
+    // tile 0 is published (its staged codes expanded) before tile 4 is issued
+    // into the staging slot it used
 #pragma unroll
-  for (int t = 0; t < kAhead; ++t) load_tile(t, t);
-  finish_tile(0, std::integral_constant<int, kAhead - 1>{});
+    for (int t = 0; t < kAhead - 1; ++t) load_tile(t, t);
+    finish_tile(0, std::integral_constant<int, kAhead - 2>{});
+    load_tile(kAhead - 1, kAhead - 2);
+  } else {
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) load_tile(t, t);
+    finish_tile(0, std::integral_constant<int, kAhead - 1>{});
+  }
   finish_tile(1, std::integral_constant<int, kAhead - 2>{});
   __syncthreads();
   f32x16 sA[kCB], sB[kCB];
