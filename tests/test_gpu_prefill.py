@@ -461,3 +461,42 @@ def test_mfma_fp8_prefix_long_many_tiles():
                          block_table=tdev, attend_prefix=True).cpu().numpy()
     want = _oracle(q2, k2, v2, P, n2, prefix=prefix)
     assert max_abs(got, want) <= TOL
+
+
+@pytest.mark.parametrize("cache_dtype", [K.BF16, K.FP8_E4M3])
+def test_prefill_graph_replay_matches_eager(cache_dtype):
+    """A chunked prefill against a cached prefix captured in a HIP graph (for
+    fp8 the graph holds the append kernel and the attention kernel): every
+    replay, with other eager prefills in between, equals the eager call bit
+    for bit, and the cache holds the same bytes."""
+    B, Hq, Hkv, d = 2, 8, 2, 128
+    scales = FP8_SCALES if cache_dtype == K.FP8_E4M3 else None
+    case = _prefix_case(B, Hq, Hkv, d, [77, 130], [100, 37], K.PAGED, 90, cache_dtype=cache_dtype, scales=scales)
+    cache, table, tdev, q2, k2, v2, P, n2, prefix = case
+    q2, k2, v2 = q2.to(DEV), k2.to(DEV), v2.to(DEV)
+    pos = torch.from_numpy(P).to(DEV)
+    ql = torch.from_numpy(n2).to(DEV)
+    want = K.attn_prefill(q2, k2, v2, cache=cache, positions=pos, q_lens=ql, block_table=tdev,
+                          attend_prefix=True).clone()
+    cache_bytes = (cache.k.clone(), cache.v.clone())
+    out = torch.empty_like(want)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        K.attn_prefill(q2, k2, v2, cache=cache, positions=pos, q_lens=ql, block_table=tdev, attend_prefix=True,
+                       out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        K.attn_prefill(q2, k2, v2, cache=cache, positions=pos, q_lens=ql, block_table=tdev, attend_prefix=True,
+                       out=out)
+    other = torch.randn_like(q2)
+    for r in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), r
+        K.attn_prefill(other, k2, v2, causal=False)   # eager work between replays
+        torch.cuda.synchronize()
+    assert torch.equal(cache.k, cache_bytes[0]) and torch.equal(cache.v, cache_bytes[1])
