@@ -344,3 +344,40 @@ def test_graph_replay_matches_eager():
         K.attn_decode(eager_cache, q, lens, c.maxlen, block_table=c.table, workspace=ws, part_tokens=64)
         torch.cuda.synchronize()
     np.testing.assert_array_equal(storage(graph_cache.k), storage(eager_cache.k))
+
+
+def test_decode_maximum_batch_single_partition():
+    """The largest batch the call takes (65,535 sequences, the grid's z
+    extent), lengths 1..16 in one partition each (no merge launch), bf16
+    contiguous cache, GQA 4: 1,024 sampled sequences (incl. the first and the
+    last) against the oracle; every one-key sequence returns its V row
+    exactly (one weight of exactly 1); every output lies within the range of
+    its sequence's V rows (a convex combination; the margin is the parity
+    tolerance: the weights the kernel applies carry about 16 bits, so their
+    sum differs from the normaliser by about 2^-16)."""
+    B, Hq, Hkv, d, cap = 65535, 8, 2, 64, 16
+    G = Hq // Hkv
+    gen = torch.Generator().manual_seed(60)
+    k = torch.randn((B, Hkv, cap, d), generator=gen).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, cap, d), generator=gen).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=gen).to(torch.bfloat16)
+    lens = (1 + np.arange(B) % 16).astype(np.int32)
+    cache = K.KVCache.contiguous(B, Hkv, cap, d, K.BF16, DEV)
+    zeros = torch.zeros(B, dtype=torch.int32, device=DEV)
+    K.kv_append(cache, k.to(DEV), v.to(DEV), zeros, n_valid=torch.from_numpy(lens).to(DEV))
+    out = K.attn_decode(cache, q.to(DEV), torch.from_numpy(lens).to(DEV), cap).cpu().numpy()
+    assert np.isfinite(out).all()
+    vf = v.float().numpy()
+    one = lens == 1
+    np.testing.assert_array_equal(out[one], np.repeat(vf[one, :, 0], G, axis=1))
+    live = np.arange(cap)[None, :] < lens[:, None]                       # [B, cap]
+    vmask = np.where(live[:, None, :, None], vf, np.nan)                  # [B, Hkv, cap, d]
+    lo = np.repeat(np.nanmin(vmask, axis=2), G, axis=1)
+    hi = np.repeat(np.nanmax(vmask, axis=2), G, axis=1)
+    assert (out >= lo - TOL).all() and (out <= hi + TOL).all()
+    picks = sorted({0, B - 1} | set(np.random.default_rng(61).choice(B, size=1022, replace=False).tolist()))
+    kf, vd, qf = f64(k), f64(v), f64(q)
+    scale = 1.0 / math.sqrt(d)
+    for b in picks:
+        want = OA.decode(qf[b:b + 1], [kf[b]], [vd[b]], [int(lens[b])], scale)
+        assert max_abs(out[b:b + 1], want) <= TOL, b
