@@ -38,6 +38,7 @@ import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -75,18 +76,31 @@ def _launch_struct(text, name):
     return text[i:text.index("};", i) + 2]
 
 
+_C_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def _code_only(text):
+    """C/C++ source without comments and with whitespace runs collapsed: a
+    change to the comments does not change the kernels."""
+    return " ".join(_C_COMMENT.sub(" ", text).split())
+
+
 def source_sha(kind, read=None):
-    """Hash of the sources the `kind` kernels ("decode", "prefill") are built from."""
+    """Hash of the sources the `kind` kernels ("decode", "prefill") are built
+    from: the code of the kernel files (comments and layout ignored), the
+    build script, and the launch struct they compile against."""
     if read is None:
         def read(rel):
             with open(os.path.join(ROOT, rel), "rb") as f:
                 return f.read()
     h = hashlib.sha256()
     for item in KERNEL_SOURCES[kind]:
-        if item.endswith((".hip", ".h", ".py")):
+        if item.endswith((".hip", ".h")):
+            h.update(_code_only(read(item).decode()).encode())
+        elif item.endswith(".py"):
             h.update(read(item))
         else:
-            h.update(_launch_struct(read(CSRC + "launch.h").decode(), item).encode())
+            h.update(_code_only(_launch_struct(read(CSRC + "launch.h").decode(), item)).encode())
     return h.hexdigest()
 
 

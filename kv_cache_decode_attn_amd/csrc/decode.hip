@@ -27,7 +27,16 @@
 // Pass 2 (decode_merge): per (sequence, query head), the partials are merged
 // with the exact running max/sum renormalisation of "KV Cache, Flash
 // Attention and Inference Optimization" (factory.pai-world.com), section
-// "Flash Attention", numerical trick.
+// "Flash Attention", numerical trick.  It is not launched when every
+// sequence fits one partition.
+//
+// Pass 1 comes in four forms, chosen by cache type and query columns per KV
+// head (each has its own header below): decode_partition (the three phases
+// above, vector ALU: f32 caches and groups of 1 or 2), decode_partition_bf16_mfma
+// (bf16, 4 or 8 columns: the three phases with both contractions on the
+// matrix cores), decode_partition_bf16_online (bf16, 16 columns: one sweep
+// with a running softmax) and decode_partition_fp8_mfma (fp8, 4 or more
+// columns: one sweep with a running softmax).
 #include <math.h>
 
 #include "launch.h"

@@ -34,6 +34,10 @@ def test_source_hash_follows_every_input_of_the_kernels():
     f = _files()
     f[bench.CSRC + "launch.h"] = f[bench.CSRC + "launch.h"].replace(b"int x;", b"int x, y;")
     assert bench.source_sha("decode", read=_reader(f)) == base
+    # comments and layout do not count
+    f = _files()
+    f[bench.CSRC + "decode.hip"] = b"// a note\ndecode   /* inline */ v1\n"
+    assert bench.source_sha("decode", read=_reader(f)) == base
     # the prefill kernels' hash does not see the decode source
     f = _files()
     f[bench.CSRC + "decode.hip"] += b" changed"
