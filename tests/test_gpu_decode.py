@@ -381,3 +381,17 @@ def test_decode_maximum_batch_single_partition():
     for b in picks:
         want = OA.decode(qf[b:b + 1], [kf[b]], [vd[b]], [int(lens[b])], scale)
         assert max_abs(out[b:b + 1], want) <= TOL, b
+
+
+@pytest.mark.parametrize("dtype,Hq", [(K.BF16, 1), (K.BF16, 2), (K.BF16, 8), (K.BF16, 16), (K.FP8_E4M3, 8),
+                                      (K.F32, 4)])
+def test_mqa_single_kv_head(dtype, Hq):
+    """MQA: one KV head shared by every query head (the vector pass for 1 and
+    2 heads and f32, the matrix-core passes for 8 and 16), against the oracle."""
+    lens = [1, 64, 300, 513]
+    c = Case(4, Hq, 1, 128, lens, dtype=dtype, seed=70 + Hq)
+    got = c.run(128).cpu().numpy()
+    if dtype == K.FP8_E4M3:
+        assert max_abs(got, c.oracle(quantised=True)) <= TOL
+    else:
+        assert max_abs(got, c.oracle()) <= TOL

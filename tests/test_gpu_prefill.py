@@ -500,3 +500,13 @@ def test_prefill_graph_replay_matches_eager(cache_dtype):
         K.attn_prefill(other, k2, v2, causal=False)   # eager work between replays
         torch.cuda.synchronize()
     assert torch.equal(cache.k, cache_bytes[0]) and torch.equal(cache.v, cache_bytes[1])
+
+
+@pytest.mark.parametrize("Hq,d", [(8, 128), (4, 64), (1, 128)])
+def test_prefill_mqa_single_kv_head(Hq, d):
+    """MQA prefill: one KV head for every query head, causal, ragged q_lens."""
+    B, N = 2, 150
+    q, k, v = _inputs(B, Hq, 1, N, d, torch.bfloat16, 95 + Hq, std=1 / math.sqrt(d))
+    q_lens = np.array([150, 61], np.int32)
+    got = K.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), q_lens=torch.from_numpy(q_lens).to(DEV)).cpu().numpy()
+    assert max_abs(got, _oracle(q, k, v, [0, 0], q_lens)) <= TOL
