@@ -104,11 +104,10 @@ def source_sha(kind, read=None):
     return h.hexdigest()
 
 
-def traffic(workload):
-    """HBM bytes per launch of the workload's dominant call measured with
-    rocprofv3 FETCH_SIZE / WRITE_SIZE counters and scaled by the copy-kernel
-    calibration (profiles/traffic.json), or None when that measurement was
-    taken on different kernel sources."""
+def _stored(workload):
+    """The workload's entry of profiles/traffic.json (rocprofv3 figures of
+    its dominant call), or None when they were measured on different kernel
+    sources or are missing."""
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             d = json.load(f)["workloads"][workload]
@@ -116,7 +115,31 @@ def traffic(workload):
         return None
     if d.get("source_sha256") != source_sha(WORKLOAD_KERNELS[workload]):
         return None
-    return d.get("bytes_per_launch")
+    return d
+
+
+def traffic(workload):
+    """HBM bytes per launch of the workload's dominant call measured with
+    rocprofv3 FETCH_SIZE / WRITE_SIZE counters and scaled by the copy-kernel
+    calibration (profiles/traffic.json), or None (see _stored)."""
+    d = _stored(workload)
+    return None if d is None else d.get("bytes_per_launch")
+
+
+def kernel_times(workload, work, peak, unit):
+    """The same call at the rocprofv3 kernel-trace averages of its kernels
+    (partition pass and merge, or the prefill kernel), stored beside the
+    traffic figures: {"kernel_avg_us", "us_per_call", "achieved", "frac"}
+    for `work` algorithmic bytes (GB/s) or FLOPs (TFLOP/s) per call, or None
+    (see _stored)."""
+    d = _stored(workload)
+    if d is None or not d.get("kernel_avg_us"):
+        return None
+    us = float(sum(d["kernel_avg_us"].values()))
+    scale = 1e9 if unit == "GB/s" else 1e12
+    achieved = work / (us * 1e-6) / scale
+    return {"kernel_avg_us": d["kernel_avg_us"], "us_per_call": us, "achieved": achieved, "frac": achieved / peak,
+            "unit": unit, "source": "rocprofv3 kernel trace, profiles/kernels_per_workload.md"}
 
 
 def _events(n):
@@ -841,7 +864,8 @@ def run_leg(name, args, cpu):
                "roofline": {"bound": "hbm", "kernel": "attn_decode_append per layer (decode_partition vector pass "
                             "with the key mask and fused append, then decode_merge)",
                             "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                            "bytes_per_launch": p.layer_bytes(), "traffic": traffic("padded32")}}
+                            "bytes_per_launch": p.layer_bytes(), "traffic": traffic("padded32"),
+                            "rocprof": kernel_times("padded32", p.layer_bytes(), HBM_PEAK_GBS, "GB/s")}}
         if cpu:
             rec["cpu_baseline"], rec["parity_max_abs_err_vs_oracle"] = p.cpu_baseline()
         return rec
@@ -855,7 +879,8 @@ def run_leg(name, args, cpu):
                "roofline": {"bound": "hbm", "kernel": "attn_decode_append per layer (decode_partition_fp8_mfma "
                             "with the fused append, then decode_merge)",
                             "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                            "bytes_per_launch": lw.step_bytes() // lw.L, "traffic": traffic("longctx70b")}}
+                            "bytes_per_launch": lw.step_bytes() // lw.L, "traffic": traffic("longctx70b"),
+                            "rocprof": kernel_times("longctx70b", lw.step_bytes() // lw.L, HBM_PEAK_GBS, "GB/s")}}
         if cpu:
             rec["cpu_baseline"], rec["parity_max_abs_err_vs_quantised_oracle"] = lw.cpu_baseline()
         return rec
@@ -869,7 +894,8 @@ def run_leg(name, args, cpu):
                 "roofline": {"bound": "hbm", "kernel": "attn_decode_append with 4 queries per sequence "
                              "(decode_partition_bf16_online with the fused append, then decode_merge)",
                              "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                             "bytes_per_launch": vw.step_bytes(), "traffic": traffic("verify8b")}}
+                             "bytes_per_launch": vw.step_bytes(), "traffic": traffic("verify8b"),
+                             "rocprof": kernel_times("verify8b", vw.step_bytes(), HBM_PEAK_GBS, "GB/s")}}
     if name == "prefill8k":
         pf = CausalPrefill()
         # the first calls run below the steady-state rate (clocks ramp under sustained
@@ -881,7 +907,8 @@ def run_leg(name, args, cpu):
                "flops": pf.flops(),
                "roofline": {"bound": "mfma", "kernel": "attn_prefill (prefill_mfma_kernel, which also writes the cache)",
                             "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
-                            "traffic": traffic("prefill8k")}}
+                            "traffic": traffic("prefill8k"),
+                            "rocprof": kernel_times("prefill8k", pf.flops(), BF16_PEAK_TFLOPS, "TFLOP/s")}}
         if cpu:
             rec["cpu_baseline"], rec["parity_max_abs_err_vs_oracle"] = pf.cpu_baseline()
         return rec
@@ -1001,7 +1028,8 @@ def main(argv=None):
                      "kernel": "attn_decode_append (decode_partition_bf16_mfma with the fused append, "
                                "then decode_merge)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "bytes_per_launch": step_bytes, "traffic": traffic("decode8b")},
+                     "bytes_per_launch": step_bytes, "traffic": traffic("decode8b"),
+                     "rocprof": kernel_times("decode8b", step_bytes, HBM_PEAK_GBS, "GB/s")},
     }
     if cpu:
         base, err = w.cpu_baseline()

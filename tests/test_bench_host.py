@@ -68,3 +68,16 @@ def test_every_leg_is_known():
                         "chunkprefill_fp8", "cowcopy", "beamreorder", "stream")
     with pytest.raises(ValueError):
         bench.run_leg("no-such-leg", None, False)
+
+
+def test_kernel_times_are_stored_figures_of_the_same_sources(monkeypatch):
+    with open(os.path.join(bench.ROOT, "profiles", "traffic.json")) as fh:
+        entry = json.load(fh)["workloads"]["decode8b"]
+    monkeypatch.setattr(bench, "source_sha", lambda k, read=None: entry["source_sha256"])
+    rec = bench.kernel_times("decode8b", 1e9, bench.HBM_PEAK_GBS, "GB/s")
+    us = sum(entry["kernel_avg_us"].values())
+    assert rec["us_per_call"] == pytest.approx(us)
+    assert rec["achieved"] == pytest.approx(1.0 / (us * 1e-6))          # 1e9 bytes per call, in GB/s
+    assert rec["frac"] == pytest.approx(rec["achieved"] / bench.HBM_PEAK_GBS)
+    monkeypatch.setattr(bench, "source_sha", lambda k, read=None: "0" * 64)
+    assert bench.kernel_times("decode8b", 1e9, bench.HBM_PEAK_GBS, "GB/s") is None
