@@ -167,8 +167,11 @@ constexpr int kDppRowRor8 = 0x128;
 // for the cross-wave output reduction [kWaves][G][D]), then (max, sum) per
 // head.
 __host__ __device__ constexpr int decode_off_floats(int T) { return 2 * (T / kBlockTokens); }
+// Row stride (floats) of the cross-wave reduction [wave][head][d]: D + 4, so
+// the 16-byte writes of 8 consecutive heads' rows fall on distinct LDS banks.
+__host__ __device__ constexpr int red_stride(int D) { return D + 4; }
 __host__ __device__ constexpr int decode_lds_floats(int T, int G, int D) {
-  return decode_off_floats(T) + ((T * G > kWaves * G * D) ? T * G : kWaves * G * D) + 2 * G;
+  return decode_off_floats(T) + ((T * G > kWaves * G * red_stride(D)) ? T * G : kWaves * G * red_stride(D)) + 2 * G;
 }
 // Fused append: the new tokens' K and V rows (k_new/v_new [batch,
 // num_kv_heads, n_tail, head_dim]) go to positions seq_lens[b] - n_tail ..
@@ -811,30 +814,41 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
   stream_ring(wave, nblk, vring, load_v, accumulate);
 
   __syncthreads();  // every wave is done reading weights; reuse LDS
-  float* red = s_lds;  // [kWaves][G][D]
+  constexpr int RS = red_stride(D);
+  float* red = s_lds;  // [kWaves][G][RS]
+  // lane (r16, lg) holds d = 64 hf + 4 (4 lg + rr) + j of head r16 in o[4 hf + j][rr]
   if (r16 < G) {
+    float* row = red + (wave * G + r16) * RS;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int hf = t / 4, j = t % 4;
+    for (int hf = 0; hf < HALVES; ++hf)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) red[(wave * G + r16) * D + 64 * hf + 4 * (4 * lg + rr) + j] = o[t][rr];
-    }
+      for (int rr = 0; rr < 4; ++rr)
+        *reinterpret_cast<float4*>(row + 64 * hf + 4 * (4 * lg + rr)) =
+            make_float4(o[4 * hf][rr], o[4 * hf + 1][rr], o[4 * hf + 2][rr], o[4 * hf + 3][rr]);
   }
   __syncthreads();
 
   const int nparts_b = (ctx + T - 1) / T;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx - h * D;
-    float acc = red[(0 * G + h) * D + d];
+  for (int idx = tid; idx < G * D / 4; idx += 256) {
+    const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
+    float4 acc = *reinterpret_cast<const float4*>(red + h * RS + d);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) acc += red[(w * G + h) * D + d];
+    for (int w = 1; w < kWaves; ++w) {
+      const float4 x = *reinterpret_cast<const float4*>(red + (w * G + h) * RS + d);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
     const int hq = hq0 + h;
     const float l = stat[2 * h + 1];
     if (nparts_b == 1) {
-      p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = (l > 0.f) ? acc / l : 0.f;
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      *reinterpret_cast<float4*>(p.out + ((int64_t)b * p.num_q_heads + hq) * D + d) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     } else {
       const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.num_parts + part;
-      p.ws_o[slot * D + d] = acc;
+      *reinterpret_cast<float4*>(p.ws_o + slot * D + d) = acc;
       if (d == 0) {
         p.ws_ml[slot * 2] = stat[2 * h];
         p.ws_ml[slot * 2 + 1] = l;
@@ -885,8 +899,8 @@ __host__ __device__ constexpr int bf16_online_area_offset(int T, int G, bool mas
 }
 __host__ __device__ constexpr int bf16_online_lds_bytes(int T, int G, int D, bool mask) {
   // two K slots per wave of one 16-token block of bf16 rows (2 D bytes each)
-  return bf16_online_area_offset(T, G, mask) + (kWaves * G * D * 4 > kWaves * 2 * kBlockTokens * 2 * D
-                                                    ? kWaves * G * D * 4
+  return bf16_online_area_offset(T, G, mask) + (kWaves * G * red_stride(D) * 4 > kWaves * 2 * kBlockTokens * 2 * D
+                                                    ? kWaves * G * red_stride(D) * 4
                                                     : kWaves * 2 * kBlockTokens * 2 * D);
 }
 
@@ -1084,38 +1098,33 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
     }
   };
 
-  // The wave's blocks jb = wave + kWaves i stream through the V register ring
-  // (stream_ring); K goes through the wave's two slots two blocks ahead, with
-  // transfers the compiler does not count (the waits below are the only ones
-  // on them).  Issue order: V of the first kRingBf16 - 1 blocks, K of the
-  // first two; then each step issues V of the block kRingBf16 - 1 places
-  // ahead and, inside the body, once the slot is read out, K of the block two
-  // places ahead into it.  So when block i's K transfer must have landed, the
-  // loads issued after it are: V of block i + 1 (issued a step earlier, when
-  // kRingBf16 = 3), K of block i + 1 and V of block i + kRingBf16 - 1 -
-  // whichever exist - and the load-count wait releases exactly the transfer.
-  static_assert(kRingBf16 == 3, "wait accounting below");
+  // The wave's blocks jb = wave + kWaves i stream one block ahead: V through
+  // a two-set register ring (stream_ring), K through the wave's two LDS
+  // slots with transfers the compiler does not count (the waits below are
+  // the only ones on them).  V of block i + 1 is issued before block i's
+  // body, K of block i + 1 (into the other slot, read out in the previous
+  // body) at the start of the body, so the loads issued after K of block i
+  // are V and K of block i + 1, if it exists, and the load-count wait
+  // releases exactly block i.  With the whole device streaming, more blocks
+  // in flight per wave only lengthen every load's wait: each workgroup takes
+  // longer to start and to finish for the same bandwidth, and the grid's
+  // last workgroups, which run with the device half idle, finish later.
   constexpr int VL = 4 * HALVES;     // V loads per block
   constexpr int KL = KST::XFERS;     // K transfers per block
-  uint2 vring[kRingBf16][HALVES][4];
+  uint2 vring[2][HALVES][4];
   auto body = [&](int jb, const uint2 (*vr)[4]) {
-    const bool b1 = jb + kWaves < nblk, b2 = jb + 2 * kWaves < nblk;
-    // after K of block jb: V of jb + 1 and K of jb + 1 (if jb + 1 exists; V of
-    // jb + 1 was issued before K of jb only for the first block), V of jb + 2
-    const bool first = jb < kWaves;
-    const int after = (b1 ? (first ? 0 : VL) + KL : 0) + (b2 ? VL : 0);
-    wait_vm_dyn(after);
+    const bool b1 = jb + kWaves < nblk;
+    if (b1) issue_k(jb + kWaves);
+    wait_vm_dyn(b1 ? VL + KL : 0);
     const uint8_t* slot = kslots + ((jb / kWaves) & 1) * KST::BYTES;
     U4 kr[KC];
 #pragma unroll
     for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const U4*>(slot + kat[c]);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot is read out before its next transfer
-    if (b2) issue_k(jb + 2 * kWaves);
     process(jb, kr, vr);
   };
   ring_fill(wave, nblk, vring, load_v);
   if (wave < nblk) issue_k(wave);
-  if (wave + kWaves < nblk) issue_k(wave + kWaves);
   stream_ring(wave, nblk, vring, load_v, body);
   __syncthreads();  // every wave is done with its K slots: the area becomes the reduction
 
@@ -1130,34 +1139,47 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
   float M = -INFINITY;
   if (r16 < G)
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wstat[(w * G + r16) * 2]);
-  const float mine = (mrun == -INFINITY || M == -INFINITY) ? 0.f : exp2f(mrun - M);
+  const float mine = (mrun == -INFINITY || M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - M);
+  constexpr int RS = red_stride(D);
+  // lane (r16, lg) holds d = 64 hf + 4 (4 lg + rr) + j of head r16 in o[4 hf + j][rr]
   if (r16 < G) {
+    float* row = red + (wave * G + r16) * RS;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int hf = t / 4, j = t % 4;
+    for (int hf = 0; hf < HALVES; ++hf)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) red[(wave * G + r16) * D + 64 * hf + 4 * (4 * lg + rr) + j] = o[t][rr] * mine;
-    }
+      for (int rr = 0; rr < 4; ++rr)
+        *reinterpret_cast<float4*>(row + 64 * hf + 4 * (4 * lg + rr)) =
+            make_float4(o[4 * hf][rr] * mine, o[4 * hf + 1][rr] * mine, o[4 * hf + 2][rr] * mine,
+                        o[4 * hf + 3][rr] * mine);
   }
   __syncthreads();
   const int nparts_b = (ctx + T - 1) / T;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx - h * D;
+  for (int idx = tid; idx < G * D / 4; idx += 256) {
+    const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
     float Mh = -INFINITY;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) Mh = fmaxf(Mh, wstat[(w * G + h) * 2]);
-    float acc = 0.f, L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = wstat[(w * G + h) * 2];
-      const float sw = (mw == -INFINITY) ? 0.f : exp2f(mw - Mh);
+      const float sw = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mh);
       L = fmaf(sw, wstat[(w * G + h) * 2 + 1], L);
-      acc += red[(w * G + h) * D + d];
+      const float4 x = *reinterpret_cast<const float4*>(red + (w * G + h) * RS + d);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
     }
     const int hq = hq0 + h;
     if (nparts_b == 1) {
-      p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = (L > 0.f) ? acc / L : 0.f;
+      const float inv = (L > 0.f) ? 1.f / L : 0.f;
+      *reinterpret_cast<float4*>(p.out + ((int64_t)b * p.num_q_heads + hq) * D + d) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     } else {
       const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.num_parts + part;
-      p.ws_o[slot * D + d] = acc;
+      *reinterpret_cast<float4*>(p.ws_o + slot * D + d) = acc;
       if (d == 0) {
         p.ws_ml[slot * 2] = Mh;
         p.ws_ml[slot * 2 + 1] = L;
@@ -1221,8 +1243,9 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
   const int j0 = t0 / kBlockTokens;
 
   int64_t* offs = reinterpret_cast<int64_t*>(lds);
-  float* red = lds + decode_off_floats(T);  // [kWaves][G][D] outputs, then [kWaves][G][2]
-  float* wstat = red + kWaves * G * D;
+  float* red = lds + decode_off_floats(T);  // [kWaves][G][kRedStride] outputs, then [kWaves][G][2]
+  constexpr int RS = red_stride(D);
+  float* wstat = red + kWaves * G * RS;
   uint8_t* mflag = reinterpret_cast<uint8_t*>(wstat + kWaves * G * 2);  // [T] mask (MASK only)
   for (int i = tid; i < nblk; i += 256) offs[i] = block_offset(p.c, b, g, j0 + i);
   if constexpr (MASK) {
@@ -1433,34 +1456,51 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
   float M = -INFINITY;
   if (r16 < G)
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wstat[(w * G + r16) * 2]);
-  const float mine = (mrun == -INFINITY || M == -INFINITY) ? 0.f : exp2f(mrun - M);
+  const float mine = (mrun == -INFINITY || M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - M);
+  // lane (r16, lg) holds d = VB (4 lg + rr) + t of head r16: 16-byte writes
+  // of t = 4c .. 4c + 3
   if (r16 < G) {
+    float* row = red + (wave * G + r16) * RS;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) red[(wave * G + r16) * D + VB * (4 * lg + rr) + t] = o[t][rr] * mine;
+      for (int c = 0; c < NT / 4; ++c)
+        *reinterpret_cast<float4*>(row + VB * (4 * lg + rr) + 4 * c) =
+            make_float4(o[4 * c][rr] * mine, o[4 * c + 1][rr] * mine, o[4 * c + 2][rr] * mine, o[4 * c + 3][rr] * mine);
   }
   __syncthreads();
   const int nparts_b = (ctx + T - 1) / T;
   const float vscale = p.v_scale[g];
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx - h * D;
+  for (int idx = tid; idx < G * D / 4; idx += 256) {
+    const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
     float Mh = -INFINITY;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) Mh = fmaxf(Mh, wstat[(w * G + h) * 2]);
-    float acc = 0.f, L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = wstat[(w * G + h) * 2];
-      const float sw = (mw == -INFINITY) ? 0.f : exp2f(mw - Mh);
+      const float sw = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mh);
       L = fmaf(sw, wstat[(w * G + h) * 2 + 1], L);
-      acc += red[(w * G + h) * D + d];
+      const float4 x = *reinterpret_cast<const float4*>(red + (w * G + h) * RS + d);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
     }
-    acc *= vscale;
+    acc.x *= vscale;
+    acc.y *= vscale;
+    acc.z *= vscale;
+    acc.w *= vscale;
     const int hq = hq0 + h;
     if (nparts_b == 1) {
-      p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = (L > 0.f) ? acc / L : 0.f;
+      const float inv = (L > 0.f) ? 1.f / L : 0.f;
+      *reinterpret_cast<float4*>(p.out + ((int64_t)b * p.num_q_heads + hq) * D + d) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     } else {
       const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.num_parts + part;
-      p.ws_o[slot * D + d] = acc;
+      *reinterpret_cast<float4*>(p.ws_o + slot * D + d) = acc;
       if (d == 0) {
         p.ws_ml[slot * 2] = Mh;
         p.ws_ml[slot * 2 + 1] = L;
@@ -1575,7 +1615,7 @@ template <int KVT, int D, int G, bool MASK, bool TAIL>
 int launch_typed(const DecodeLaunch& a, hipStream_t s) {
   const dim3 grid(a.num_kv_heads, a.num_parts, a.batch);
   if constexpr (KVT == KVATTN_FP8_E4M3 && G >= 4) {
-    const size_t lds = (size_t)(decode_off_floats(a.part_tokens) + kWaves * G * D + kWaves * G * 2 +
+    const size_t lds = (size_t)(decode_off_floats(a.part_tokens) + kWaves * G * red_stride(D) + kWaves * G * 2 +
                                 (MASK ? a.part_tokens / 4 : 0)) * sizeof(float);
     hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
   } else if constexpr (KVT == KVATTN_BF16 && G >= KVATTN_BF16_ONLINE_MIN_G) {
