@@ -1135,13 +1135,9 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
     wstat[(wave * G + r16) * 2] = mrun;
     wstat[(wave * G + r16) * 2 + 1] = lsum;
   }
-  __syncthreads();
-  float M = -INFINITY;
-  if (r16 < G)
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wstat[(w * G + r16) * 2]);
-  const float mine = (mrun == -INFINITY || M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - M);
   constexpr int RS = red_stride(D);
-  // lane (r16, lg) holds d = 64 hf + 4 (4 lg + rr) + j of head r16 in o[4 hf + j][rr]
+  // lane (r16, lg) holds d = 64 hf + 4 (4 lg + rr) + j of head r16 in
+  // o[4 hf + j][rr] (each wave's own scale is applied when combining)
   if (r16 < G) {
     float* row = red + (wave * G + r16) * RS;
 #pragma unroll
@@ -1149,8 +1145,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         *reinterpret_cast<float4*>(row + 64 * hf + 4 * (4 * lg + rr)) =
-            make_float4(o[4 * hf][rr] * mine, o[4 * hf + 1][rr] * mine, o[4 * hf + 2][rr] * mine,
-                        o[4 * hf + 3][rr] * mine);
+            make_float4(o[4 * hf][rr], o[4 * hf + 1][rr], o[4 * hf + 2][rr], o[4 * hf + 3][rr]);
   }
   __syncthreads();
   const int nparts_b = (ctx + T - 1) / T;
@@ -1167,10 +1162,10 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
       const float sw = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mh);
       L = fmaf(sw, wstat[(w * G + h) * 2 + 1], L);
       const float4 x = *reinterpret_cast<const float4*>(red + (w * G + h) * RS + d);
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+      acc.x = fmaf(sw, x.x, acc.x);
+      acc.y = fmaf(sw, x.y, acc.y);
+      acc.z = fmaf(sw, x.z, acc.z);
+      acc.w = fmaf(sw, x.w, acc.w);
     }
     const int hq = hq0 + h;
     if (nparts_b == 1) {
@@ -1452,13 +1447,8 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
     wstat[(wave * G + r16) * 2] = mrun;
     wstat[(wave * G + r16) * 2 + 1] = lsum;
   }
-  __syncthreads();
-  float M = -INFINITY;
-  if (r16 < G)
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wstat[(w * G + r16) * 2]);
-  const float mine = (mrun == -INFINITY || M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - M);
   // lane (r16, lg) holds d = VB (4 lg + rr) + t of head r16: 16-byte writes
-  // of t = 4c .. 4c + 3
+  // of t = 4c .. 4c + 3 (each wave's own scale is applied when combining)
   if (r16 < G) {
     float* row = red + (wave * G + r16) * RS;
 #pragma unroll
@@ -1466,7 +1456,7 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
 #pragma unroll
       for (int c = 0; c < NT / 4; ++c)
         *reinterpret_cast<float4*>(row + VB * (4 * lg + rr) + 4 * c) =
-            make_float4(o[4 * c][rr] * mine, o[4 * c + 1][rr] * mine, o[4 * c + 2][rr] * mine, o[4 * c + 3][rr] * mine);
+            make_float4(o[4 * c][rr], o[4 * c + 1][rr], o[4 * c + 2][rr], o[4 * c + 3][rr]);
   }
   __syncthreads();
   const int nparts_b = (ctx + T - 1) / T;
@@ -1484,10 +1474,10 @@ __global__ void __launch_bounds__(256) decode_partition_fp8_mfma(const DecodeLau
       const float sw = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mh);
       L = fmaf(sw, wstat[(w * G + h) * 2 + 1], L);
       const float4 x = *reinterpret_cast<const float4*>(red + (w * G + h) * RS + d);
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+      acc.x = fmaf(sw, x.x, acc.x);
+      acc.y = fmaf(sw, x.y, acc.y);
+      acc.z = fmaf(sw, x.z, acc.z);
+      acc.w = fmaf(sw, x.w, acc.w);
     }
     acc.x *= vscale;
     acc.y *= vscale;
