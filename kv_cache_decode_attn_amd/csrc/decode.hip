@@ -537,30 +537,44 @@ __global__ void __launch_bounds__(256) decode_partition(const DecodeLaunch p) {
 
   __syncthreads();  // every wave is done reading weights; reuse LDS
   float* red = s_lds;  // [kWaves][G][D]
+  static_assert(EPL % 4 == 0, "16-byte reduction writes");
   if (row == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) red[(wave * G + h) * D + col * EPL + e] = o[h][e];
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(red + (wave * G + h) * D + col * EPL + e) =
+            make_float4(o[h][e], o[h][e + 1], o[h][e + 2], o[h][e + 3]);
   }
   __syncthreads();
 
   const int nparts_b = (ctx + T - 1) / T;
   float vscale = 1.f;
   if constexpr (KVT == KVATTN_FP8_E4M3) vscale = p.v_scale[g];
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx - h * D;
-    float acc = red[(0 * G + h) * D + d];
+  for (int idx = tid; idx < G * D / 4; idx += 256) {
+    const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
+    float4 acc = *reinterpret_cast<const float4*>(red + h * D + d);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) acc += red[(w * G + h) * D + d];
-    acc *= vscale;
+    for (int w = 1; w < kWaves; ++w) {
+      const float4 x = *reinterpret_cast<const float4*>(red + (w * G + h) * D + d);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    acc.x *= vscale;
+    acc.y *= vscale;
+    acc.z *= vscale;
+    acc.w *= vscale;
     const int hq = hq0 + h;
     const float l = stat[2 * h + 1];
     if (nparts_b == 1) {
-      p.out[((int64_t)b * p.num_q_heads + hq) * D + d] = (l > 0.f) ? acc / l : 0.f;
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      *reinterpret_cast<float4*>(p.out + ((int64_t)b * p.num_q_heads + hq) * D + d) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     } else {
       const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.num_parts + part;
-      p.ws_o[slot * D + d] = acc;
+      *reinterpret_cast<float4*>(p.ws_o + slot * D + d) = acc;
       if (d == 0) {
         p.ws_ml[slot * 2] = stat[2 * h];
         p.ws_ml[slot * 2 + 1] = l;
