@@ -35,8 +35,8 @@
 // above, vector ALU: f32 caches and groups of 1 or 2), decode_partition_bf16_mfma
 // (bf16, 4 or 8 columns: the three phases with both contractions on the
 // matrix cores), decode_partition_bf16_online (bf16, 16 columns: one sweep
-// with a running softmax) and decode_partition_fp8_mfma (fp8, 4 or more
-// columns: one sweep with a running softmax).
+// with a running softmax, 8 waves per workgroup) and decode_partition_fp8_mfma
+// (fp8, 4 or more columns: one sweep with a running softmax).
 #include <math.h>
 
 #include "launch.h"
@@ -241,29 +241,29 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 // load-count waits release exactly the block about to be consumed; the
 // scheduling barriers keep each prefetch ahead of the wait for the block
 // before it.  The last 2 NB - 2 blocks form an explicit tail.
-template <int NB, typename Buf, typename LoadF>
+template <int NB, typename Buf, typename LoadF, int STEP = kWaves>
 __device__ __forceinline__ void ring_fill(int jb, int nblk, Buf (&r)[NB], const LoadF& load) {
 #pragma unroll
   for (int i = 0; i < NB - 1; ++i)
-    if (jb + i * kWaves < nblk) load(jb + i * kWaves, r[i]);
+    if (jb + i * STEP < nblk) load(jb + i * STEP, r[i]);
 }
 
-template <int NB, typename Buf, typename LoadF, typename BodyF>
+template <int NB, typename Buf, typename LoadF, typename BodyF, int STEP = kWaves>
 __device__ __forceinline__ void stream_ring(int jb, int nblk, Buf (&r)[NB], const LoadF& load, const BodyF& body) {
   static_assert(NB >= 2, "ring");
-  for (; jb + (2 * NB - 2) * kWaves < nblk; jb += NB * kWaves) {
+  for (; jb + (2 * NB - 2) * STEP < nblk; jb += NB * STEP) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      load(jb + (i + NB - 1) * kWaves, r[(i + NB - 1) % NB]);
+      load(jb + (i + NB - 1) * STEP, r[(i + NB - 1) % NB]);
       __builtin_amdgcn_sched_barrier(0);
-      body(jb + i * kWaves, r[i]);
+      body(jb + i * STEP, r[i]);
     }
   }
 #pragma unroll
   for (int i = 0; i < 2 * NB - 2; ++i) {
-    if (i <= NB - 2 && jb + (i + NB - 1) * kWaves < nblk) load(jb + (i + NB - 1) * kWaves, r[(i + NB - 1) % NB]);
+    if (i <= NB - 2 && jb + (i + NB - 1) * STEP < nblk) load(jb + (i + NB - 1) * STEP, r[(i + NB - 1) % NB]);
     __builtin_amdgcn_sched_barrier(0);
-    if (jb + i * kWaves < nblk) body(jb + i * kWaves, r[i % NB]);
+    if (jb + i * STEP < nblk) body(jb + i * STEP, r[i % NB]);
   }
 }
 
@@ -885,7 +885,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_mfma(const DecodeLa
 //   lazily raised running max (as in decode_partition_fp8_mfma), weights
 //   exp2(z - m) split into bf16 hi + lo, then O^T += V^T P^T with V^T built
 //   by 16-bit v_perm_b32 transposes of the lane's own V loads.
-// Each wave keeps its own (max, sum, O) over its blocks; the four waves are
+// Each wave keeps its own (max, sum, O) over its blocks; the waves are
 // combined through LDS.
 // s_waitcnt vmcnt(n) for a count known only at run time (0 <= n <= 31).
 __device__ __forceinline__ void wait_vm_dyn(int n) {
@@ -904,22 +904,30 @@ __device__ __forceinline__ void wait_vm_dyn(int n) {
   }
 }
 
+// Waves per workgroup of decode_partition_bf16_online: eight, two per SIMD,
+// so a workgroup gets through its partition in half the time of four waves
+// and the grid's last workgroups finish sooner, for the same partials.
+#ifndef KVATTN_ONLINE_WAVES
+#define KVATTN_ONLINE_WAVES 8
+#endif
+constexpr int kOnlineWaves = KVATTN_ONLINE_WAVES;
+
 // LDS of decode_partition_bf16_online: block offsets, (max, sum) per wave and
 // head, the key mask flags (MASK), then one area that holds the waves' K
 // slots (two per wave) during the sweep and the cross-wave reduction
-// [kWaves][G][D] afterwards.
+// [kOnlineWaves][G][D] afterwards.
 __host__ __device__ constexpr int bf16_online_area_offset(int T, int G, bool mask) {
-  return kslot_offset(decode_off_floats(T) + kWaves * G * 2 + (mask ? T / 4 : 0));
+  return kslot_offset(decode_off_floats(T) + kOnlineWaves * G * 2 + (mask ? T / 4 : 0));
 }
 __host__ __device__ constexpr int bf16_online_lds_bytes(int T, int G, int D, bool mask) {
   // two K slots per wave of one 16-token block of bf16 rows (2 D bytes each)
-  return bf16_online_area_offset(T, G, mask) + (kWaves * G * red_stride(D) * 4 > kWaves * 2 * kBlockTokens * 2 * D
-                                                    ? kWaves * G * red_stride(D) * 4
-                                                    : kWaves * 2 * kBlockTokens * 2 * D);
+  return bf16_online_area_offset(T, G, mask) + (kOnlineWaves * G * red_stride(D) * 4 > kOnlineWaves * 2 * kBlockTokens * 2 * D
+                                                    ? kOnlineWaves * G * red_stride(D) * 4
+                                                    : kOnlineWaves * 2 * kBlockTokens * 2 * D);
 }
 
 template <int D, int G, bool MASK, bool TAIL>
-__global__ void __launch_bounds__(256) decode_partition_bf16_online(const DecodeLaunch p) {
+__global__ void __launch_bounds__(kOnlineWaves * kWave) decode_partition_bf16_online(const DecodeLaunch p) {
   typedef short v4s __attribute__((ext_vector_type(4)));
   typedef float v4f __attribute__((ext_vector_type(4)));
   typedef unsigned v2u __attribute__((ext_vector_type(2)));
@@ -941,7 +949,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
   const int t0 = part * T;
   if (t0 >= ctx) {
     if (part == 0)
-      for (int i = tid; i < G * D; i += 256) p.out[((int64_t)b * p.num_q_heads + hq0) * D + i] = 0.f;
+      for (int i = tid; i < G * D; i += kOnlineWaves * kWave) p.out[((int64_t)b * p.num_q_heads + hq0) * D + i] = 0.f;
     return;
   }
   const int t1 = min(t0 + T, ctx);
@@ -950,15 +958,15 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
   const int j0 = t0 / kBlockTokens;
 
   int64_t* offs = reinterpret_cast<int64_t*>(lds);
-  float* wstat = lds + decode_off_floats(T);                            // [kWaves][G][2]
-  uint8_t* mflag = reinterpret_cast<uint8_t*>(wstat + kWaves * G * 2);  // [T] mask (MASK only)
-  // the K slots during the sweep, then the cross-wave reduction [kWaves][G][D]
+  float* wstat = lds + decode_off_floats(T);                            // [kOnlineWaves][G][2]
+  uint8_t* mflag = reinterpret_cast<uint8_t*>(wstat + kOnlineWaves * G * 2);  // [T] mask (MASK only)
+  // the K slots during the sweep, then the cross-wave reduction [kOnlineWaves][G][D]
   uint8_t* area = reinterpret_cast<uint8_t*>(lds) + bf16_online_area_offset(T, G, MASK);
   float* red = reinterpret_cast<float*>(area);
-  for (int i = tid; i < nblk; i += 256) offs[i] = block_offset(p.c, b, g, j0 + i);
+  for (int i = tid; i < nblk; i += kOnlineWaves * kWave) offs[i] = block_offset(p.c, b, g, j0 + i);
   if constexpr (MASK) {
     const uint8_t* mask_row = p.key_mask + (int64_t)b * p.key_mask_stride + t0;
-    for (int t = tid; t < n; t += 256) mflag[t] = mask_row[t];
+    for (int t = tid; t < n; t += kOnlineWaves * kWave) mflag[t] = mask_row[t];
   }
   // fused append (as in decode_partition)
   if (p.k_new != nullptr && p.seq_lens[b] == ctx) {
@@ -1002,10 +1010,10 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
   for (int x = 0; x < KST::XFERS; ++x) ksrc[x] = KST::src(x, lane);
 #pragma unroll
   for (int c = 0; c < KC; ++c) kat[c] = KST::at(r16, 4 * c + lg);
-  // block jb goes to slot (jb / kWaves) % 2
+  // block jb goes to slot (jb / kOnlineWaves) % 2
   auto issue_k = [&](int jb) {
     const uint8_t* blk = p.c.k + load_off(jb);
-    uint8_t* slot = kslots + ((jb / kWaves) & 1) * KST::BYTES;
+    uint8_t* slot = kslots + ((jb / kOnlineWaves) & 1) * KST::BYTES;
 #pragma unroll
     for (int x = 0; x < KST::XFERS; ++x) copy16_to_lds_async(blk + ksrc[x], slot + x * 1024);
   };
@@ -1112,7 +1120,7 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
     }
   };
 
-  // The wave's blocks jb = wave + kWaves i stream one block ahead: V through
+  // The wave's blocks jb = wave + kOnlineWaves i stream one block ahead: V through
   // a two-set register ring (stream_ring), K through the wave's two LDS
   // slots with transfers the compiler does not count (the waits below are
   // the only ones on them).  V of block i + 1 is issued before block i's
@@ -1127,19 +1135,19 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
   constexpr int KL = KST::XFERS;     // K transfers per block
   uint2 vring[2][HALVES][4];
   auto body = [&](int jb, const uint2 (*vr)[4]) {
-    const bool b1 = jb + kWaves < nblk;
-    if (b1) issue_k(jb + kWaves);
+    const bool b1 = jb + kOnlineWaves < nblk;
+    if (b1) issue_k(jb + kOnlineWaves);
     wait_vm_dyn(b1 ? VL + KL : 0);
-    const uint8_t* slot = kslots + ((jb / kWaves) & 1) * KST::BYTES;
+    const uint8_t* slot = kslots + ((jb / kOnlineWaves) & 1) * KST::BYTES;
     U4 kr[KC];
 #pragma unroll
     for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const U4*>(slot + kat[c]);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot is read out before its next transfer
     process(jb, kr, vr);
   };
-  ring_fill(wave, nblk, vring, load_v);
+  ring_fill<2, uint2[HALVES][4], decltype(load_v), kOnlineWaves>(wave, nblk, vring, load_v);
   if (wave < nblk) issue_k(wave);
-  stream_ring(wave, nblk, vring, load_v, body);
+  stream_ring<2, uint2[HALVES][4], decltype(load_v), decltype(body), kOnlineWaves>(wave, nblk, vring, load_v, body);
   __syncthreads();  // every wave is done with its K slots: the area becomes the reduction
 
   // ---- combine the waves (as in decode_partition_fp8_mfma) ----
@@ -1163,15 +1171,15 @@ __global__ void __launch_bounds__(256) decode_partition_bf16_online(const Decode
   }
   __syncthreads();
   const int nparts_b = (ctx + T - 1) / T;
-  for (int idx = tid; idx < G * D / 4; idx += 256) {
+  for (int idx = tid; idx < G * D / 4; idx += kOnlineWaves * kWave) {
     const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
     float Mh = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) Mh = fmaxf(Mh, wstat[(w * G + h) * 2]);
+    for (int w = 0; w < kOnlineWaves; ++w) Mh = fmaxf(Mh, wstat[(w * G + h) * 2]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kOnlineWaves; ++w) {
       const float mw = wstat[(w * G + h) * 2];
       const float sw = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mh);
       L = fmaf(sw, wstat[(w * G + h) * 2 + 1], L);
@@ -1624,7 +1632,7 @@ int launch_typed(const DecodeLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_partition_fp8_mfma<D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
   } else if constexpr (KVT == KVATTN_BF16 && G >= KVATTN_BF16_ONLINE_MIN_G) {
     const size_t lds = (size_t)bf16_online_lds_bytes(a.part_tokens, G, D, MASK);
-    hipLaunchKernelGGL((decode_partition_bf16_online<D, G, MASK, TAIL>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((decode_partition_bf16_online<D, G, MASK, TAIL>), grid, dim3(kOnlineWaves * kWave), lds, s, a);
   } else if constexpr (KVT == KVATTN_BF16 && G >= 4) {
     const size_t lds = (size_t)kslot_offset(decode_lds_floats(a.part_tokens, G, D) + (MASK ? a.part_tokens / 4 : 0)) +
                        (size_t)kWaves * KStage<2 * D>::BYTES;
