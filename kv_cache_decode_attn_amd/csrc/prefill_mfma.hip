@@ -135,6 +135,23 @@ __device__ __forceinline__ void settle(const U4& x) {
 #endif
 }
 
+// Marks the scores as written at this point (an empty asm statement), so
+// the softmax that reads them stays inside the step that issues it, between
+// the matrix products it is meant to overlap, instead of being moved into a
+// block of its own between steps.
+__device__ __forceinline__ void pin(f32x16& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+}
+
+// Marks a value as used at this point (an empty asm statement).
+__device__ __forceinline__ void keep(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
+
 // sum of the two bf16 weights of w, accumulated in fp32
 __device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
   const uint32_t one2 = 0x3F803F80u;  // two bf16 1.0
@@ -688,10 +705,23 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   auto fast_step = [&](int it, f32x16 (&s_cur)[kCB], f32x16 (&s_nxt)[kCB], const U4 (&p_prev)[kCB][2],
                        U4 (&p_cur)[kCB][2], float (&alpha)[kCB], bool& resc, f32x16 (&o)[kCB][DT]) {
     load_tile(it + kAhead, kAhead - 2);
+    // after the transfers' (uniform) branch, in the block of the products
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) pin(s_cur[cb]);
     scores((it + 1) % NB, s_nxt);
     softmax(std::false_type{}, it * kKeys - ksh, it % NB, s_cur, p_cur, alpha, resc);
     pv((it + NB - 1) % NB, p_prev, o);
     finish_tile(it + 2, std::integral_constant<int, kAhead - 2>{});
+    // the weights and row sums are complete here, beside this step's matrix
+    // products: left to itself the compiler moves their computation down to
+    // the next step's PV product, which for the second step of the loop
+    // body means into a block of its own between the steps
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      settle(p_cur[cb][0]);
+      settle(p_cur[cb][1]);
+      keep(lpart[cb]);
+    }
     __syncthreads();
   };
   // General step: masked softmax, the parts this step has, and the rescale.
