@@ -169,12 +169,20 @@ __device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
 //     d = 64 (128-byte rows, two per 256 bytes): c ^ ((r / 2) % 8);
 //   V (transposing 8-byte reads, 32 lanes = 4 rows x 2 d halves x 4 pieces):
 //     d = 128: c ^ 4 (r % 4);  d = 64: c ^ 4 ((r / 2) % 2).
-template <int D>
+// VP: the V tile in placed-row form (d = 128), so that every transposing V
+// read of a step is one per-lane address plus constant offsets.  Key k of
+// the tile sits in piece k % 4 + 4 (k / 16), row (k / 4) % 4 of that 1 KB
+// piece, its chunks in order, and each piece is followed by 64 bytes of
+// padding: the four keys a 16-lane group reads together (k % 4 = 0..3) lie
+// in four pieces whose rows start 64 bytes apart in the bank cycle, so the
+// group's reads fall on distinct banks without an XOR swizzle of the chunks.
+template <int D, bool VP = false>
 struct Geo {
   static constexpr int RB = D * 2;  // row bytes
   static constexpr int NC = D / 8;  // 16-byte chunks per row
   static constexpr int KBYTES = kKeys * RB;
-  static constexpr int VBYTES = kKeys * RB;
+  static constexpr int VPIECE = VP ? 1024 + 64 : 1024;  // bytes per 1 KB piece of V in LDS
+  static constexpr int VBYTES = kKeys * RB / 1024 * VPIECE;
   static constexpr int BUF = KBYTES + VBYTES;
   static constexpr int PIECES = kKeys * NC / 64;                   // 1 KB pieces per operand
   static constexpr int LOADS = PIECES >= kWaves ? PIECES / kWaves : 1;  // pieces per loading wave
@@ -246,13 +254,21 @@ __device__ __forceinline__ s16x4 read_tr16(const uint8_t* lds) {
 // published: at most tiles it + 2 .. it + kAhead, four (the prologue publishes
 // tile 0 before it issues tile 4).  At d = 128 the two fill the 160 KB.
 constexpr int kStage = kAhead - 1;
-template <int D, bool FP8P>
-constexpr int prefill_lds_bytes() { return kBufs * Geo<D>::BUF + (FP8P ? kStage * 2 * kKeys * D : 0); }
+// The placed-row V form needs d = 128 and the tile-wide transfers of a
+// prompt without a cached prefix (a prefix tile is gathered row by row with
+// K and V rows in the same order; the fp8 prefix has no LDS to spare).
+template <int D, bool PREFIX, bool FP8P>
+constexpr bool v_placed() { return D == 128 && !PREFIX && !FP8P; }
+template <int D, bool PREFIX, bool FP8P>
+constexpr int prefill_lds_bytes() {
+  return kBufs * Geo<D, v_placed<D, PREFIX, FP8P>()>::BUF + (FP8P ? kStage * 2 * kKeys * D : 0);
+}
 
 template <int D, bool CAUSAL, bool MASK, bool PREFIX, bool FP8P>
 __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const PrefillLaunch a, int hw) {
   static_assert(PREFIX || !FP8P, "fp8 rows come only from a cached prefix");
-  using GE = Geo<D>;
+  constexpr bool VPL = v_placed<D, PREFIX, FP8P>();
+  using GE = Geo<D, VPL>;
   constexpr int NB = kBufs;                 // tile buffers in the ring
   constexpr int S8 = kKeys * D;             // bytes of one operand's fp8 codes per tile
   constexpr int DK = D / 16;  // 16-wide d chunks of the QK^T contraction
@@ -385,14 +401,23 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // mask, rows of masked keys are zeroed by the loading wave once its loads
   // have landed, so no non-finite padding reaches the PV product.
   const int key_lim = min(Ltot, ntiles * kKeys - ksh);
-  int koff[GE::LOADS], voff[GE::LOADS], lrow[GE::LOADS];  // per lane, tile independent
+  // per lane, tile independent: the rows of its K and V slots and the
+  // global offsets of the chunks that fill them
+  int koff[GE::LOADS], voff[GE::LOADS], lrow[GE::LOADS], vrow[GE::LOADS];
 #pragma unroll
   for (int i = 0; i < GE::LOADS; ++i) {
     const int slot = (wave * GE::LOADS + i) * 64 + lane;  // 16-byte slot in the tile
     const int r = slot / GE::NC, cs = slot % GE::NC;
     lrow[i] = r;
     koff[i] = r * GE::RB + (cs ^ GE::swz_k(r)) * 16;
-    voff[i] = r * GE::RB + (cs ^ GE::swz_v(r)) * 16;
+    if constexpr (VPL) {  // piece pc, row lane / 16 of it: key pc % 4 + 4 (lane / 16) + 16 (pc / 4)
+      const int pc = wave * GE::LOADS + i;
+      vrow[i] = (pc & 3) + 4 * (lane >> 4) + 16 * (pc >> 2);
+      voff[i] = vrow[i] * GE::RB + (lane & 15) * 16;
+    } else {
+      vrow[i] = r;
+      voff[i] = r * GE::RB + (cs ^ GE::swz_v(r)) * 16;
+    }
   }
   // With a prefix, every tile is gathered row by row: key index k is cache
   // position kbase + k (below P) or new token k - QO.  A row that is absent
@@ -446,7 +471,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
       uint32_t info = 0;
 #pragma unroll
       for (int i = 0; i < GE::LOADS; ++i) {
-        const int key = kt0 + lrow[i];
+        const int key = kt0 + vrow[i];  // the key of this lane's V slot
         // without a prefix, rows at or past key_lim arrive as zeros already
         if ((prefix || key < key_lim) && !key_valid(key)) info |= 1u << i;
       }
@@ -487,7 +512,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
         }
         const int piece = wave * GE::LOADS + i;
         load_lds16_ptr(rk + (koff[i] - lrow[i] * GE::RB), kl + piece * 1024);
-        load_lds16_ptr(rv + (voff[i] - lrow[i] * GE::RB), vl + piece * 1024);
+        load_lds16_ptr(rv + (voff[i] - lrow[i] * GE::RB), vl + piece * GE::VPIECE);
       }
       return;
     }
@@ -498,7 +523,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
     for (int i = 0; i < GE::LOADS; ++i) {
       const int piece = wave * GE::LOADS + i;
       load_lds16(kr, kl + piece * 1024, koff[i]);
-      load_lds16(vr, vl + piece * 1024, voff[i]);
+      load_lds16(vr, vl + piece * GE::VPIECE, voff[i]);
     }
   };
   // Waits until at most `younger` tiles' loads of this wave are in flight
@@ -534,7 +559,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
       }
 #pragma unroll
       for (int i = 0; i < GE::LOADS; ++i)
-        if (info & (1u << i)) *reinterpret_cast<U4*>(vl + (wave * GE::LOADS + i) * 1024 + lane * 16) = U4{0, 0, 0, 0};
+        if (info & (1u << i)) *reinterpret_cast<U4*>(vl + (wave * GE::LOADS + i) * GE::VPIECE + lane * 16) = U4{0, 0, 0, 0};
     }
   };
 
@@ -661,13 +686,20 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   auto k_frag = [&](const uint8_t* kl, int cc) -> U4 {
     return *reinterpret_cast<const U4*>(kl + lc * GE::RB + ((2 * cc + hh) ^ GE::swz_k(lc)) * 16);
   };
+  // Placed V rows: key r = 16 m + 8 u + 4 h + e is in piece e + 4 m, row
+  // 2 u + h, so the address is one per-lane base plus constants.
+  const int vbase = tr_e * GE::VPIECE + hh * GE::RB + (2 * tr_dh + (tr_q >> 1)) * 16 + 8 * (tr_q & 1);
   auto v_frag = [&](const uint8_t* vl, int m, int dt) -> U4 {
-    const int ch = 4 * dt + 2 * tr_dh + (tr_q >> 1);  // 16-byte chunk of d
     s16x4 half[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int r = 16 * m + 8 * u + 4 * hh + tr_e;
-      half[u] = read_tr16(vl + r * GE::RB + ((ch ^ GE::swz_v(r)) * 16) + 8 * (tr_q & 1));
+      if constexpr (VPL) {
+        half[u] = read_tr16(vl + vbase + m * 4 * GE::VPIECE + u * 2 * GE::RB + dt * 64);
+      } else {
+        const int ch = 4 * dt + 2 * tr_dh + (tr_q >> 1);  // 16-byte chunk of d
+        const int r = 16 * m + 8 * u + 4 * hh + tr_e;
+        half[u] = read_tr16(vl + r * GE::RB + ((ch ^ GE::swz_v(r)) * 16) + 8 * (tr_q & 1));
+      }
     }
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 h0 = __builtin_bit_cast(u32x2, half[0]), h1 = __builtin_bit_cast(u32x2, half[1]);
@@ -857,7 +889,7 @@ int launch_typed(const PrefillLaunch& a, hipStream_t s) {
   const int hw = G < kBlocks ? G : kBlocks;
   const int rows = 32 * kBlocks / hw;
   const dim3 grid(a.num_q_heads / hw, (a.n_max + rows - 1) / rows, a.batch);
-  const size_t lds = prefill_lds_bytes<D, FP8P>();
+  const size_t lds = prefill_lds_bytes<D, PREFIX, FP8P>();
   hipLaunchKernelGGL((prefill_mfma_kernel<D, CAUSAL, MASK, PREFIX, FP8P>), grid, dim3(kThreads), lds, s, a, hw);
   return hipGetLastError() == hipSuccess ? KVATTN_OK : KVATTN_ELAUNCH;
 }
