@@ -59,13 +59,15 @@ DEV = "cuda"
 
 
 # Sources each workload's timed kernels are built from: files (the build
-# script included: it holds the compiler flags), and the launch-argument
-# structs of launch.h they compile against.
+# script included: it holds the compiler flags; and the host side of the
+# library, which picks the launch shapes, such as the default partition
+# size), and the launch-argument structs of launch.h they compile against.
 CSRC = "kv_cache_decode_attn_amd/csrc/"
 BUILD_PY = "kv_cache_decode_attn_amd/build.py"
+API_CPP = CSRC + "kvattn_api.cpp"
 KERNEL_SOURCES = {
-    "decode": (CSRC + "decode.hip", CSRC + "common.h", BUILD_PY, "DecodeLaunch"),
-    "prefill": (CSRC + "prefill_mfma.hip", CSRC + "common.h", BUILD_PY, "PrefillLaunch"),
+    "decode": (CSRC + "decode.hip", CSRC + "common.h", API_CPP, BUILD_PY, "DecodeLaunch"),
+    "prefill": (CSRC + "prefill_mfma.hip", CSRC + "common.h", API_CPP, BUILD_PY, "PrefillLaunch"),
 }
 WORKLOAD_KERNELS = {"decode8b": "decode", "padded32": "decode", "longctx70b": "decode", "verify8b": "decode",
                     "prefill8k": "prefill"}
@@ -87,15 +89,16 @@ def _code_only(text):
 
 def source_sha(kind, read=None):
     """Hash of the sources the `kind` kernels ("decode", "prefill") are built
-    from: the code of the kernel files (comments and layout ignored), the
-    build script, and the launch struct they compile against."""
+    and launched from: the code of the kernel files and of the library's host
+    side (comments and layout ignored), the build script, and the launch
+    struct they compile against."""
     if read is None:
         def read(rel):
             with open(os.path.join(ROOT, rel), "rb") as f:
                 return f.read()
     h = hashlib.sha256()
     for item in KERNEL_SOURCES[kind]:
-        if item.endswith((".hip", ".h")):
+        if item.endswith((".hip", ".h", ".cpp")):
             h.update(_code_only(read(item).decode()).encode())
         elif item.endswith(".py"):
             h.update(read(item))

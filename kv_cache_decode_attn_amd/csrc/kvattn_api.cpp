@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -141,8 +142,13 @@ constexpr int32_t kMaxPartScores = 8192;  // part_tokens * group, bounds the LDS
 //    last).  Take as many partitions per (sequence, KV head) as the device's
 //    compute units hold, with the keys split as evenly as 64-key steps allow
 //    (4160 keys at 131,073 keys x 8 KV heads: exactly 256 workgroups).
-//  - vector-ALU pass: 512 keys for G >= 4, 256 for G <= 2, shrunk until the
-//    grid offers >= 2048 workgroups.
+//  - bf16 cache with 16 query columns per KV head (the single-sweep pass, in
+//    eight-wave workgroups): 1,280 keys, halved in 64-key steps while the
+//    grid has fewer than 768 workgroups.  On the check of 4 drafted tokens
+//    (lengths U[1, 8192]) this gives 640 keys at batch 8 and 1,280 at
+//    batches 16-64, the best of 256-1,536 at each.
+//  - the three-phase passes: 512 keys for G >= 4, 256 for G <= 2, shrunk
+//    until the grid offers >= 2048 workgroups.
 bool fp8_mfma_pass(int32_t dtype, int32_t group) { return dtype == KVATTN_FP8_E4M3 && group >= 4; }
 
 int32_t default_part_tokens(int32_t dtype, int32_t batch, int32_t hq, int32_t hkv, int32_t max_seq_len) {
@@ -159,10 +165,16 @@ int32_t default_part_tokens(int32_t dtype, int32_t batch, int32_t hq, int32_t hk
     const int64_t t = ((max_seq_len + per - 1) / per + 63) / 64 * 64;
     return (int32_t)(t < 256 ? 256 : t > kMaxPartTokens ? kMaxPartTokens : t);
   }
-  // the single-sweep bf16 pass keeps no scores in LDS: longer partitions, fewer partials
-  int32_t t = kvattn::decode_single_pass(dtype, group) ? 1024 : group >= 4 ? 512 : 256;
-  if (!kvattn::decode_single_pass(dtype, group))
-    while (t * group > kMaxPartScores) t /= 2;
+  if (kvattn::decode_single_pass(dtype, group)) {
+    // the single-sweep bf16 pass (eight-wave workgroups, no scores in LDS):
+    // 1,280 keys, halved in 64-key steps while the grid has fewer than 768
+    // workgroups
+    int32_t t = 1280;
+    while (t > 64 && wgs(t) < 768) t = std::max<int32_t>(64, t / 2 / 64 * 64);
+    return t;
+  }
+  int32_t t = group >= 4 ? 512 : 256;
+  while (t * group > kMaxPartScores) t /= 2;
   while (t > 64 && wgs(t) < 2048) t /= 2;
   return t;
 }

@@ -17,13 +17,13 @@ def _files():
     launch = ("struct Other {\n  int x;\n};\nstruct DecodeLaunch {\n  int a;\n};\n"
               "struct PrefillLaunch {\n  int b;\n};\n")
     return {bench.CSRC + "decode.hip": b"decode v1", bench.CSRC + "prefill_mfma.hip": b"prefill v1",
-            bench.CSRC + "common.h": b"common v1", bench.BUILD_PY: b"flags v1",
+            bench.CSRC + "common.h": b"common v1", bench.API_CPP: b"host v1", bench.BUILD_PY: b"flags v1",
             bench.CSRC + "launch.h": launch.encode()}
 
 
 def test_source_hash_follows_every_input_of_the_kernels():
     base = bench.source_sha("decode", read=_reader(_files()))
-    for rel in (bench.CSRC + "decode.hip", bench.CSRC + "common.h", bench.BUILD_PY):
+    for rel in (bench.CSRC + "decode.hip", bench.CSRC + "common.h", bench.API_CPP, bench.BUILD_PY):
         f = _files()
         f[rel] += b" changed"
         assert bench.source_sha("decode", read=_reader(f)) != base, rel
