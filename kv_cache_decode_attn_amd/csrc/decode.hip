@@ -314,7 +314,7 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // s_waitcnt immediate: at most n vector memory operations outstanding.
 __host__ __device__ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 // Cache policy of the K transfers: non-temporal (each byte is read once).
-constexpr int kPolicyNT = 2;
+[[maybe_unused]] constexpr int kPolicyNT = 2;  // used in the device pass only
 
 // 16 bytes per lane from `src` into LDS at dst + 16 * lane (dst uniform over
 // the wave), non-temporally.  The body exists in the device pass only: the

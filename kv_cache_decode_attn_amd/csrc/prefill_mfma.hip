@@ -681,11 +681,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // d = 32 dt + l % 32 and the 8 keys of its operand slots, 4h + 0..3 and
   // 8 + 4h + 0..3 of the 16-key slab (h = l / 32): two reads.
   const int tr_e = (lane & 15) >> 2, tr_q = lane & 3, tr_dh = (lane >> 4) & 1;
-  // One K fragment (A operand of the QK^T product, d chunk cc) and one V^T
-  // fragment (A operand of the PV product, key slab m, d tile dt).
-  auto k_frag = [&](const uint8_t* kl, int cc) -> U4 {
-    return *reinterpret_cast<const U4*>(kl + lc * GE::RB + ((2 * cc + hh) ^ GE::swz_k(lc)) * 16);
-  };
+  // One V^T fragment (A operand of the PV product, key slab m, d tile dt).
   // Placed V rows: key r = 16 m + 8 u + 4 h + e is in piece e + 4 m, row
   // 2 u + h, so the address is one per-lane base plus constants.
   const int vbase = tr_e * GE::VPIECE + hh * GE::RB + (2 * tr_dh + (tr_q >> 1)) * 16 + 8 * (tr_q & 1);
