@@ -485,9 +485,10 @@ int kvattn_copy_blocks(const kvattn_cache* cache, int32_t n,
  * one plain pass over device memory, the context figure for the HBM-bound
  * calls above (decode reads the whole cache every step, "KV Cache", section
  * "Prefill and Decode").  Reads [src, src + bytes) once with 16-byte
- * non-temporal loads (each wave 1 KB contiguous per instruction, 8
- * workgroups of 256 threads per compute unit) and XORs the XOR of all its
- * 32-bit words into *sink, so the result can be checked exactly.
+ * non-temporal loads (each wave 1 KB contiguous per instruction; 4
+ * workgroups of 256 threads per compute unit, each reading one contiguous
+ * range) and XORs the XOR of all its 32-bit words into *sink, so the result
+ * can be checked exactly.
  *
  *  src    device, 16-byte aligned
  *  bytes  a multiple of 16 (0 is a no-op)

@@ -669,13 +669,15 @@ int kvattn_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* str
   if (!src || !sink) return fail(KVATTN_EINVAL, "%s: src and sink are required", who);
   if (!aligned16(src)) return fail(KVATTN_EINVAL, "%s: src not 16-byte aligned", who);
   if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return fail(KVATTN_EINVAL, "%s: sink not 4-byte aligned", who);
-  // enough workgroups to keep every compute unit's loads in flight: 8 per
-  // unit, fewer for a small buffer (each thread takes at least 4 chunks)
+  // one contiguous range per workgroup, 4 workgroups per compute unit
+  // (fewer for a small buffer); ranges are whole 16 KB steps (1024 chunks
+  // of 16 bytes) so only the last one is ragged
   const int64_t chunks = bytes / 16;
-  int64_t wgs = (chunks + 256 * 4 - 1) / (256 * 4);
-  const int64_t cap = 8 * compute_units();
-  if (wgs > cap) wgs = cap;
-  kvattn::StreamReadLaunch a{static_cast<const uint8_t*>(src), bytes, sink};
+  const int64_t target = 4 * compute_units();
+  int64_t per = (chunks + target - 1) / target;
+  per = (per + 1023) / 1024 * 1024;
+  const int64_t wgs = (chunks + per - 1) / per;  // every range starts below the end
+  kvattn::StreamReadLaunch a{static_cast<const uint8_t*>(src), bytes, per, sink};
   int rc = kvattn::launch_stream_read(a, (int32_t)wgs, static_cast<hipStream_t>(stream));
   if (rc) return fail(rc, "%s: %s", who, kvattn_status_string(rc));
   return ok();

@@ -152,6 +152,7 @@ int launch_copy_blocks(const BlockCopyLaunch& a, hipStream_t stream);
 struct StreamReadLaunch {
   const uint8_t* src;
   int64_t bytes;
+  int64_t chunks_per_wg;  // 16-byte chunks each workgroup reads, a multiple of 1024
   uint32_t* sink;
 };
 int launch_stream_read(const StreamReadLaunch& a, int32_t workgroups, hipStream_t stream);

@@ -5,11 +5,16 @@
 // "Prefill and Decode"), so this is the ceiling its kernels are compared
 // with.
 //
-// Each thread reads 16-byte chunks with non-temporal loads, four in flight,
-// over a grid-stride loop (a wave reads 1 KB contiguous per instruction),
-// and folds them into one 32-bit XOR; each wave XORs its lanes' words into
-// *sink with one atomic, so the loads cannot be dropped and the result is
-// checkable bit for bit.
+// Each workgroup reads one contiguous range of the buffer (a multiple of
+// 16 KB; the last one takes the ragged tail): its threads read 16-byte
+// chunks with non-temporal loads, four in flight, so a wave reads 1 KB
+// contiguous per instruction and the workgroup walks its range in 16 KB
+// steps.  Contiguous ranges per workgroup read faster on this GPU than a
+// grid-stride walk of the whole buffer (about 7.0 against 6.1-6.4 TB/s
+// measured on a 4 GiB buffer), so this is the faster of the two plain
+// forms.  The chunks fold into one 32-bit XOR; each wave XORs its lanes'
+// words into *sink with one atomic, so the loads cannot be dropped and the
+// result is checkable bit for bit.
 #include "launch.h"
 
 namespace kvattn {
@@ -22,17 +27,18 @@ __device__ __forceinline__ uint32_t fold(const u32x4 v) { return v.x ^ v.y ^ v.z
 __global__ void __launch_bounds__(256) stream_read_kernel(const StreamReadLaunch a) {
   const u32x4* src = reinterpret_cast<const u32x4*>(a.src);
   const int64_t n = a.bytes / 16;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t lo = (int64_t)blockIdx.x * a.chunks_per_wg;
+  const int64_t hi = lo + a.chunks_per_wg < n ? lo + a.chunks_per_wg : n;
+  int64_t i = lo + threadIdx.x;
   uint32_t x = 0;
-  for (; i + 3 * stride < n; i += 4 * stride) {
+  for (; i + 3 * 256 < hi; i += 4 * 256) {
     const u32x4 v0 = __builtin_nontemporal_load(src + i);
-    const u32x4 v1 = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 v2 = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 v3 = __builtin_nontemporal_load(src + i + 3 * stride);
+    const u32x4 v1 = __builtin_nontemporal_load(src + i + 256);
+    const u32x4 v2 = __builtin_nontemporal_load(src + i + 2 * 256);
+    const u32x4 v3 = __builtin_nontemporal_load(src + i + 3 * 256);
     x ^= fold(v0) ^ fold(v1) ^ fold(v2) ^ fold(v3);
   }
-  for (; i < n; i += stride) x ^= fold(__builtin_nontemporal_load(src + i));
+  for (; i < hi; i += 256) x ^= fold(__builtin_nontemporal_load(src + i));
   for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
   if ((threadIdx.x & 63) == 0 && x != 0) atomicXor(a.sink, x);
 }

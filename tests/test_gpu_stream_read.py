@@ -1,7 +1,8 @@
 """The streaming-read measurement helper on the GPU: every byte is read (the
-XOR of all 32-bit words comes back exactly) for sizes below one chunk per
-thread, with a ragged tail past the grid's stride, and larger than the grid
-covers in one pass."""
+XOR of all 32-bit words comes back exactly) for a buffer of one 16-byte
+chunk, one below a workgroup's 16 KB step, one whose last workgroup range
+holds a single chunk (1 MiB + 16: 65 ranges), and one of 821 ranges of
+80 KB with a two-chunk last range (on 256 compute units)."""
 import numpy as np
 import pytest
 import torch
