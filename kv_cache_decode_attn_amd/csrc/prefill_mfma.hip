@@ -68,7 +68,9 @@
 // by row, a prefix row through the block table (or the contiguous cache) and
 // a new row from the new K/V, with per-lane global-to-LDS transfers.  The
 // workgroup first checks that every prefix block id is valid; if one is not,
-// its positions are masked keys and every tile takes the masked step.
+// its positions are masked keys and every tile takes the masked step.  The
+// ids of a paged prefix are copied to LDS by that check, and a tile of whole
+// cached blocks takes its rows' addresses from them without a branch.
 //
 // fp8 cache prefix.  An E4M3FN code is exactly a bf16 value, so a cached row
 // is staged as its codes (not yet scaled).  The 32-key tile grid is shifted
@@ -259,9 +261,17 @@ constexpr int kStage = kAhead - 1;
 // K and V rows in the same order; the fp8 prefix has no LDS to spare).
 template <int D, bool PREFIX, bool FP8P>
 constexpr bool v_placed() { return D == 128 && !PREFIX && !FP8P; }
+// With a bf16 cached prefix in a paged cache, the block ids of the prefix
+// (up to kTblMax blocks) are copied to LDS after the tile ring when the
+// workgroup checks them, so gathering a tile's rows reads its block ids
+// from LDS: a global read of the table would make the wave wait for its
+// tile transfers still in flight (the vector-memory counter is in order).
+// At d = 128 the ring and the table fill the 160 KB.
+constexpr int kTblMax = 8192;
 template <int D, bool PREFIX, bool FP8P>
 constexpr int prefill_lds_bytes() {
-  return kBufs * Geo<D, v_placed<D, PREFIX, FP8P>()>::BUF + (FP8P ? kStage * 2 * kKeys * D : 0);
+  return kBufs * Geo<D, v_placed<D, PREFIX, FP8P>()>::BUF + (FP8P ? kStage * 2 * kKeys * D : 0) +
+         ((PREFIX && !FP8P) ? kTblMax * 4 : 0);
 }
 
 template <int D, bool CAUSAL, bool MASK, bool PREFIX, bool FP8P>
@@ -331,6 +341,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // each of its blocks): one scan of the sequence's table row by the
   // workgroup.  Prefix positions outside the cache are masked keys.
   bool prefix_ok = true;
+  constexpr bool TBL = PREFIX && !FP8P;
+  int32_t* const tbl = reinterpret_cast<int32_t*>(smem + NB * GE::BUF);  // prefix block ids (TBL)
+  bool tbl_ok = false;  // uniform: every prefix block id is in tbl
   if (PREFIX && P > 0) {
     // the flag lives in the first bytes of the tile ring (no static LDS: with
     // an fp8 prefix the dynamic LDS is the whole 160 KB); a barrier after it
@@ -346,8 +359,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
       for (int j = tid; j < min(nb, cv.max_blocks); j += kThreads) {
         const int32_t blk = row[j];
         mine |= (blk < 0) | ((int64_t)blk >= cv.num_blocks);
+        if (TBL && j < kTblMax) tbl[j] = blk;
       }
       if (mine) bad = 1;
+      tbl_ok = TBL && nb <= min(cv.max_blocks, kTblMax);
     } else if (tid == 0 && (int64_t)P > cv.capacity) {
       bad = 1;
     }
@@ -462,6 +477,21 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   const int f_row = f_slot / GE::NC;
   const int f_chunk = (((f_slot % GE::NC) ^ (f_op ? GE::swz_v(f_row) : GE::swz_k(f_row))) >> 1) * 16;
   uint8_t* const stage = smem + NB * GE::BUF;  // [kStage][pieces][K 512 B, V 512 B] (fp8 prefix)
+  // per lane (tbl_ok): offset of its K chunk within a block of the cache
+  // (head g, row lrow % 16); its V chunk is voff - koff further
+  int64_t tile_row_off[GE::LOADS];
+#pragma unroll
+  for (int i = 0; i < GE::LOADS; ++i)
+    tile_row_off[i] = (int64_t)g * a.c.head_stride + (int64_t)(lrow[i] % kBlockTokens) * a.c.row_stride +
+                      (koff[i] - lrow[i] * GE::RB);
+  // cache offset of prefix position ka (0 <= ka < P) from the block ids in
+  // LDS (tbl_ok), -1 for an invalid id, as position_offset gives
+  auto tbl_offset = [&](int ka) -> int64_t {
+    const CacheView& cv = a.c;
+    const int32_t blk = tbl[ka / kBlockTokens];
+    if (blk < 0 || (int64_t)blk >= cv.num_blocks) return -1;
+    return (int64_t)blk * cv.block_stride + (int64_t)g * cv.head_stride + (int64_t)(ka % kBlockTokens) * cv.row_stride;
+  };
   auto load_tile = [&](int t, int slot) {
     const int kt0 = t * kKeys - ksh;
     uint8_t* kl = smem + (t % NB) * GE::BUF;
@@ -492,6 +522,19 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
         pending |= (uint64_t)16 << (8 * slot);
         return;
       }
+      if (tbl_ok && prefix_ok && kt0 + kKeys <= P) {  // uniform: cached rows only, every id valid
+        // a tile is whole blocks (kt0 is a multiple of kKeys), so a lane's row
+        // sits at the same place in its block in every tile
+        static_assert(kKeys % kBlockTokens == 0, "tiles of whole cache blocks");
+#pragma unroll
+        for (int i = 0; i < GE::LOADS; ++i) {
+          const int64_t off = (int64_t)tbl[(kt0 + lrow[i]) / kBlockTokens] * a.c.block_stride + tile_row_off[i];
+          const int piece = wave * GE::LOADS + i;
+          load_lds16_ptr(a.c.k + off, kl + piece * 1024);
+          load_lds16_ptr(a.c.v + off + (voff[i] - koff[i]), vl + piece * GE::VPIECE);
+        }
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < GE::LOADS; ++i) {
         const int key = kt0 + lrow[i];
@@ -503,7 +546,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
             rk = kg + (int64_t)(ka - P) * GE::RB;
             rv = vg + (int64_t)(ka - P) * GE::RB;
           } else {
-            const int64_t off = position_offset(a.c, b, g, ka);
+            const int64_t off = tbl_ok ? tbl_offset(ka) : position_offset(a.c, b, g, ka);
             if (off >= 0) {
               rk = a.c.k + off;
               rv = a.c.v + off;
@@ -885,6 +928,7 @@ int launch_typed(const PrefillLaunch& a, hipStream_t s) {
   const int hw = G < kBlocks ? G : kBlocks;
   const int rows = 32 * kBlocks / hw;
   const dim3 grid(a.num_q_heads / hw, (a.n_max + rows - 1) / rows, a.batch);
+  static_assert(prefill_lds_bytes<D, PREFIX, FP8P>() <= 160 * 1024, "LDS of one workgroup");
   const size_t lds = prefill_lds_bytes<D, PREFIX, FP8P>();
   hipLaunchKernelGGL((prefill_mfma_kernel<D, CAUSAL, MASK, PREFIX, FP8P>), grid, dim3(kThreads), lds, s, a, hw);
   return hipGetLastError() == hipSuccess ? KVATTN_OK : KVATTN_ELAUNCH;

@@ -367,6 +367,45 @@ def test_mfma_chunked_prefill_long_prefix_many_tiles():
     assert max_abs(got[0], full[0, :, P0:]) <= TOL
 
 
+
+@pytest.mark.parametrize("P0", [131072, 140007])
+def test_mfma_chunked_prefill_prefix_of_many_blocks(P0):
+    """Paged prefixes of 8,192 blocks (131,072 positions) and of 8,751
+    blocks: the kernel keeps up to a fixed number of a prefix's block ids in
+    LDS and otherwise reads them from the table in global memory; both give
+    the oracle's rows (GQA 2, d 64, a 40-token causal chunk).  Attention over
+    the prefix does not depend on the order of its keys, and one row among
+    10^5 barely moves an average, so 24 "needle" keys spread over the prefix
+    (the last block included) are made to dominate every query's weights: a
+    needle's block read from its neighbour changes the result by 5e-3 to
+    8e-2 (the oracle with that mistake), while rounding the weights to bf16
+    can move it by at most 2^-9 of the needles' largest V element (1.8e-3)."""
+    Hq, Hkv, d, n = 2, 1, 64, 40
+    total = P0 + n
+    kp = synth.normal((1, Hkv, total, d), (75, synth.T_K), torch.bfloat16, std=1 / math.sqrt(d))
+    vp = synth.normal((1, Hkv, total, d), (75, synth.T_V), torch.bfloat16, std=1 / math.sqrt(d))
+    u = synth.normal((d,), (76, synth.T_Q), torch.float32)
+    u = u / u.norm()
+    needles = np.linspace(5, P0 - 1, 24).astype(np.int64)
+    for j, pos in enumerate(needles):
+        kp[0, :, pos] = ((40.0 + 0.25 * j) * u).to(torch.bfloat16)   # scores ~20 against 4u
+        vp[0, :, pos] = synth.normal((d,), (77 + j, synth.T_V), torch.bfloat16, std=0.25)
+    q2 = (synth.normal((1, Hq, n, d), (78, synth.T_Q), torch.float32, std=0.1) + 4.0 * u).to(torch.bfloat16)
+    k2 = kp[:, :, P0:].contiguous()
+    v2 = vp[:, :, P0:].contiguous()
+    nb = synth.blocks_for(total)
+    table, nblk = synth.block_table([nb], nb, (75, synth.T_PERM))
+    tdev = torch.from_numpy(table).to(DEV)
+    cache = K.KVCache.paged(nblk, Hkv, d, K.BF16, DEV)
+    P = torch.tensor([P0], dtype=torch.int32, device=DEV)
+    K.kv_append(cache, kp.to(DEV), vp.to(DEV), torch.zeros(1, dtype=torch.int32, device=DEV), block_table=tdev,
+                n_valid=P)
+    got = K.attn_prefill(q2.to(DEV), k2.to(DEV), v2.to(DEV), cache=cache, positions=P, block_table=tdev,
+                         attend_prefix=True).cpu().numpy()
+    want = _oracle(q2, k2, v2, [P0], [n], prefix=([f64(kp[0, :, :P0])], [f64(vp[0, :, :P0])]))
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= TOL
+
 def test_mfma_prefix_key_mask_nan_poisoned_and_verify_shape():
     """Key mask over absolute positions with NaN in the masked cached rows
     (weights exactly 0, outputs finite), and a 4-token chunk (the shape of
