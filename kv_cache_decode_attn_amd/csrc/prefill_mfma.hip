@@ -30,8 +30,9 @@
 // first.
 //
 // Staging.  32-key tiles of K and V go from global memory straight into an
-// 8-tile LDS ring (buffer loads that write LDS), 5 tiles ahead of the one
-// being scored; each wave waits only for its own transfers of the tile it
+// 8-tile LDS ring (7 with an fp8 prefix; buffer loads that write LDS), 5
+// tiles ahead of the one being scored; each wave waits only for its own
+// transfers of the tile it
 // publishes, and one barrier per step publishes it.  V stays row-major in
 // LDS and its MFMA operand is read with the transposing LDS read.
 //
@@ -250,28 +251,33 @@ __device__ __forceinline__ s16x4 read_tr16(const uint8_t* lds) {
 #endif
 }
 
-// LDS of the kernel: the kBufs tile buffers, then (fp8 prefix) a staging
+// LDS of the kernel: the tile buffers, then (fp8 prefix) a staging
 // ring of kStage tiles of fp8 codes (per loading wave 512 bytes of K codes,
 // then 512 of V).  Codes wait in it from their transfer until the tile is
 // published: at most tiles it + 2 .. it + kAhead, four (the prologue publishes
-// tile 0 before it issues tile 4).  At d = 128 the two fill the 160 KB.
+// tile 0 before it issues tile 4).
 constexpr int kStage = kAhead - 1;
 // The placed-row V form needs d = 128 and the tile-wide transfers of a
 // prompt without a cached prefix (a prefix tile is gathered row by row with
 // K and V rows in the same order; the fp8 prefix has no LDS to spare).
 template <int D, bool PREFIX, bool FP8P>
 constexpr bool v_placed() { return D == 128 && !PREFIX && !FP8P; }
-// With a bf16 cached prefix in a paged cache, the block ids of the prefix
-// (up to kTblMax blocks) are copied to LDS after the tile ring when the
-// workgroup checks them, so gathering a tile's rows reads its block ids
-// from LDS: a global read of the table would make the wave wait for its
-// tile transfers still in flight (the vector-memory counter is in order).
-// At d = 128 the ring and the table fill the 160 KB.
-constexpr int kTblMax = 8192;
+// With a cached prefix in a paged cache, the block ids of the prefix (up to
+// tbl_max blocks) are copied to LDS after the tile ring (and the staging
+// ring) when the workgroup checks them, so gathering a tile's rows reads
+// its block ids from LDS: a global read of the table would make the wave
+// wait for its tile transfers still in flight (the vector-memory counter is
+// in order).  An fp8 prefix gives one of the 8 tile buffers to it (7 still
+// hold the tiles it - 1 .. it + kAhead in use).  At d = 128 the rings and
+// the table fill the 160 KB.
+template <bool FP8P>
+constexpr int ring_bufs() { return FP8P ? kAhead + 2 : kBufs; }
+template <bool PREFIX, bool FP8P>
+constexpr int tbl_max() { return !PREFIX ? 0 : FP8P ? 4096 : 8192; }
 template <int D, bool PREFIX, bool FP8P>
 constexpr int prefill_lds_bytes() {
-  return kBufs * Geo<D, v_placed<D, PREFIX, FP8P>()>::BUF + (FP8P ? kStage * 2 * kKeys * D : 0) +
-         ((PREFIX && !FP8P) ? kTblMax * 4 : 0);
+  return ring_bufs<FP8P>() * Geo<D, v_placed<D, PREFIX, FP8P>()>::BUF + (FP8P ? kStage * 2 * kKeys * D : 0) +
+         tbl_max<PREFIX, FP8P>() * 4;
 }
 
 template <int D, bool CAUSAL, bool MASK, bool PREFIX, bool FP8P>
@@ -279,7 +285,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   static_assert(PREFIX || !FP8P, "fp8 rows come only from a cached prefix");
   constexpr bool VPL = v_placed<D, PREFIX, FP8P>();
   using GE = Geo<D, VPL>;
-  constexpr int NB = kBufs;                 // tile buffers in the ring
+  constexpr int NB = ring_bufs<FP8P>();     // tile buffers in the ring
   constexpr int S8 = kKeys * D;             // bytes of one operand's fp8 codes per tile
   constexpr int DK = D / 16;  // 16-wide d chunks of the QK^T contraction
   constexpr int DT = D / 32;  // 32-row d tiles of the output
@@ -341,8 +347,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   // each of its blocks): one scan of the sequence's table row by the
   // workgroup.  Prefix positions outside the cache are masked keys.
   bool prefix_ok = true;
-  constexpr bool TBL = PREFIX && !FP8P;
-  int32_t* const tbl = reinterpret_cast<int32_t*>(smem + NB * GE::BUF);  // prefix block ids (TBL)
+  constexpr bool TBL = PREFIX;
+  constexpr int kTblMax = tbl_max<PREFIX, FP8P>();
+  // prefix block ids (TBL), after the tile ring and the fp8 staging ring
+  int32_t* const tbl = reinterpret_cast<int32_t*>(smem + NB * GE::BUF + (FP8P ? kStage * 2 * S8 : 0));
   bool tbl_ok = false;  // uniform: every prefix block id is in tbl
   if (PREFIX && P > 0) {
     // the flag lives in the first bytes of the tile ring (no static LDS: with
@@ -476,6 +484,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
   const int f_slot = wave * 64 + 2 * (lane & 31);
   const int f_row = f_slot / GE::NC;
   const int f_chunk = (((f_slot % GE::NC) ^ (f_op ? GE::swz_v(f_row) : GE::swz_k(f_row))) >> 1) * 16;
+  // the cache operand this lane fetches codes of, chosen once (a per-lane
+  // choice between the two kernel-argument pointers inside the loop became a
+  // per-lane load of the argument, waited for with the tile transfers)
+  const uintptr_t f_cache =
+      (uintptr_t)a.c.k + (f_op ? (uintptr_t)a.c.v - (uintptr_t)a.c.k : (uintptr_t)0);
   uint8_t* const stage = smem + NB * GE::BUF;  // [kStage][pieces][K 512 B, V 512 B] (fp8 prefix)
   // per lane (tbl_ok): offset of its K chunk within a block of the cache
   // (head g, row lrow % 16); its V chunk is voff - koff further
@@ -512,8 +525,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
         const int key = kt0 + f_row;
         const uint8_t* src = kg;  // new token 0: the stand-in for rows outside the cache
         if (key >= 0) {
-          const int64_t off = position_offset(a.c, b, g, kbase + key);
-          if (off >= 0) src = (f_op ? a.c.v : a.c.k) + off + f_chunk;
+          const int64_t off = tbl_ok ? tbl_offset(kbase + key) : position_offset(a.c, b, g, kbase + key);
+          if (off >= 0) src = reinterpret_cast<const uint8_t*>(f_cache + off + f_chunk);
         }
         // issued twice (the same bytes to the same place): every tile then
         // takes two transfers per lane, and the waits stay constants
