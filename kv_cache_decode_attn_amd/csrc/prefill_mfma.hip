@@ -32,9 +32,9 @@
 // Staging.  32-key tiles of K and V go from global memory straight into an
 // 8-tile LDS ring (7 with an fp8 prefix; buffer loads that write LDS), 5
 // tiles ahead of the one being scored; each wave waits only for its own
-// transfers of the tile it
-// publishes, and one barrier per step publishes it.  V stays row-major in
-// LDS and its MFMA operand is read with the transposing LDS read.
+// transfers of the tile it publishes, and one barrier per step publishes
+// it.  V stays row-major in LDS and its MFMA operand is read with the
+// transposing LDS read.
 //
 // Pipeline.  Step t runs the QK^T product of tile t+1, the softmax of tile
 // t and the PV product of tile t-1: three independent parts that the
