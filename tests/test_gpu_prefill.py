@@ -368,19 +368,19 @@ def test_mfma_chunked_prefill_long_prefix_many_tiles():
 
 
 
-@pytest.mark.parametrize("P0", [131072, 140007])
-def test_mfma_chunked_prefill_prefix_of_many_blocks(P0):
+@pytest.mark.parametrize("P0,d", [(131072, 64), (140007, 64), (140007, 128)])
+def test_mfma_chunked_prefill_prefix_of_many_blocks(P0, d):
     """Paged prefixes of 8,192 blocks (131,072 positions) and of 8,751
-    blocks: the kernel keeps up to a fixed number of a prefix's block ids in
-    LDS and otherwise reads them from the table in global memory; both give
-    the oracle's rows (GQA 2, d 64, a 40-token causal chunk).  Attention over
+    blocks: the kernel keeps up to 8,192 of a prefix's block ids in LDS and
+    otherwise reads them from the table in global memory; both give the
+    oracle's rows (GQA 2, a 40-token causal chunk).  Attention over
     the prefix does not depend on the order of its keys, and one row among
     10^5 barely moves an average, so 24 "needle" keys spread over the prefix
     (the last block included) are made to dominate every query's weights: a
-    needle's block read from its neighbour changes the result by 5e-3 to
-    8e-2 (the oracle with that mistake), while rounding the weights to bf16
-    can move it by at most 2^-9 of the needles' largest V element (1.8e-3)."""
-    Hq, Hkv, d, n = 2, 1, 64, 40
+    needle's block read from its neighbour changes the result by 5e-3 or
+    more (the oracle with that mistake), while rounding the weights to bf16
+    can move it by at most 2^-9 of the needles' largest V element (< 2e-3)."""
+    Hq, Hkv, n = 2, 1, 40
     total = P0 + n
     kp = synth.normal((1, Hkv, total, d), (75, synth.T_K), torch.bfloat16, std=1 / math.sqrt(d))
     vp = synth.normal((1, Hkv, total, d), (75, synth.T_V), torch.bfloat16, std=1 / math.sqrt(d))
