@@ -535,6 +535,21 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
         pending |= (uint64_t)16 << (8 * slot);
         return;
       }
+      if (FP8P && kt0 >= P) {  // uniform: new tokens only, contiguous in k / v
+        // one bounded buffer resource per operand: rows at or past Ltot read
+        // as zeros (and are zeroed again as absent keys).  With a bf16 prefix
+        // this measured slower (the row-by-row path below serves it).
+        const int nbytes = max(Ltot - kt0, 0) * GE::RB;
+        const i32x4 kr = make_rsrc(kg + (int64_t)(kt0 - P) * GE::RB, nbytes);
+        const i32x4 vr = make_rsrc(vg + (int64_t)(kt0 - P) * GE::RB, nbytes);
+#pragma unroll
+        for (int i = 0; i < GE::LOADS; ++i) {
+          const int piece = wave * GE::LOADS + i;
+          load_lds16(kr, kl + piece * 1024, koff[i]);
+          load_lds16(vr, vl + piece * GE::VPIECE, voff[i]);
+        }
+        return;
+      }
       if (tbl_ok && prefix_ok && kt0 + kKeys <= P) {  // uniform: cached rows only, every id valid
         // a tile is whole blocks (kt0 is a multiple of kKeys), so a lane's row
         // sits at the same place in its block in every tile
