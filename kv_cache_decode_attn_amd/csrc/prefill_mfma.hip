@@ -702,9 +702,13 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_mfma_kernel(const Prefill
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
       // running maximum of this query (log2 domain), raised lazily
-      float tm = fmaxf(s[cb][0], s[cb][1]);
+      // a balanced tree (depth 4): both waves of a SIMD reach it together
+      float t8[8];
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) tm = fmaxf(tm, fmaxf(s[cb][r], s[cb][r + 1]));
+      for (int r = 0; r < 8; ++r) t8[r] = fmaxf(s[cb][2 * r], s[cb][2 * r + 1]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t8[r] = fmaxf(t8[2 * r], t8[2 * r + 1]);
+      float tm = fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3]));
       {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
         tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * ct;
