@@ -406,6 +406,46 @@ def test_mfma_chunked_prefill_prefix_of_many_blocks(P0, d):
     assert np.isfinite(got).all()
     assert max_abs(got, want) <= TOL
 
+
+@pytest.mark.parametrize("P0", [65536, 70007])
+def test_mfma_fp8_prefix_of_many_blocks(P0):
+    """An fp8 paged prefix of 4,096 blocks (65,536 positions, as many block
+    ids as the fp8-prefix kernel keeps in LDS) and of 4,376 blocks (ids read
+    from the table in global memory), with 24 dominant needle keys as in the
+    bf16 case above, against the oracle's decoding of its own E4M3FN encoding
+    of the same rows (GQA 2, d 128, a 40-token causal chunk at bf16)."""
+    Hq, Hkv, d, n = 2, 1, 128, 40
+    ks, vs = 0.05, 0.005   # needle K codes up to ~300, needle V codes up to ~180
+    total = P0 + n
+    kp = synth.normal((1, Hkv, total, d), (85, synth.T_K), torch.bfloat16, std=1 / math.sqrt(d))
+    vp = synth.normal((1, Hkv, total, d), (85, synth.T_V), torch.bfloat16, std=1 / math.sqrt(d))
+    u = synth.normal((d,), (86, synth.T_Q), torch.float32)
+    u = u / u.norm()
+    needles = np.linspace(5, P0 - 1, 24).astype(np.int64)
+    for j, pos in enumerate(needles):
+        kp[0, :, pos] = ((40.0 + 0.25 * j) * u).to(torch.bfloat16)
+        vp[0, :, pos] = synth.normal((d,), (87 + j, synth.T_V), torch.bfloat16, std=0.25)
+    q2 = (synth.normal((1, Hq, n, d), (88, synth.T_Q), torch.float32, std=0.1) + 4.0 * u).to(torch.bfloat16)
+    k2 = kp[:, :, P0:].contiguous()
+    v2 = vp[:, :, P0:].contiguous()
+    nb = synth.blocks_for(total)
+    table, nblk = synth.block_table([nb], nb, (85, synth.T_PERM))
+    tdev = torch.from_numpy(table).to(DEV)
+    cache = K.KVCache.paged(nblk, Hkv, d, K.FP8_E4M3, DEV, torch.tensor([ks], device=DEV),
+                            torch.tensor([vs], device=DEV))
+    P = torch.tensor([P0], dtype=torch.int32, device=DEV)
+    K.kv_append(cache, kp.to(DEV), vp.to(DEV), torch.zeros(1, dtype=torch.int32, device=DEV), block_table=tdev,
+                n_valid=P)
+    got = K.attn_prefill(q2.to(DEV), k2.to(DEV), v2.to(DEV), cache=cache, positions=P, block_table=tdev,
+                         attend_prefix=True).cpu().numpy()
+
+    def deq(x, sc):
+        codes = OC.encode_rows(storage(x)[0, 0, :P0], OC.BF16, OC.FP8_E4M3, np.float32(sc))
+        return OC.to_f64(codes, OC.FP8_E4M3, np.float32(sc))[None]
+    want = _oracle(q2, k2, v2, [P0], [n], prefix=([deq(kp, ks)], [deq(vp, vs)]))
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= TOL
+
 def test_mfma_prefix_key_mask_nan_poisoned_and_verify_shape():
     """Key mask over absolute positions with NaN in the masked cached rows
     (weights exactly 0, outputs finite), and a 4-token chunk (the shape of
