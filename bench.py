@@ -70,7 +70,7 @@ KERNEL_SOURCES = {
     "prefill": (CSRC + "prefill_mfma.hip", CSRC + "common.h", API_CPP, BUILD_PY, "PrefillLaunch"),
 }
 WORKLOAD_KERNELS = {"decode8b": "decode", "padded32": "decode", "longctx70b": "decode", "verify8b": "decode",
-                    "prefill8k": "prefill"}
+                    "prefill8k": "prefill", "chunkprefill": "prefill", "chunkprefill_fp8": "prefill"}
 
 
 def _launch_struct(text, name):
@@ -927,7 +927,7 @@ def run_leg(name, args, cpu):
                                  "; fp8 codes expanded to bf16 in LDS, after kv_append_kernel quantises the chunk "
                                  "into the cache)" if cp.kv_dtype == K.FP8_E4M3 else ")"),
                              "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}}
+                             "frac": tf / BF16_PEAK_TFLOPS, "traffic": traffic(name)}}
     if name in ("cowcopy", "beamreorder"):
         cw = CowBlockCopy() if name == "cowcopy" else BeamReorder()
         warm_clocks(cw)
